@@ -1,0 +1,25 @@
+"""CPU oracle for the DDTree verification step -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, float64 NumPy definition of what the step computes, written from
+the source pages (cited per function by page title and section) and from the
+readings listed in the design doc where the pages are silent.  It is independent of
+the HIP library: the two share no code, and neither imports the other.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call anything in this package.  The product path
+(``tree_speculative_decoding_ddt_amd``) never does, and fails loudly when its
+HIP library is missing instead of falling back to this code.
+
+Modules
+  tree       -- per-depth log-softmax + top-K, best-first tree build, flatten
+  attention  -- tree-masked attention as a dense masked softmax
+  gdn        -- short causal conv + gated delta rule over the tree
+  accept     -- target argmax + greedy tree walk
+  commit     -- copy of the accepted path into the committed buffers
+  step       -- the whole verify step composed from the above
+
+Every function takes and returns NumPy arrays; floating-point inputs are
+promoted to float64 before any arithmetic.
+"""
+
+from . import tree, attention, gdn, accept, commit, step, gaps  # noqa: F401

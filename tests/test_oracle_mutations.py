@@ -1,0 +1,86 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case rewrites one line of an oracle function on the CPU (a dropped term,
+a wrong sign, a wrong index, a flipped tie rule ...) and checks that at least
+one pin test then fails.  Nothing here touches a GPU.
+"""
+
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.accept
+import oracle.attention
+import oracle.commit
+import oracle.gdn
+import oracle.tree
+from tests import test_oracle_accept_commit as t_ac
+from tests import test_oracle_attention as t_attn
+from tests import test_oracle_gdn as t_gdn
+from tests import test_oracle_tree as t_tree
+
+
+def mutated(module, name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(module, name)))
+    assert old in src, (name, old)
+    ns = dict(vars(module))
+    exec(compile(src.replace(old, new, 1), "<mutant>", "exec"), ns)
+    return ns[name]
+
+
+def run_pins(pins):
+    """True if at least one pin fails."""
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+TREE_PINS = [lambda: t_tree.test_heap_equals_brute_force_rank_limited(0),
+             lambda: t_tree.test_heap_equals_full_enumeration(1, 20),
+             t_tree.test_hand_worked_example_with_ties,
+             t_tree.test_single_depth_is_top_b_of_one_row]
+ATTN_PINS = [lambda: t_attn.test_matches_per_path_replay(0), t_attn.test_chain_tree_equals_causal_attention,
+             t_attn.test_closed_forms]
+GDN_PINS = [lambda: t_gdn.test_tree_matches_chain_replay(0), t_gdn.test_hand_computed_update,
+            t_gdn.test_identity_tap_is_silu, t_gdn.test_conv_scratch_exact_copies_short_path,
+            t_gdn.test_unit_beta_stores_value]
+ACC_PINS = [lambda: t_ac.test_walk_matches_brute_force(0), t_ac.test_argmax_ties_take_lowest_id,
+            lambda: t_ac.test_commit_copies_replay_and_decode(0)]
+
+CASES = [
+    (oracle.tree, "build_tree", "int(ids[0, 0]), 0, 1, 0", "int(ids[0, 0]), 0, 1, 1", TREE_PINS),
+    (oracle.tree, "build_tree", "score[p] + vals[d - 1, r + 1]", "score[p] + vals[d - 1, r]", TREE_PINS),
+    (oracle.tree, "build_tree", "score[i] + vals[d, 0]", "score[p] + vals[d, 0]", TREE_PINS),
+    (oracle.tree, "build_tree", "-(score[i] + vals[d, 0]), int(ids[d, 0])", "-(score[i] + vals[d, 0]), -int(ids[d, 0])", TREE_PINS),
+    (oracle.tree, "build_tree", "anc[p] | (1 << (i - 1))", "anc[p] | (1 << i)", TREE_PINS),
+    (oracle.tree, "topk_per_depth", "np.lexsort((tok, -lp[d]))", "np.lexsort((-tok, -lp[d]))", TREE_PINS),
+    (oracle.tree, "log_softmax", "z - lse", "z - m", TREE_PINS),
+    (oracle.attention, "tree_attention", "mask[:, :P] = True", "mask[:, :P - 1] = True", ATTN_PINS),
+    (oracle.attention, "tree_attention", "kvh = h // G", "kvh = h % Hkv", ATTN_PINS),
+    (oracle.attention, "tree_attention", "scale = D ** -0.5 if", "scale = D ** -1.0 if", ATTN_PINS),
+    (oracle.attention, "visible_tree_rows", "[0] + [j + 1", "[j + 1", ATTN_PINS),
+    (oracle.attention, "visible_tree_rows", "[j + 1 for", "[j for", ATTN_PINS),
+    (oracle.gdn, "gated_delta_tree", "np.outer(v[i, h] - u, k[i, h])", "np.outer(v[i, h] + u, k[i, h])", GDN_PINS),
+    (oracle.gdn, "gated_delta_tree", "Sd = g[i, h] * Sp[h]", "Sd = Sp[h]", GDN_PINS),
+    (oracle.gdn, "gated_delta_tree", "o[i, h] = S[i, h] @ q[i, h]", "o[i, h] = S[i, h].T @ q[i, h]", GDN_PINS),
+    (oracle.gdn, "short_conv_tree", 'np.einsum("jc,cj->c", window, w)', 'np.einsum("jc,cj->c", window[::-1], w)', GDN_PINS),
+    (oracle.gdn, "short_conv_tree", "scratch[i] = window[1:]", "scratch[i] = window[:-1]", GDN_PINS),
+    (oracle.gdn, "split_qk", "+ K_NORM_EPS)", "+ 1.0)", GDN_PINS),
+    (oracle.gdn, "split_qk", "* dk ** -0.5", "* 1.0", GDN_PINS),
+    (oracle.accept, "argmax_lowest", "[0])", "[-1])", ACC_PINS),
+    (oracle.accept, "tree_accept", "tok[c] == t[cur]", "tok[c] == t[c]", ACC_PINS),
+    (oracle.commit, "commit", 'lay["k_cache"][:, P + j, :] = lay["k_tree"][:, r, :]',
+     'lay["k_cache"][:, P + j + 1, :] = lay["k_tree"][:, r, :]', ACC_PINS),
+    (oracle.commit, "commit", "last = rows[-1]", "last = rows[0]", ACC_PINS),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=lambda i: "%s.%s#%d" % (CASES[i][0].__name__.split(".")[-1], CASES[i][1], i))
+def test_pins_catch_planted_mistake(case, monkeypatch):
+    module, name, old, new, pins = CASES[case]
+    monkeypatch.setattr(module, name, mutated(module, name, old, new))
+    assert run_pins(pins), "no pin caught: %s.%s %r -> %r" % (module.__name__, name, old, new)
