@@ -1,0 +1,248 @@
+"""Benchmark: full DDTree hybrid verify step on one MI355X.
+
+Workload (one "step" = one verify round over the whole hot path):
+  8 sequences, budget B = 64 (65 tree rows), drafter depth L = 15, vocab 151936,
+  committed prefix 32768 tokens; build the tree from bf16 drafter logits, 64 layers
+  in the pattern [GDN, GDN, GDN, attention] x 16 (attention: 24 q / 4 kv heads,
+  head_dim 256; GDN: 32 heads, dk = dv = 128, fp32 state, conv width 4 over 8192
+  channels, bf16 activations), greedy walk against bf16 target logits, commit of
+  the accepted path.  Inputs are seeded synthetic draws resident in HBM before the
+  timed region; the bonus token of each round is the next round's root and every
+  commit grows the prefix, as in decoding.
+
+Output: one JSON line (metric, value = steps/s, per-kernel breakdown, roofline of
+the dominant kernel, tree-attention KV bandwidth, CPU-oracle baseline).
+
+    python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix
+KERNEL_SOURCES = {
+    "gdn_tree_step": "gdn_tree.hip",
+    "tree_attn": "tree_attn.hip",
+    "build_tree": "build_tree.hip",
+    "tree_accept": "accept.hip",
+    "commit": "commit.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefix", type=int, default=32768)
+    ap.add_argument("--n", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    return ap.parse_args()
+
+
+def src_hash(name):
+    path = os.path.join(ROOT, "tree_speculative_decoding_ddt_amd", "csrc", KERNEL_SOURCES[name])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic(cfg, prefix_now):
+    """Algorithmic HBM bytes (and flops) per launch of each call, for the current prefix."""
+    n, T, V, L = cfg.n, cfg.T, cfg.V, cfg.L
+    kv = n * cfg.Hkv * (prefix_now + T) * cfg.D * 2 * 2                  # K and V, bf16
+    attn_io = 2 * n * T * cfg.Hq * cfg.D * 2                              # q in, out
+    attn_flops = 4.0 * n * T * cfg.Hq * cfg.D * (prefix_now + T)           # QK^T + PV over all keys
+    state = cfg.H * cfg.dk * cfg.dk * 4
+    gdn = (n * T * state                                                  # S_scratch written
+           + n * state                                                    # committed S read
+           + n * T * cfg.C * 2                                            # x read
+           + n * (cfg.W - 1) * cfg.C * 2                                  # committed conv state read
+           + n * T * (cfg.W - 1) * cfg.C * 2                              # conv scratch written
+           + 2 * n * T * cfg.H * cfg.dk * 2                               # v read, o written
+           + 2 * n * T * cfg.H * 4)                                       # beta, g
+    build = n * L * V * 2 + n * T * 24
+    accept = n * T * V * 2
+    return {"tree_attn": (kv + attn_io, attn_flops), "gdn_tree_step": (gdn, 0.0),
+            "build_tree": (build, 0.0), "tree_accept": (accept, 0.0)}
+
+
+def cpu_baseline(cfg, prefix):
+    """Time the oracle on a bounded sample of the same workload; extrapolate to steps/s."""
+    import numpy as np
+
+    from oracle import accept as oacc
+    from oracle import attention as oattn
+    from oracle import gdn as ogdn
+    from oracle import tree as otree
+    from tree_speculative_decoding_ddt_amd import synth
+
+    rng = np.random.default_rng(1)
+    z = synth.quantize(synth.draft_logits(rng, 1, cfg.L, cfg.V, 3.0, plant_p=0.6), "bf16")[1][0]
+    t0 = time.perf_counter()
+    tree = otree.build_tree(z, cfg.B, 0)
+    t_build = time.perf_counter() - t0
+    at = synth.attention_inputs(rng, 1, cfg.T, cfg.Hq, cfg.Hkv, cfg.D, prefix)
+    at = {k: synth.quantize(v, "bf16")[1][0].astype(np.float64) for k, v in at.items()}
+    t0 = time.perf_counter()
+    oattn.tree_attention(at["q"], at["k_cache"], at["v_cache"], prefix, at["k_tree"], at["v_tree"], tree["anc"])
+    t_attn = time.perf_counter() - t0
+    del at
+    gi = synth.gdn_inputs(rng, 1, cfg.T, cfg.H, cfg.dk, cfg.dk, cfg.W)
+    t0 = time.perf_counter()
+    ogdn.gdn_tree_step(gi["x"][0], gi["conv_w"], gi["conv_state"][0], gi["v"][0], gi["beta"][0], gi["g"][0],
+                       gi["S"][0], tree["parent"], cfg.H, cfg.dk)
+    t_gdn = time.perf_counter() - t0
+    y = synth.quantize(synth.target_logits(rng, 1, cfg.T, cfg.V, 3.0, tree["depth"][None],
+                                           synth.draft_top1(z[None]), 0.7), "bf16")[1][0]
+    t0 = time.perf_counter()
+    oacc.tree_accept(y, tree["tok"], tree["parent"], cfg.L)
+    t_acc = time.perf_counter() - t0
+    per_seq = t_build + cfg.n_attn * t_attn + cfg.n_gdn * t_gdn + t_acc
+    t_step = cfg.n * per_seq
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": ("1 of %d sequences at the full shapes: tree build (%.2fs), 1 of %d attention layers at "
+                       "prefix %d (%.2fs), 1 of %d GDN layers (%.2fs), walk (%.2fs); step time extrapolated "
+                       "as %d x (build + %d attn + %d gdn + walk) = %.1fs; numpy fp64, BLAS on %d cores"
+                       % (cfg.n, t_build, cfg.n_attn, prefix, t_attn, cfg.n_gdn, t_gdn, t_acc, cfg.n, cfg.n_attn,
+                          cfg.n_gdn, t_step, cores))}
+
+
+def load_traffic(name):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(name)
+    if not rec or rec.get("source_sha") != src_hash(name):
+        return None  # counters were taken on another version of the kernel
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: the verify step is measured on a single MI355X "
+              "(requested --gpus %d)" % a.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    from tree_speculative_decoding_ddt_amd import ddt
+    from tree_speculative_decoding_ddt_amd.step import HybridConfig, HybridVerifyStep
+
+    ddt.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(a.steps + a.warmup + 2) * 16 + 64)
+    step = HybridVerifyStep(cfg, dev)
+    step.fill_random(seed=a.seed)
+    print("bench: inputs ready (%.1f GB on device)" % (torch.cuda.memory_allocated(dev) / 1e9),
+          file=sys.stderr, flush=True)
+
+    names = ("build_tree", "tree_attn", "gdn_tree_step", "tree_accept", "commit")
+    ev = {k: [] for k in names}
+
+    def timed(name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        ev[name].append((s, e))
+
+    def run_step(record):
+        if not record:
+            step()
+            return
+        timed("build_tree", step.build)
+        ia = ig = 0
+        for kind in step.pattern:
+            if kind == "attn":
+                lay = step.attn[ia]
+                ia += 1
+                timed("tree_attn", lambda: ddt.tree_attn(lay["q"], lay["k_cache"], lay["v_cache"], step.prefix_len,
+                                                         lay["k_tree"], lay["v_tree"], step.tree["anc"],
+                                                         ws=step.ws_attn, out=lay["out"]))
+            else:
+                g = step.gdn[ig]
+                ig += 1
+                timed("gdn_tree_step", lambda: ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"],
+                                                                 g["beta"], g["g"], g["S"], step.tree["parent"],
+                                                                 cfg.L, out=g["out"]))
+        timed("tree_accept", step.accept)
+        timed("commit", step.commit)
+
+    for _ in range(a.warmup):
+        run_step(False)
+    torch.cuda.synchronize(dev)
+    p0 = int(step.prefix_len.float().mean().item())
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        run_step(True)
+    torch.cuda.synchronize(dev)
+    dt = time.perf_counter() - t0
+    p1 = int(step.prefix_len.float().mean().item())
+    acc_mean = float(step.acc["acc_len"].float().mean().item())
+
+    alg = algorithmic(cfg, (p0 + p1) // 2)
+    kernels = {}
+    for k in names:
+        ms = [s.elapsed_time(e) for s, e in ev[k]]
+        per = sum(ms) / len(ms)
+        rec = {"ms_per_launch": round(per, 4), "launches_per_step": len(ms) // a.steps,
+               "ms_per_step": round(sum(ms) / a.steps, 4)}
+        if k in alg:
+            b, fl = alg[k]
+            rec["algorithmic_bytes"] = b
+            rec["GBps"] = round(b / (per * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["GBps"] / HBM_PEAK_GBPS, 4)
+            if fl:
+                rec["TFLOPps"] = round(fl / (per * 1e-3) / 1e12, 1)
+                rec["mfma_frac"] = round(rec["TFLOPps"] / BF16_PEAK_TFLOPS, 4)
+        kernels[k] = rec
+    dom = max(("gdn_tree_step", "tree_attn", "build_tree", "tree_accept"), key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    if dom == "tree_attn":
+        roof = {"bound": "mfma", "achieved": kd["TFLOPps"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": kd["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kd["hbm_frac"]}
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom)
+    ka = kernels["tree_attn"]
+    kv_bytes = cfg.n * cfg.Hkv * ((p0 + p1) // 2 + cfg.T) * cfg.D * 4
+    attn = {"kv_bytes_per_launch": kv_bytes, "kv_GBps": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9, 1),
+            "kv_frac_of_hbm_peak": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "TFLOPps": ka.get("TFLOPps"), "mfma_frac": ka.get("mfma_frac")}
+
+    cpu = None
+    if not a.no_cpu:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, a.prefix)
+
+    value = a.steps / dt
+    line = {
+        "metric": "tree-verify steps/sec at B=64, 32K prefix; tree-attn KV GB/s vs HBM peak",
+        "value": round(value, 3), "unit": "steps/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(dt / a.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded device RNG draws)",
+        "config": {"workload": "full hybrid verify step: 8 seqs, B=64, L=15, vocab 151936, prefix %d, "
+                               "16 attn (24/4 heads, D 256) + 48 GDN (32 heads, dk=dv=128, C 8192, W 4) layers"
+                               % a.prefix,
+                   "global_batch": cfg.n, "seq_len": a.prefix, "parallelism": "single GPU"},
+        "roofline": roof, "tree_attn": attn, "kernels": kernels,
+        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p0, p1],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

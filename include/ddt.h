@@ -1,0 +1,196 @@
+/* ddt.h -- C ABI of libddt.so: the DDTree tree-verification step on MI355X (gfx950).
+ *
+ * One verify round of tree speculative decoding on a hybrid model (full-attention
+ * layers with a KV cache, Gated DeltaNet layers with a fixed-size recurrent state and
+ * a short-conv state):
+ *   ddt_build_tree     draft tree of B nodes from the drafter's per-depth logits
+ *   ddt_tree_attn      tree-masked attention of every node over prefix + ancestors
+ *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
+ *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
+ *   ddt_commit         copy only the accepted path into the committed buffers
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller; the library allocates
+ *     no device memory and keeps no state between calls.  Scratch space, where a call
+ *     needs it, is a caller-provided device buffer `ws` of at least the size the
+ *     matching *_workspace() query returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  It returns a status synchronously after host-side validation and the
+ *     launches; a fault inside a kernel surfaces at the caller's next stream sync.
+ *   - No call synchronises the device or reads device memory on the host: lengths
+ *     such as prefix_len and acc_len are read on the device, so a round can be
+ *     captured in a HIP graph.
+ *   - Arrays are row-major, leftmost index slowest.  n = batch, B = budget (non-root
+ *     nodes), T = B+1 tree rows (row 0 is the root), L = maximum depth, V = vocab,
+ *     P = committed prefix length (per sequence, on the device), Pmax = cache capacity.
+ *   - bf16 data is IEEE bfloat16 (upper half of a float32), stored as 16-bit words.
+ *   - Limits: 1 <= B <= 64 (one 64-bit mask word per row, root implicit), L <= 63.
+ *   - Errors: DDT_ERR_ARG for a null pointer or an out-of-range size;
+ *     DDT_ERR_UNSUPPORTED for a dtype or head size outside the built set;
+ *     DDT_ERR_WORKSPACE for a workspace smaller than the query; DDT_ERR_HIP when a
+ *     launch fails.  ddt_last_error() returns a message for the last failure on the
+ *     calling thread.
+ *
+ * Sources (web pages on DDTree tree speculative decoding):
+ *   [notes]  "DDTree on vLLM: candid research notes on tree speculation for Qwen3.6"
+ *            (lotusmake.com): sections "Why hybrid attention makes it hard",
+ *            "What broke along the way", "Where the next step is".
+ *   [arch]   "From DDTree to drafter training" (magik.net): section
+ *            "The Architecture of DDTree".
+ *   [spec]   "The architecture of speculation" (magik.net): section
+ *            "The DDTree Integration Challenge".
+ */
+#ifndef DDT_H
+#define DDT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DDT_OK = 0,
+  DDT_ERR_ARG = 1,
+  DDT_ERR_UNSUPPORTED = 2,
+  DDT_ERR_WORKSPACE = 3,
+  DDT_ERR_HIP = 4
+} ddt_status;
+
+typedef enum { DDT_F32 = 0, DDT_BF16 = 1 } ddt_dtype;
+
+/* Name of a status code (static string). */
+const char* ddt_status_string(int status);
+/* Message describing the last failed call on this thread ("" if none). */
+const char* ddt_last_error(void);
+/* ABI version of this header/library pair. */
+int ddt_abi_version(void);
+
+/* ---------------------------------------------------------------- tree build
+ * [arch]: a block drafter gives one distribution per future position; take the
+ * top-K tokens and log-probs of every depth, seed a max-heap with the best depth-1
+ * token, pop the globally best node, push its next-ranked sibling and its best
+ * child, stop after B pops; flatten into ids, per-depth positions and an
+ * ancestor-only mask.  [notes] "What broke along the way": depth logits are not
+ * branch-conditioned, so a node's score is the sum of its path's log-probs.
+ *
+ *   draft_logits [n][L][V] (dt)  row d = logits of depth d+1 (full-vocab log-softmax
+ *                                is taken in fp32)
+ *   K            candidates per depth (0 = B; must be <= 64)
+ *   root_token   [n] int32       token of row 0 (the previous round's bonus token)
+ * outputs, rows in pop order (parents precede children):
+ *   tok, parent, depth [n][T] int32   row 0: root_token, -1, 0
+ *   score [n][T] f32                  summed log-prob (row 0: 0)
+ *   anc   [n][T] u64                  bit j set <=> row j+1 is an ancestor of, or is,
+ *                                     the row (row 0 implicit, anc[0] = 0)
+ * Heap order: score desc, token id asc, parent row asc.  Rows left unused because the
+ * tree has fewer than B prefixes get tok = parent = depth = -1, score = -inf, anc = 0.
+ * Position ids are prefix_len + depth.  Requires V <= 2^20 and ceil(V/16384)*K <= 2048.
+ */
+size_t ddt_build_tree_workspace(int n, int L, int V, int B, int K);
+int ddt_build_tree(const void* draft_logits, int dt, int n, int L, int V, int B, int K,
+                   const int32_t* root_token, int32_t* tok, int32_t* parent, int32_t* depth,
+                   float* score, uint64_t* anc, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- tree attention
+ * [notes] "Why hybrid attention makes it hard": each tree row attends to the
+ * committed prefix plus its own ancestors and never to its siblings.  [arch]: one
+ * verify pass over root + all nodes with an ancestor-only mask.
+ *
+ *   q       [n][T][Hq][D]     (dt) queries of the tree rows (post-RoPE)
+ *   k_cache [n][Hkv][Pmax][D] (dt) committed keys; rows >= prefix_len[s] are ignored
+ *   v_cache [n][Hkv][Pmax][D] (dt)
+ *   prefix_len [n] int32 (device), each in [0, Pmax]
+ *   k_tree, v_tree [n][Hkv][T][D] (dt) keys/values of the tree rows (separate scratch;
+ *                  the committed cache is not written)
+ *   anc     [n][T] u64        masks from ddt_build_tree
+ *   out     [n][T][Hq][D]     (dt)
+ * Query head h uses kv head h / (Hq/Hkv).  Scores, softmax and accumulation in fp32;
+ * bf16 products on the matrix cores.  scale <= 0 selects D^-1/2.
+ * Built: D in {64, 128, 256}; Hq % Hkv == 0; Hq/Hkv <= 16.
+ */
+size_t ddt_tree_attn_workspace(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);
+int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                  const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, int Pmax,
+                  float scale, int dt, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- GDN tree step
+ * [notes] "Why hybrid attention makes it hard": every node reads the Gated DeltaNet
+ * state and the short-conv state of its parent and writes its own to scratch, never
+ * to the committed state.  [spec]: per-branch state, not one shared state.
+ * Per node i with parent p (the committed state when p < 0), per head:
+ *   conv:  window = [conv state of p (W-1 rows, oldest first), x_i];
+ *          y = SiLU(sum_j conv_w[c][j] * window[j][c]); conv_scratch[i] = window[1..W-1]
+ *          channels C = 2*H*dk hold [q | k]; q *= dk^-1/2; k /= sqrt(|k|^2 + 1e-6)
+ *   delta: S' = g_i S_p;  S_i = S' + beta_i (v_i - S' k_i) k_i^T;  o_i = S_i q_i
+ *   x [n][T][C] (act_dt), conv_w [C][W] (f32), conv_state [n][W-1][C] (act_dt),
+ *   conv_scratch [n][T][W-1][C] (act_dt, written; exact copies of inputs)
+ *   v [n][T][H][dv] (act_dt), beta, g [n][T][H] (f32)
+ *   S [n][H][dv][dk] (f32, committed, read only), S_scratch [n][T][H][dv][dk] (f32, written)
+ *   o [n][T][H][dv] (act_dt, written)
+ *   parent [n][T] int32: parent[i] < i, or < 0 for a row that reads the committed state
+ *   L: upper bound on the tree depth (row depth by parent chain), L <= 38
+ * Built: dk = dv in {32, 64, 128}; W in [2, 8]; C == 2*H*dk.
+ */
+int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,
+                      void* conv_scratch, const void* v, const float* beta, const float* g,
+                      const float* S, float* S_scratch, void* o, const int32_t* parent,
+                      int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
+                      void* stream);
+
+/* ---------------------------------------------------------------- tree walk
+ * [arch]: after the verify pass, walk down from the root while the target's token
+ * at the current node equals one of its children's tokens.  [notes] "What broke
+ * along the way": the bonus token is emitted, not accepted as a draft node.
+ *   target_logits [n][T][V] (dt); argmax ties go to the lowest token id
+ *   tok, parent [n][T] int32 from ddt_build_tree
+ * outputs: acc_rows [n][L+1] int32 (root first, then accepted rows, -1 padded),
+ *          acc_len [n] int32 (accepted non-root nodes a, 0..L; -1 if the tree is
+ *          malformed: a parent row not before its child, or two siblings sharing the
+ *          matched token), bonus [n] int32 (target argmax at the last accepted row).
+ */
+size_t ddt_tree_accept_workspace(int n, int B, int V);
+int ddt_tree_accept(const void* target_logits, int dt, const int32_t* tok, const int32_t* parent,
+                    int n, int B, int L, int V, int32_t* acc_rows, int32_t* acc_len,
+                    int32_t* bonus, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- commit
+ * [notes] "Why hybrid attention makes it hard" and "Where the next step is": only
+ * the accepted path is copied into the contiguous KV and recurrent buffers, through
+ * an explicit commit keyed by node ids.  [arch]: the KV cache keeps only the
+ * accepted path's entries.
+ * For every sequence s with a = acc_len[s] >= 0 and P = prefix_len[s], P + a + 1 <= Pmax:
+ *   every attention layer:  k_cache/v_cache[s][:][P+j] = k_tree/v_tree[s][:][acc_rows[s][j]], j = 0..a
+ *   every GDN layer:        S[s] = S_scratch[s][r], conv_state[s] = conv_scratch[s][r],
+ *                           r = acc_rows[s][a] (the deepest accepted row)
+ *   prefix_len[s] += a + 1
+ * Otherwise nothing of s is written and acc_len[s] becomes -1.  Copies are exact.
+ * kv and gdn are HOST arrays of per-layer device pointers (n_kv, n_gdn entries; either
+ * may be 0).  kv_dt is the element type of the KV buffers, act_dt of the conv buffers.
+ */
+typedef struct {
+  const void* k_tree; /* [n][Hkv][T][D] */
+  const void* v_tree;
+  void* k_cache;      /* [n][Hkv][Pmax][D] */
+  void* v_cache;
+} ddt_kv_layer;
+
+typedef struct {
+  const float* S_scratch;   /* [n][T][H][dv][dk] */
+  float* S;                 /* [n][H][dv][dk] */
+  const void* conv_scratch; /* [n][T][W-1][C] */
+  void* conv_state;         /* [n][W-1][C] */
+} ddt_gdn_layer;
+
+int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
+               const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_dt,
+               const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
+               int act_dt, int n, int B, int L, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDT_H */

@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU parity tests: upload seeded inputs in a storage dtype,
+read results back, and compare against the oracle with the stated tolerances."""
+
+import numpy as np
+import torch
+
+from tree_speculative_decoding_ddt_amd import synth
+
+# (atol, rtol), elementwise |x - ref| <= atol + rtol * |ref|
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2)}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def up(x, dtype):
+    """float32 numpy -> (device tensor in `dtype`, float64 numpy of the stored values)."""
+    store, exact = synth.quantize(x, dtype)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(store).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(store))
+    return t.to(dev()), exact.astype(np.float64)
+
+
+def up_int(x, dtype=torch.int32):
+    return torch.as_tensor(np.asarray(x), dtype=dtype).to(dev())
+
+
+def down(t):
+    """Device tensor -> float64 numpy (bf16 decoded exactly)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy().astype(np.float64)
+    return t.numpy().astype(np.float64) if t.is_floating_point() else t.numpy()
+
+
+def assert_close(got, ref, dtype, what=""):
+    atol, rtol = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        raise AssertionError("%s: %d/%d elements out of tolerance (%s); worst at %s: got %r ref %r; "
+                             "max abs err %.3g" % (what, bad.sum(), bad.size, dtype, i, got[i], ref[i], err.max()))
+
+
+def anc_tensor(anc_u64):
+    """uint64 masks -> int64 device tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(anc_u64, np.uint64)).view(np.int64)).to(dev())
+
+
+def anc_numpy(t):
+    return t.detach().cpu().numpy().view(np.uint64)
+
+
+def say(*a):
+    print(*a, flush=True)

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function include/ddt.h
+declares, sizes its workspaces, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_speculative_decoding_ddt_amd import ddt
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ddt.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddt_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    L = ddt.lib()
+    names = declared()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(ddt.EXPORTS) == names
+
+
+def test_status_strings_and_version():
+    L = ddt.lib()
+    assert L.ddt_abi_version() == 1
+    assert [L.ddt_status_string(i).decode() for i in range(5)] == [
+        "DDT_OK", "DDT_ERR_ARG", "DDT_ERR_UNSUPPORTED", "DDT_ERR_WORKSPACE", "DDT_ERR_HIP"]
+
+
+def test_workspace_queries():
+    assert ddt.build_tree_workspace(16, 15, 151936, 64) > ddt.build_tree_workspace(1, 15, 151936, 64) > 0
+    assert ddt.build_tree_workspace(1, 4, 512, 8) > 0
+    assert ddt.build_tree_workspace(1, 4, 512, 65) == 0          # B > 64
+    assert ddt.build_tree_workspace(1, 15, 2 ** 21, 64) == 0      # V > 2^20
+    import torch
+    assert ddt.tree_attn_workspace(1, 8, 2, 1, 64, 128, torch.float32) == 0   # scalar path: no workspace
+    assert ddt.tree_attn_workspace(8, 64, 24, 4, 256, 32768, torch.bfloat16) > 0
+    assert ddt.tree_attn_workspace(8, 64, 24, 4, 96, 32768, torch.bfloat16) == 0  # D not built
+    assert ddt.tree_accept_workspace(8, 64, 151936) > 0
+
+
+P = ctypes.c_void_p(256)  # a non-null placeholder: every call below fails validation before using it
+
+
+def status(fn, *args):
+    return getattr(ddt.lib(), fn)(*args)
+
+
+def test_build_tree_validation():
+    args = lambda **k: [k.get("z", P), k.get("dt", 1), k.get("n", 1), k.get("L", 15), k.get("V", 1000),
+                        k.get("B", 64), k.get("K", 0), P, P, P, P, P, P, P, k.get("ws", 1 << 30), None]
+    assert status("ddt_build_tree", *args(z=None)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree", *args(B=65)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree", *args(L=0)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree", *args(K=65)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree", *args(dt=7)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_build_tree", *args(V=(1 << 20) + 1)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_build_tree", *args(ws=16)) == ddt.DDT_ERR_WORKSPACE
+    assert "workspace" in ddt.lib().ddt_last_error().decode()
+
+
+def test_tree_attn_validation():
+    def args(**k):
+        return [k.get("q", P), P, P, P, P, P, P, 1, k.get("B", 8), k.get("Hq", 2), k.get("Hkv", 1),
+                k.get("D", 64), 128, ctypes.c_float(0.0), k.get("dt", 0), P, k.get("ws", P), k.get("wsb", 1 << 30), None]
+    assert status("ddt_tree_attn", *args(q=None)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn", *args(B=65)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn", *args(Hq=3, Hkv=2)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn", *args(D=96)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_tree_attn", *args(dt=3)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_tree_attn", *args(dt=1, D=256, wsb=8)) == ddt.DDT_ERR_WORKSPACE
+
+
+def test_gdn_validation():
+    def args(**k):
+        return [P] * 11 + [1, 8, k.get("L", 4), k.get("H", 1), k.get("dk", 32), k.get("dv", 32), k.get("C", 64),
+                           k.get("W", 4), k.get("dt", 0), None]
+    assert status("ddt_gdn_tree_step", *args(C=63)) == ddt.DDT_ERR_ARG
+    assert status("ddt_gdn_tree_step", *args(dk=48, dv=48, C=96)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(dv=64)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(W=9)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(L=36)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(dt=2)) == ddt.DDT_ERR_UNSUPPORTED
+    a = args()
+    a[0] = None
+    assert status("ddt_gdn_tree_step", *a) == ddt.DDT_ERR_ARG
+
+
+def test_accept_and_commit_validation():
+    a = [P, 0, P, P, 1, 8, 4, 512, P, P, P, P, 8, None]
+    assert status("ddt_tree_accept", *a) == ddt.DDT_ERR_WORKSPACE
+    a[5] = 65
+    assert status("ddt_tree_accept", *a) == ddt.DDT_ERR_ARG
+    kv = (ddt.KVLayer * 1)(ddt.KVLayer(256, 256, None, 256))
+    gd = (ddt.GDNLayer * 1)()
+    c = [P, P, P, kv, 1, 2, 64, 48, 1, gd, 0, 1, 32, 32, 64, 4, 1, 1, 8, 4, None]
+    assert status("ddt_commit", *c) == ddt.DDT_ERR_ARG        # null cache pointer in layer 0
+    kv[0] = ddt.KVLayer(256, 256, 256 + 8, 256)
+    assert status("ddt_commit", *c) == ddt.DDT_ERR_ARG        # misaligned
+    c[6] = 60
+    kv[0] = ddt.KVLayer(256, 256, 256, 256)
+    assert status("ddt_commit", *c) == ddt.DDT_ERR_ARG        # D*2 bytes not a multiple of 16
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ddt.build_tree(torch.zeros(1, 4, 512), 8, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,127 @@
+"""GPU parity of ddt_tree_accept and ddt_commit against the oracle (bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import accept as oacc
+from oracle import commit as ocommit
+from oracle import tree as otree
+from tests.gpu_util import down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def tree_and_target(seed, n, L, V, B, dtype, plant=0.7, sigma=2.0):
+    rng = np.random.default_rng(seed)
+    z = synth.draft_logits(rng, n, L, V, sigma)
+    t = otree.build_tree_batch(z, B, np.zeros(n, np.int64))
+    y = synth.target_logits(rng, n, B + 1, V, sigma, t["depth"], synth.draft_top1(z), plant)
+    return t, y
+
+
+def run_accept(t, y, L, dtype):
+    yt, ye = up(y, dtype)
+    out = ddt.tree_accept(yt, up_int(t["tok"]), up_int(t["parent"]), L)
+    torch.cuda.synchronize()
+    rows, alen, bonus = down(out["acc_rows"]), down(out["acc_len"]), down(out["bonus"])
+    ref = oacc.tree_accept_batch(ye, t["tok"], t["parent"], L)
+    np.testing.assert_array_equal(rows, ref[0])
+    np.testing.assert_array_equal(alen, ref[1])
+    np.testing.assert_array_equal(bonus, ref[2])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_tiny_fp32(seed):
+    say("accept tiny fp32 seed", seed)
+    t, y = tree_and_target(seed, 4, 4, 512, 8, "f32")
+    run_accept(t, y, 4, "f32")
+
+
+@pytest.mark.parametrize("plant", [0.0, 0.7, 1.0])
+def test_accept_full_vocab_bf16(plant):
+    say("accept bf16 n=8 V=151936 B=64 plant", plant)
+    t, y = tree_and_target(5, 8, 15, 151936, 64, "bf16", plant=plant, sigma=3.0)
+    out = run_accept(t, y, 15, "bf16")
+    if plant == 1.0:
+        assert (down(out["acc_len"]) > 0).all()
+
+
+def test_accept_ties_and_ragged_vocab():
+    rng = np.random.default_rng(8)
+    t, _ = tree_and_target(8, 3, 5, 1001, 16, "f32")
+    y = rng.integers(-3, 3, size=(3, 17, 1001)).astype(np.float32)  # exact ties everywhere
+    run_accept(t, y, 5, "bf16")
+    run_accept(t, y, 5, "f32")
+
+
+def test_accept_malformed_trees():
+    tok = np.array([[9, 1, 1, 2], [9, 1, 2, 3]], dtype=np.int64)
+    parent = np.array([[-1, 0, 0, 1], [-1, 0, 3, 1]], dtype=np.int64)  # twin siblings / parent after child
+    y = np.zeros((2, 4, 8), dtype=np.float32)
+    y[:, :, 1] = 5.0
+    out = ddt.tree_accept(up(y, "f32")[0], up_int(tok), up_int(parent), 3)
+    torch.cuda.synchronize()
+    assert down(out["acc_len"]).tolist() == [-1, -1]
+
+
+def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None):
+    rng = np.random.default_rng(seed)
+    L, B, Hkv, D, H, dk, W = 5, 12, 2, 64, 2, 32, 4
+    T, C = B + 1, 2 * H * dk
+    t, _ = tree_and_target(seed, n, L, 300, B, "f32", plant=0.9)
+    # accepted paths: the root path of a chosen row per sequence (deepest row last)
+    rows_np = np.full((n, L + 1), -1, dtype=np.int64)
+    alen_np = np.zeros(n, dtype=np.int64)
+    for s in range(n):
+        i = 0 if s == 0 else int(rng.integers(1, T))  # sequence 0 accepts nothing beyond the root
+        path = [i]
+        while path[-1] > 0:
+            path.append(int(t["parent"][s][path[-1]]))
+        path = path[::-1] if i > 0 else [0]
+        rows_np[s, : len(path)] = path
+        alen_np[s] = len(path) - 1
+    if acc_override is not None:
+        alen_np = np.where(acc_override < 0, -1, alen_np)
+    acc = {"acc_rows": up_int(rows_np), "acc_len": up_int(alen_np)}
+    kv_np, kv_dev = [], []
+    for _ in range(n_kv):
+        a = synth.attention_inputs(rng, n, T, 2 * Hkv, Hkv, D, Pmax)
+        d = {k: up(a[k], dtype)[0] for k in ("k_tree", "v_tree", "k_cache", "v_cache")}
+        kv_dev.append((d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"]))
+        kv_np.append({k: down(v) for k, v in d.items()})
+    gd_np, gd_dev = [], []
+    for _ in range(n_gdn):
+        Ssc = up(rng.standard_normal((n, T, H, dk, dk)).astype(np.float32), "f32")[0]
+        S = up(rng.standard_normal((n, H, dk, dk)).astype(np.float32), "f32")[0]
+        csc = up(rng.standard_normal((n, T, W - 1, C)).astype(np.float32), dtype)[0]
+        cst = up(rng.standard_normal((n, W - 1, C)).astype(np.float32), dtype)[0]
+        gd_dev.append((Ssc, S, csc, cst))
+        gd_np.append(dict(S_scratch=down(Ssc), S=down(S), conv_scratch=down(csc), conv_state=down(cst)))
+    pl = up_int(prefix)
+    ddt.commit(acc["acc_rows"], acc["acc_len"], pl, kv_dev, gd_dev, B=B)
+    torch.cuda.synchronize()
+    for s in range(n):
+        kv_s = [{k: v[s] for k, v in lay.items()} for lay in kv_np]
+        gd_s = [{k: v[s] for k, v in lay.items()} for lay in gd_np]
+        P2, a2, kv2, gd2 = ocommit.commit(rows_np[s], alen_np[s], prefix[s], kv_s, gd_s, Pmax)
+        assert down(pl)[s] == P2 and down(acc["acc_len"])[s] == a2
+        for j, (_, _, kc, vc) in enumerate(kv_dev):
+            np.testing.assert_array_equal(down(kc)[s], kv2[j]["k_cache"])
+            np.testing.assert_array_equal(down(vc)[s], kv2[j]["v_cache"])
+        for j, (_, S, _, cst) in enumerate(gd_dev):
+            np.testing.assert_array_equal(down(S)[s], gd2[j]["S"])
+            np.testing.assert_array_equal(down(cst)[s], gd2[j]["conv_state"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_commit_bit_exact(dtype):
+    say("commit", dtype)
+    commit_case(1, 3, 2, 3, dtype, np.array([10, 0, 33]), 48)
+
+
+def test_commit_many_layers_and_guards():
+    # more layers than one launch carries; sequence 1 overflows Pmax; sequence 2 had a failed walk
+    commit_case(2, 3, 18, 20, "bf16", np.array([5, 47, 7]), 48, acc_override=np.array([0, 0, -1]))

@@ -1,0 +1,108 @@
+"""GPU parity of ddt_tree_attn against the oracle's dense masked softmax.
+
+fp32 within 1e-5, bf16 within atol 2e-2 / rtol 1e-2 (elementwise).  Small cases are
+compared in full; the full-size shapes (prefix 8192 / 32768 / 131072, 24 q heads over
+4 kv heads, head_dim 256, 65 tree rows) on rows sampled from every tree depth, which
+the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from oracle import tree as otree
+from tests.gpu_util import anc_tensor, assert_close, down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def make_tree(rng, n, B, L, kind="random"):
+    if kind == "lopsided":
+        parent, _ = synth.lopsided_parents()
+        parents = np.stack([parent] * n)
+    elif kind == "chain":
+        parents = np.stack([np.arange(-1, B)] * n)
+    else:
+        parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    anc = np.stack([otree.ancestor_masks(p) for p in parents])
+    return parents, anc
+
+
+def run_case(seed, n, B, L, Hq, Hkv, D, Pmax, prefix, dtype, kind="random", rows=None, scale=0.0):
+    rng = np.random.default_rng(seed)
+    parents, anc = make_tree(rng, n, B, L, kind)
+    x = synth.attention_inputs(rng, n, B + 1, Hq, Hkv, D, Pmax)
+    dv = {k: up(v, dtype) for k, v in x.items()}
+    pl = np.asarray(prefix, dtype=np.int64)
+    out = ddt.tree_attn(dv["q"][0], dv["k_cache"][0], dv["v_cache"][0], up_int(pl), dv["k_tree"][0],
+                        dv["v_tree"][0], anc_tensor(anc), scale=scale)
+    torch.cuda.synchronize()
+    got = down(out)
+    ex = {k: v[1] for k, v in dv.items()}
+    sc = None if scale <= 0 else scale
+    if callable(rows):
+        rows = rows(parents[0])
+    for s in range(n):
+        if rows is None:
+            ref = oattn.tree_attention(ex["q"][s], ex["k_cache"][s], ex["v_cache"][s], pl[s], ex["k_tree"][s],
+                                       ex["v_tree"][s], anc[s], sc)
+            assert_close(got[s], ref, dtype, "seq %d" % s)
+        else:
+            for i in rows:
+                ref = oattn.tree_attention_row(ex["q"][s][i], ex["k_cache"][s], ex["v_cache"][s], pl[s],
+                                               ex["k_tree"][s], ex["v_tree"][s], anc[s][i], sc)
+                assert_close(got[s][i], ref, dtype, "seq %d row %d" % (s, i))
+    return got
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tiny_fp32(seed):
+    # 2 q heads / 1 kv head, head_dim 64, prefix 128, budget 8
+    say("tree_attn tiny fp32 seed", seed)
+    run_case(seed, 2, 8, 4, 2, 1, 64, 128, [128, 128], "f32")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_fp32_head_sizes(D):
+    run_case(10 + D, 2, 12, 5, 4, 2, D, 300, [300, 173], "f32")
+
+
+@pytest.mark.parametrize("D,P", [(256, 1000), (256, 1024), (128, 777), (64, 200)])
+def test_bf16_small_full_compare(D, P):
+    # several key tiles with a ragged tail; 24/4 heads, 65 rows
+    say("tree_attn bf16 D=%d P=%d" % (D, P))
+    run_case(20 + P, 2, 64, 15, 24, 4, D, P + 40, [P, P // 3], "bf16")
+
+
+def test_bf16_gqa_and_small_budget():
+    run_case(31, 2, 32, 15, 8, 1, 256, 600, [600, 599], "bf16")    # G = 8, B = 32
+    run_case(32, 1, 0, 1, 4, 4, 256, 333, [333], "bf16")           # B = 0 (root only), G = 1
+    run_case(33, 2, 5, 3, 16, 2, 128, 100, [0, 64], "bf16")        # empty prefix on one sequence
+    run_case(34, 1, 64, 15, 24, 4, 256, 512, [512], "bf16", kind="chain")
+    run_case(35, 1, 20, 6, 6, 2, 256, 256, [256], "bf16", scale=0.02)
+
+
+def sample_rows(parents):
+    depth = [0] * len(parents)
+    for i in range(1, len(parents)):
+        depth[i] = depth[parents[i]] + 1
+    rows, seen = [0], {0}
+    for i in range(1, len(parents)):
+        if depth[i] not in seen:
+            seen.add(depth[i])
+            rows.append(i)
+    return rows + [len(parents) - 1]
+
+
+@pytest.mark.parametrize("n,P", [(1, 8192), (8, 8192), (1, 32768)])
+def test_bf16_full_size_sampled(n, P):
+    say("tree_attn bf16 full size n=%d P=%d (sampled rows)" % (n, P))
+    run_case(40 + n + P, n, 64, 15, 24, 4, 256, P + 64, [P] * n, "bf16", rows=lambda p: sample_rows(p)[:6])
+
+
+def test_bf16_long_context_lopsided():
+    say("tree_attn bf16 P=131072 lopsided tree (sampled rows)")
+    rows = [0, 2, 15, 16, 64]
+    run_case(77, 1, 64, 15, 24, 4, 256, 131072, [131072], "bf16", kind="lopsided", rows=rows)

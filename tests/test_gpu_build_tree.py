@@ -1,0 +1,124 @@
+"""GPU parity of ddt_build_tree against the oracle: topology bit-exact, scores within
+fp32 rounding of the fp64 oracle.
+
+Inputs: drafter logits drawn by synth (config-style N(0,2) fp32 vocab 512 depth 4;
+bf16 N(0,3) vocab 151936 depth 15 with planted peaks), redrawn by the oracle's gap
+guard until the best B+1 prefixes are separated by more than 1e-4.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gaps
+from oracle import tree as otree
+from tests.gpu_util import anc_numpy, down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_and_compare(z32, dtype, B, root, K=0, score_rtol=2e-6):
+    zt, zexact = up(z32, dtype)
+    n = z32.shape[0]
+    out = ddt.build_tree(zt, B, up_int(root), K=K)
+    torch.cuda.synchronize()
+    ref = otree.build_tree_batch(zexact, B, root, K=None if K == 0 else K)
+    for s in range(n):
+        for key in ("tok", "parent", "depth"):
+            np.testing.assert_array_equal(down(out[key])[s], ref[key][s], err_msg="%s seq %d" % (key, s))
+        np.testing.assert_array_equal(anc_numpy(out["anc"])[s], ref["anc"][s], err_msg="anc seq %d" % s)
+        sc = down(out["score"])[s]
+        used = ref["tok"][s] >= 0
+        np.testing.assert_allclose(sc[used], ref["score"][s][used], rtol=score_rtol, atol=1e-5)
+        assert np.isneginf(sc[~used]).all()
+    return out, ref
+
+
+@pytest.mark.parametrize("seed", range(0, 40, 4))
+def test_tiny_fp32(seed):
+    say("build_tree tiny fp32 seed", seed)
+    s, z, _ = gaps.first_gapped_seed(lambda t: (synth.draft_logits(np.random.default_rng(t), 3, 4, 512, 2.0), None),
+                                     8, seed)
+    run_and_compare(z, "f32", 8, np.array([5, 6, 7]))
+
+
+@pytest.mark.parametrize("n,B,seed", [(1, 32, 0), (1, 64, 1), (16, 64, 2), (3, 32, 3)])
+def test_vocab151936_bf16(n, B, seed):
+    say("build_tree bf16 V=151936 L=15 n=%d B=%d seed %d" % (n, B, seed))
+
+    def make(t):
+        z = synth.draft_logits(np.random.default_rng(t), n, 15, 151936, 3.0, plant_p=0.6)
+        return synth.quantize(z, "bf16")[1], z
+
+    s, zq, z = gaps.first_gapped_seed(make, B, seed)
+    run_and_compare(z, "bf16", B, np.arange(n) + 11)
+
+
+def test_hand_example_ties():
+    g = json.load(open(os.path.join(GOLDEN, "tree_hand_example.json")))
+    z = np.log(np.array(g["logits_ln"], dtype=np.float64)).astype(np.float32)[None]
+    out, _ = run_and_compare(z, "f32", g["B"], np.array([g["root_token"]]))
+    assert down(out["tok"])[0].tolist() == g["tok"]
+    assert down(out["parent"])[0].tolist() == g["parent"]
+
+
+def test_exact_bf16_ties_by_token_id():
+    # integer logits: massive exact ties among siblings, broken by token id
+    rng = np.random.default_rng(7)
+    z = rng.integers(-4, 5, size=(2, 1, 3000)).astype(np.float32)
+    run_and_compare(z, "bf16", 64, np.array([0, 1]))
+
+    # tied first depth, continuous deeper depths (gap guard allows identical-value ties)
+    def make(t):
+        r = np.random.default_rng(t)
+        zz = (2.0 * r.standard_normal((2, 3, 3000))).astype(np.float32)
+        zz[:, 0] = r.integers(-4, 5, size=(2, 3000))
+        return synth.quantize(zz, "bf16")[1], zz
+
+    _, _, zz = gaps.first_gapped_seed(make, 48, 70)
+    run_and_compare(zz, "bf16", 48, np.array([0, 1]))
+
+
+@pytest.mark.parametrize("V", [1000, 5003, 16385])
+def test_ragged_vocab_fp32(V):
+    # vocab sizes that are not a multiple of the chunk or of 8
+    say("build_tree ragged V", V)
+    s, z, _ = gaps.first_gapped_seed(lambda t: (synth.draft_logits(np.random.default_rng(t), 2, 6, V, 2.0), None),
+                                     40, 100 + V)
+    run_and_compare(z, "f32", 40, np.array([1, 2]))
+
+
+def test_small_K_and_small_trees():
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((2, 6, 700)).astype(np.float32) * 2
+    run_and_compare(z, "f32", 20, np.array([3, 4]), K=4)       # --top-k 4
+    z2 = np.array([[[0.0, 1.0], [2.0, 0.0]]], dtype=np.float32)
+    out, ref = run_and_compare(z2, "f32", 10, np.array([0]))   # only 6 prefixes exist
+    assert (down(out["tok"])[0][7:] == -1).all()
+    z3 = rng.standard_normal((1, 1, 300)).astype(np.float32)
+    run_and_compare(z3, "f32", 64, np.array([0]))              # L = 1: top-64 of one row
+    run_and_compare(z3, "f32", 1, np.array([0]))               # B = 1
+
+
+def test_invariants_full_size_batch():
+    say("build_tree invariants n=16 B=64 V=151936")
+    rng = np.random.default_rng(21)
+    z = synth.draft_logits(rng, 16, 15, 151936, 3.0, plant_p=0.6)
+    zt, _ = up(z, "bf16")
+    out = ddt.build_tree(zt, 64, up_int(np.zeros(16)))
+    tok, par, dep, anc = down(out["tok"]), down(out["parent"]), down(out["depth"]), anc_numpy(out["anc"])
+    sc = down(out["score"])
+    for s in range(16):
+        assert (tok[s] >= 0).all()
+        for i in range(1, 65):
+            p = par[s, i]
+            assert 0 <= p < i and dep[s, i] == dep[s, p] + 1
+            assert anc[s, i] == anc[s, p] | np.uint64(1 << (i - 1))
+            assert sc[s, i] <= sc[s, i - 1]
+        sib = set(zip(par[s, 1:].tolist(), tok[s, 1:].tolist()))
+        assert len(sib) == 64

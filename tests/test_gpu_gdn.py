@@ -1,0 +1,76 @@
+"""GPU parity of ddt_gdn_tree_step against the oracle's tree recurrence.
+
+o within the activation dtype's tolerance (fp32 1e-5; bf16 2e-2 / 1e-2); the fp32
+state scratch within 1e-5 (its inputs are exact in both dtypes, so only fp32
+rounding separates it from the fp64 oracle); the conv scratch bit-exact (copies).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gdn as ogdn
+from tests.gpu_util import assert_close, down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(seed, n, B, L, H, dk, W, dtype, kind="random", check_heads=None):
+    rng = np.random.default_rng(seed)
+    if kind == "lopsided":
+        parents = np.stack([synth.lopsided_parents()[0]] * n)
+    elif kind == "unused":
+        parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+        parents[:, B - 3:] = -1  # rows left unused by the build read the committed state
+    else:
+        parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, W)
+    xt, xe = up(x["x"], dtype)
+    vt, ve = up(x["v"], dtype)
+    cst, cse = up(x["conv_state"], dtype)
+    f32 = lambda a: up(a, "f32")
+    (bt, be), (gt, ge), (St, Se), (wt, we) = f32(x["beta"]), f32(x["g"]), f32(x["S"]), f32(x["conv_w"])
+    out = ddt.gdn_tree_step(xt, wt, cst, vt, bt, gt, St, up_int(parents), L)
+    torch.cuda.synchronize()
+    o, Ssc, csc = down(out["o"]), down(out["S_scratch"]), down(out["conv_scratch"])
+    for s in range(n):
+        ro, rS, rc = ogdn.gdn_tree_step(xe[s], we, cse[s], ve[s], be[s], ge[s], Se[s], parents[s], H, dk)
+        hs = slice(None) if check_heads is None else check_heads
+        assert_close(o[s][:, hs], ro[:, hs], dtype, "o seq %d" % s)
+        assert_close(Ssc[s][:, hs], rS[:, hs], "f32", "S_scratch seq %d" % s)
+        np.testing.assert_array_equal(csc[s], rc, err_msg="conv_scratch seq %d" % s)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tiny_fp32(seed):
+    # 1 head, dk = dv = 32, conv width 4 over 64 channels, budget 8
+    say("gdn tiny fp32 seed", seed)
+    run_case(seed, 2, 8, 4, 1, 32, 4, "f32")
+
+
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_head_sizes_fp32(dk):
+    run_case(10 + dk, 2, 20, 6, 2, dk, 4, "f32")
+
+
+@pytest.mark.parametrize("W", [2, 3, 8])
+def test_conv_widths(W):
+    run_case(20 + W, 2, 16, 10, 2, 32, W, "bf16")
+
+
+def test_bf16_config_shape():
+    # 32 heads, dk = dv = 128, conv width 4 over 8192 channels, 65 rows, depth <= 15
+    say("gdn bf16 H=32 dk=128 C=8192 B=64 n=2")
+    run_case(30, 2, 64, 15, 32, 128, 4, "bf16")
+
+
+def test_lopsided_and_unused_rows():
+    run_case(31, 1, 64, 15, 4, 128, 4, "bf16", kind="lopsided")
+    run_case(32, 2, 24, 8, 2, 64, 4, "f32", kind="unused")
+
+
+def test_full_batch_sampled_heads():
+    say("gdn bf16 n=8 H=32 dk=128 (heads 0, 17, 31 checked)")
+    run_case(33, 8, 64, 15, 32, 128, 4, "bf16", check_heads=[0, 17, 31])

@@ -1,0 +1,65 @@
+// Internal launchers: one per kernel family, called by the C ABI in api.hip after
+// validation.  Each returns the result of hipGetLastError() after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ddt.h"
+
+namespace ddt {
+
+// ---- tree build
+struct BuildPlan {
+  int S;          // chunks per (sequence, depth) row
+  int chunk;      // elements per chunk (multiple of 8)
+  int K;          // candidates per depth
+  int sortN;      // power of two >= S*K (merge sort size)
+  size_t off_ckey, off_cid, off_stat, off_tid, off_tlp, total;
+};
+BuildPlan plan_build_tree(int n, int L, int V, int B, int K);
+hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, int B,
+                             const BuildPlan& plan, const int32_t* root_token, int32_t* tok,
+                             int32_t* parent, int32_t* depth, float* score, uint64_t* anc,
+                             void* ws, hipStream_t st);
+
+// ---- tree attention
+struct AttnPlan {
+  bool mfma;      // bf16 matrix-core path (else the scalar path, no workspace)
+  int G, R, ntiles, nwg, nsplit, split_len;
+  size_t off_lse, off_o, total;
+};
+AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);
+hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                            const uint64_t* anc, int n, int T, int Hq, int Hkv, int D, int Pmax,
+                            float scale, int dt, void* out, const AttnPlan& plan, void* ws,
+                            hipStream_t st);
+
+// ---- GDN tree step
+hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,
+                                void* conv_scratch, const void* v, const float* beta,
+                                const float* g, const float* S, float* S_scratch, void* o,
+                                const int32_t* parent, int n, int T, int L, int H, int dk, int C,
+                                int W, int act_dt, hipStream_t st);
+
+// ---- tree walk
+struct AcceptPlan {
+  int S;          // chunks per row for the argmax scan
+  int chunk;
+  size_t total;
+};
+AcceptPlan plan_tree_accept(int n, int B, int V);
+hipError_t launch_tree_accept(const void* logits, int dt, const int32_t* tok,
+                              const int32_t* parent, int n, int T, int L, int V,
+                              int32_t* acc_rows, int32_t* acc_len, int32_t* bonus,
+                              const AcceptPlan& plan, void* ws, hipStream_t st);
+
+// ---- commit
+hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
+                         const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_esize,
+                         const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
+                         int act_esize, int n, int T, int L, hipStream_t st);
+
+}  // namespace ddt

@@ -1,0 +1,188 @@
+"""One DDTree verify round on the GPU: tree build -> every layer of the hybrid
+stack -> greedy tree walk -> accepted-path commit, all enqueued on the current
+stream through libddt (no host synchronisation inside a round).
+
+Sources: "DDTree on vLLM: candid research notes", section "Why hybrid attention
+makes it hard" (tree attention, branch-local recurrent state, accepted-path
+commit); "The architecture of speculation", section "The DDTree Integration
+Challenge" (drafting, tree construction, tree attention, compaction); "From DDTree
+to drafter training", section "The Architecture of DDTree".
+
+There are no dense projections between layers: every layer consumes its own
+inputs (queries / tree keys and values for attention, x, v, beta, g for GDN), so
+a round exercises exactly the kernels of the verify path.  The round's bonus token
+is fed back as the next round's root token, and each commit grows the prefix.
+"""
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import ddt
+
+
+@dataclass
+class HybridConfig:
+    n: int = 8                 # sequences
+    V: int = 151936            # vocabulary
+    L: int = 15                # drafter depth
+    B: int = 64                # tree budget (non-root nodes)
+    K: int = 0                 # candidates per depth (0 = B)
+    prefix: int = 16384        # committed prefix at the first round
+    extra_cap: int = 1024      # cache rows beyond the prefix (room for commits)
+    n_attn: int = 16
+    n_gdn: int = 48
+    Hq: int = 24
+    Hkv: int = 4
+    D: int = 256
+    H: int = 32
+    dk: int = 128
+    W: int = 4
+    dtype: torch.dtype = torch.bfloat16
+    pattern: list = field(default_factory=list)  # "gdn"/"attn" per layer; default [gdn, gdn, gdn, attn]*
+
+    def layer_pattern(self):
+        if self.pattern:
+            return list(self.pattern)
+        out, a, g = [], 0, 0
+        while a < self.n_attn or g < self.n_gdn:
+            for _ in range(3):
+                if g < self.n_gdn:
+                    out.append("gdn")
+                    g += 1
+            if a < self.n_attn:
+                out.append("attn")
+                a += 1
+        return out
+
+    @property
+    def T(self):
+        return self.B + 1
+
+    @property
+    def C(self):
+        return 2 * self.H * self.dk
+
+    @property
+    def Pmax(self):
+        return self.prefix + self.extra_cap
+
+
+class HybridVerifyStep:
+    """Device buffers of a hybrid verify round and the round itself.
+
+    Inputs are filled by the caller (``fill_*`` helpers below use the device RNG);
+    outputs and workspaces are allocated once here.
+    """
+
+    def __init__(self, cfg: HybridConfig, device="cuda:0"):
+        self.cfg = c = cfg
+        self.dev = dev = torch.device(device)
+        n, T, dt = c.n, c.T, c.dtype
+        e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)
+        self.draft_logits = e(n, c.L, c.V)
+        self.target_logits = e(n, T, c.V)
+        self.root_token = torch.zeros(n, dtype=torch.int32, device=dev)
+        self.prefix_len = torch.full((n,), c.prefix, dtype=torch.int32, device=dev)
+        self.attn = [dict(q=e(n, T, c.Hq, c.D), k_tree=e(n, c.Hkv, T, c.D), v_tree=e(n, c.Hkv, T, c.D),
+                          k_cache=e(n, c.Hkv, c.Pmax, c.D), v_cache=e(n, c.Hkv, c.Pmax, c.D),
+                          out=e(n, T, c.Hq, c.D)) for _ in range(c.n_attn)]
+        self.gdn = [dict(x=e(n, T, c.C), v=e(n, T, c.H, c.dk), beta=e(n, T, c.H, dtype=torch.float32),
+                         g=e(n, T, c.H, dtype=torch.float32), S=e(n, c.H, c.dk, c.dk, dtype=torch.float32),
+                         conv_state=e(n, c.W - 1, c.C), conv_w=e(c.C, c.W, dtype=torch.float32),
+                         out={"o": e(n, T, c.H, c.dk), "S_scratch": e(n, T, c.H, c.dk, c.dk, dtype=torch.float32),
+                              "conv_scratch": e(n, T, c.W - 1, c.C)})
+                    for _ in range(c.n_gdn)]
+        self.tree = {"tok": e(n, T, dtype=torch.int32), "parent": e(n, T, dtype=torch.int32),
+                     "depth": e(n, T, dtype=torch.int32), "score": e(n, T, dtype=torch.float32),
+                     "anc": e(n, T, dtype=torch.int64)}
+        self.acc = {"acc_rows": e(n, c.L + 1, dtype=torch.int32), "acc_len": e(n, dtype=torch.int32),
+                    "bonus": e(n, dtype=torch.int32)}
+        u8 = lambda nb: torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        self.ws_build = u8(ddt.build_tree_workspace(n, c.L, c.V, c.B, c.K))
+        self.ws_attn = u8(ddt.tree_attn_workspace(n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, dt))
+        self.ws_acc = u8(ddt.tree_accept_workspace(n, c.B, c.V))
+        self.pattern = c.layer_pattern()
+
+    # ------------------------------------------------------------ the round
+    def build(self):
+        c = self.cfg
+        ddt.build_tree(self.draft_logits, c.B, self.root_token, K=c.K, ws=self.ws_build, out=self.tree)
+
+    def layers(self):
+        ia = ig = 0
+        for kind in self.pattern:
+            if kind == "attn":
+                a = self.attn[ia]
+                ia += 1
+                ddt.tree_attn(a["q"], a["k_cache"], a["v_cache"], self.prefix_len, a["k_tree"], a["v_tree"],
+                              self.tree["anc"], ws=self.ws_attn, out=a["out"])
+            else:
+                g = self.gdn[ig]
+                ig += 1
+                ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"], g["beta"], g["g"], g["S"],
+                                  self.tree["parent"], self.cfg.L, out=g["out"])
+
+    def accept(self):
+        ddt.tree_accept(self.target_logits, self.tree["tok"], self.tree["parent"], self.cfg.L,
+                        ws=self.ws_acc, out=self.acc)
+
+    def commit(self):
+        ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len,
+                   [(a["k_tree"], a["v_tree"], a["k_cache"], a["v_cache"]) for a in self.attn],
+                   [(g["out"]["S_scratch"], g["S"], g["out"]["conv_scratch"], g["conv_state"]) for g in self.gdn],
+                   B=self.cfg.B)
+        # the bonus token of this round is the root of the next one
+        self.root_token.copy_(self.acc["bonus"])
+
+    def __call__(self):
+        self.build()
+        self.layers()
+        self.accept()
+        self.commit()
+
+    # ------------------------------------------------------------ seeded synthetic inputs
+    def fill_random(self, seed=0, draft_sigma=3.0, plant_p=0.6, target_sigma=3.0, target_plant=0.7):
+        """Seeded device-side draws with the workload's distributions; the target
+        plant uses the tree of the current drafter logits (built once here)."""
+        c, dev = self.cfg, self.dev
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        rn = lambda *s: torch.randn(*s, generator=gen, device=dev, dtype=torch.float32)
+        ru = lambda *s: torch.rand(*s, generator=gen, device=dev, dtype=torch.float32)
+        z = draft_sigma * rn(c.n, c.L, c.V)
+        hit = ru(c.n, c.L) < plant_p
+        where = torch.randint(0, c.V, (c.n, c.L), generator=gen, device=dev)
+        zmax = z.amax(dim=-1)
+        zi = z.view(-1, c.V)
+        rows = torch.nonzero(hit.view(-1)).flatten()
+        zi[rows, where.view(-1)[rows]] = zmax.view(-1)[rows] + 8.0
+        self.draft_logits.copy_(z)
+        del z, zi
+        for a in self.attn:
+            for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache"):
+                a[k].copy_(rn(*a[k].shape))
+        for g in self.gdn:
+            g["x"].copy_(rn(*g["x"].shape))
+            g["v"].copy_(rn(*g["v"].shape))
+            g["beta"].copy_(ru(*g["beta"].shape))
+            g["g"].copy_(0.9 + 0.1 * ru(*g["g"].shape))
+            g["S"].copy_(rn(*g["S"].shape) / c.dk ** 0.5)
+            g["conv_state"].copy_(rn(*g["conv_state"].shape))
+            g["conv_w"].copy_((2 * ru(*g["conv_w"].shape) - 1) / c.W ** 0.5)
+        # target: N(0, sigma); rows at depth d get the drafter's top-1 of depth d+1 as argmax w.p. target_plant
+        self.build()
+        depth = self.tree["depth"].long()
+        top1 = self.draft_logits.float().argmax(dim=-1)               # [n][L]
+        y = target_sigma * rn(c.n, c.T, c.V)
+        thit = ru(c.n, c.L) < target_plant
+        for s in range(c.n):
+            for d in range(c.L):
+                if not bool(thit[s, d]):
+                    continue
+                rows_d = torch.nonzero(depth[s] == d).flatten()
+                if rows_d.numel():
+                    y[s, rows_d, top1[s, d]] = y[s, rows_d].amax(dim=-1) + 1.0
+        self.target_logits.copy_(y)
+        del y
+        torch.cuda.synchronize(dev)
