@@ -174,7 +174,7 @@ def main():
                 ig += 1
                 timed("gdn_tree_step", lambda: ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"],
                                                                  g["beta"], g["g"], g["S"], step.tree["parent"],
-                                                                 cfg.L, out=g["out"]))
+                                                                 cfg.L, ws=step.ws_gdn, out=g["out"]))
         timed("tree_accept", step.accept)
         timed("commit", step.commit)
 

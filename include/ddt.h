@@ -131,14 +131,17 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *   S [n][H][dv][dk] (f32, committed, read only), S_scratch [n][T][H][dv][dk] (f32, written)
  *   o [n][T][H][dv] (act_dt, written)
  *   parent [n][T] int32: parent[i] < i, or < 0 for a row that reads the committed state
- *   L: upper bound on the tree depth (row depth by parent chain), L <= 38
+ *   L: upper bound on the tree depth (row depth by parent chain), L <= 31; rows deeper
+ *      than L are not processed
+ *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q in fp32)
  * Built: dk = dv in {32, 64, 128}; W in [2, 8]; C == 2*H*dk.
  */
+size_t ddt_gdn_tree_step_workspace(int n, int B, int H, int dk);
 int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,
                       void* conv_scratch, const void* v, const float* beta, const float* g,
                       const float* S, float* S_scratch, void* o, const int32_t* parent,
                       int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
-                      void* stream);
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- tree walk
  * [arch]: after the verify pass, walk down from the root while the target's token

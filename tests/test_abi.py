@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -81,12 +81,14 @@ def test_tree_attn_validation():
 def test_gdn_validation():
     def args(**k):
         return [P] * 11 + [1, 8, k.get("L", 4), k.get("H", 1), k.get("dk", 32), k.get("dv", 32), k.get("C", 64),
-                           k.get("W", 4), k.get("dt", 0), None]
+                           k.get("W", 4), k.get("dt", 0), P, k.get("wsb", 1 << 30), None]
     assert status("ddt_gdn_tree_step", *args(C=63)) == ddt.DDT_ERR_ARG
     assert status("ddt_gdn_tree_step", *args(dk=48, dv=48, C=96)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_gdn_tree_step", *args(dv=64)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_gdn_tree_step", *args(W=9)) == ddt.DDT_ERR_UNSUPPORTED
-    assert status("ddt_gdn_tree_step", *args(L=36)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(L=32)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(wsb=64)) == ddt.DDT_ERR_WORKSPACE
+    assert ddt.gdn_tree_step_workspace(8, 64, 32, 128) > ddt.gdn_tree_step_workspace(1, 64, 32, 128) > 0
     assert status("ddt_gdn_tree_step", *args(dt=2)) == ddt.DDT_ERR_UNSUPPORTED
     a = args()
     a[0] = None

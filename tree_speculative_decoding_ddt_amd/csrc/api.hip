@@ -135,23 +135,37 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache, const
 }
 
 // ---------------------------------------------------------------- GDN tree step
-int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
-                      const float* beta, const float* g, const float* S, float* S_scratch, void* o,
-                      const int32_t* parent, int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
-                      void* stream) {
-  DDT_NEED(x); DDT_NEED(conv_w); DDT_NEED(conv_state); DDT_NEED(conv_scratch); DDT_NEED(v);
-  DDT_NEED(beta); DDT_NEED(g); DDT_NEED(S); DDT_NEED(S_scratch); DDT_NEED(o); DDT_NEED(parent);
+static int gdn_args(int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt) {
   DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && L >= 0 && H >= 1, DDT_ERR_ARG,
             "ddt_gdn_tree_step: need n>=1, 0<=B<=64, L>=0, H>=1 (got n=%d B=%d L=%d H=%d)", n, B, L, H);
-  DDT_CHECK(L <= 35, DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: depth bound L=%d exceeds 35", L);
+  DDT_CHECK(L <= 31, DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: depth bound L=%d exceeds 31", L);
   DDT_CHECK(dt_ok(act_dt), DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: dtype %d", act_dt);
   DDT_CHECK(dk == dv && (dk == 32 || dk == 64 || dk == 128), DDT_ERR_UNSUPPORTED,
             "ddt_gdn_tree_step: dk=%d dv=%d not built (dk == dv in {32, 64, 128})", dk, dv);
   DDT_CHECK(W >= 2 && W <= 8, DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: conv width W=%d not in [2, 8]", W);
   DDT_CHECK(C == 2 * H * dk, DDT_ERR_ARG, "ddt_gdn_tree_step: C=%d must equal 2*H*dk=%d", C, 2 * H * dk);
-  DDT_CHECK(aligned16(S) && aligned16(S_scratch), DDT_ERR_ARG, "ddt_gdn_tree_step: S buffers must be 16-byte aligned");
+  return DDT_OK;
+}
+
+size_t ddt_gdn_tree_step_workspace(int n, int B, int H, int dk) {
+  if (n < 1 || B < 0 || B > 64 || H < 1 || !(dk == 32 || dk == 64 || dk == 128)) return 0;
+  return ddt::gdn_workspace(n, B + 1, H, dk);
+}
+
+int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
+                      const float* beta, const float* g, const float* S, float* S_scratch, void* o,
+                      const int32_t* parent, int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
+                      void* ws, size_t ws_bytes, void* stream) {
+  DDT_NEED(x); DDT_NEED(conv_w); DDT_NEED(conv_state); DDT_NEED(conv_scratch); DDT_NEED(v);
+  DDT_NEED(beta); DDT_NEED(g); DDT_NEED(S); DDT_NEED(S_scratch); DDT_NEED(o); DDT_NEED(parent); DDT_NEED(ws);
+  const int st = gdn_args(n, B, L, H, dk, dv, C, W, act_dt);
+  if (st != DDT_OK) return st;
+  const size_t need = ddt::gdn_workspace(n, B + 1, H, dk);
+  DDT_CHECK(ws_bytes >= need, DDT_ERR_WORKSPACE, "ddt_gdn_tree_step: workspace %zu < %zu bytes", ws_bytes, need);
+  DDT_CHECK(aligned16(ws) && aligned16(S) && aligned16(S_scratch), DDT_ERR_ARG,
+            "ddt_gdn_tree_step: workspace and S buffers must be 16-byte aligned");
   return hip_status(ddt::launch_gdn_tree_step(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o,
-                                              parent, n, B + 1, L, H, dk, C, W, act_dt,
+                                              parent, n, B + 1, L, H, dk, C, W, act_dt, ws,
                                               static_cast<hipStream_t>(stream)),
                     "ddt_gdn_tree_step");
 }

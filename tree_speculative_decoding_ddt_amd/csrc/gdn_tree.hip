@@ -5,19 +5,23 @@
 // "The architecture of speculation", section "The DDTree Integration Challenge":
 // recurrent state is per branch, not shared.
 //
-// Per node i (parent p; the committed state when p < 0), per head h:
+// Per node i (parent p; the committed state when p is not an earlier row), head h:
 //   window = [conv state of p (W-1 rows), x_i];  y = SiLU(sum_j w[c][j] window[j][c])
 //   q = y[q-channels of h] * dk^-1/2;  k = y[k-channels of h] / sqrt(|k|^2 + 1e-6)
 //   S_i = g S_p + beta (v - g S_p k) k^T;  o_i = S_i q = g (S_p q) + beta (v - g S_p k) (k.q)
 //
-// Layout of the work: a block owns one (sequence, head) and R consecutive rows of
-// the [dv][dk] state; a thread owns 4 consecutive columns of one row, so the two
-// row dot products (S_p k, S_p q) reduce across dk/4 lanes.  Rows of S evolve
-// independently, so the tree dependency never crosses blocks.  Nodes are visited in
-// depth-first order: the parent's state is then always the newest one written at
-// depth d-1, so each thread keeps a private stack of (L+1) float4 slots in LDS,
-// indexed by depth -- no state is re-read from memory.  Every node's state still
-// goes to S_scratch (the scratch contract), as 16-byte stores.
+// Two kernels:
+//  gdn_conv   grid (n*T, H), one thread per channel of the head's q|k (2*dk): gathers
+//             the node's conv window along its parent chain, writes the conv scratch
+//             (exact copies), and leaves q (scaled), k (normalised) and k.q in fp32 in
+//             the workspace.  Every node is independent here.
+//  gdn_state  grid (n*H, dv/R): a block owns R rows of one head's [dv][dk] state, a
+//             thread CPT consecutive columns of one row.  The block loads every node's
+//             q, k, k.q, v, g, beta into LDS, orders the nodes depth-first (in parallel:
+//             subtree sizes and sibling offsets), then walks them with no barrier:
+//             the parent's state is the newest one at depth d-1, held in a register
+//             stack indexed by the (wave-uniform) depth.  Each node's state is written
+//             once to S_scratch; nothing is re-read from memory.
 #include <math.h>
 
 #include "common.h"
@@ -25,174 +29,282 @@
 
 namespace ddt {
 
-constexpr int kGdnThreads = 256;
-constexpr int kGdnMaxW = 8;
 constexpr int kGdnMaxT = 128;
+constexpr int kGdnMaxW = 8;
 
+// ------------------------------------------------------------------ conv + q/k
 template <typename A, int DK>
-__global__ void __launch_bounds__(kGdnThreads) gdn_tree_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
-                                                               const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
-                                                               const A* __restrict__ v, const float* __restrict__ beta,
-                                                               const float* __restrict__ g, const float* __restrict__ S,
-                                                               float* __restrict__ S_scratch, A* __restrict__ o,
-                                                               const int32_t* __restrict__ parent, int Tn, int L, int H,
-                                                               int C, int W) {
+__global__ void __launch_bounds__(2 * DK) gdn_conv_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
+                                                          const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
+                                                          const int32_t* __restrict__ parent, int Tn, int H, int C, int W,
+                                                          float* __restrict__ qk, float* __restrict__ kq) {
+  const int s = blockIdx.x / Tn, u = blockIdx.x % Tn, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const bool is_k = tid >= DK;
+  const int ch = is_k ? H * DK + h * DK + (tid - DK) : h * DK + tid;
+
+  // Window rows newest first (back b = 0 is the node itself), walking the parent
+  // chain; past the root come the committed conv-state rows, newest first.  Tap
+  // W-1-b multiplies back b; backs 0..W-2 are the node's conv state (slot W-2-b).
+  float acc = 0.f;
+  int cur = u, in_tree = 1, beyond = 0;
+#pragma unroll
+  for (int b = 0; b < kGdnMaxW; ++b) {
+    if (b < W) {
+      int r = u;
+      if (b > 0) {
+        if (in_tree) {
+          const int p = parent[(size_t)s * Tn + cur];
+          if (p >= 0 && p < cur) cur = p;
+          else in_tree = 0;
+        }
+        r = in_tree ? cur : -(1 + (W - 1 - (++beyond)));
+      }
+      const A val = r >= 0 ? x[((size_t)s * Tn + r) * C + ch] : conv_state[((size_t)s * (W - 1) + (-r - 1)) * C + ch];
+      acc += conv_w[(size_t)ch * W + (W - 1 - b)] * Elem<A>::load(&val, 0);
+      if (b <= W - 2) conv_scratch[(((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C + ch] = val;
+    }
+  }
+  const float y = acc / (1.f + __expf(-acc));
+
+  __shared__ float ys[2 * DK];
+  __shared__ float red[2][2 * DK / 64 + 1];
+  ys[tid] = y;
+  __syncthreads();
+  float kk = 0.f, kqv = 0.f;
+  if (tid < DK) {
+    const float kv = ys[DK + tid];
+    kk = kv * kv;
+    kqv = kv * ys[tid];
+  }
+  kk = wave_sum(kk);
+  kqv = wave_sum(kqv);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = kk;
+    red[1][tid >> 6] = kqv;
+  }
+  __syncthreads();
+  float skk = 0.f, skq = 0.f;
+  for (int w = 0; w < (2 * DK + 63) / 64; ++w) {
+    skk += red[0][w];
+    skq += red[1][w];
+  }
+  const float rn = 1.f / sqrtf(skk + 1e-6f);
+  const float qs = rsqrtf((float)DK);
+  const size_t base = (((size_t)s * Tn + u) * H + h) * 2 * DK;
+  qk[base + tid] = is_k ? y * rn : y * qs;
+  if (tid == 0) kq[((size_t)s * Tn + u) * H + h] = skq * rn * qs;
+}
+
+// ------------------------------------------------------------------ state walk
+typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef float fv8 __attribute__((ext_vector_type(8)));
+template <int N> struct VecT;
+template <> struct VecT<4> { typedef fv4 type; };
+template <> struct VecT<8> { typedef fv8 type; };
+
+// A stack of LMAX states (one CPT-wide vector per thread) kept in registers: one
+// named member per depth and a switch on the wave-uniform depth, so no level is
+// ever addressed through memory.
+#define DDT_L16(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15)
+#define DDT_L32(X) DDT_L16(X) X(16) X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24) X(25) X(26) X(27) X(28) \
+  X(29) X(30) X(31)
+#define DDT_DECL(i) V v##i;
+#define DDT_GET(i) case i: return v##i;
+#define DDT_PUT(i) case i: v##i = x; break;
+
+template <int LMAX, typename V> struct RegStack;
+template <typename V> struct RegStack<16, V> {
+  DDT_L16(DDT_DECL)
+  __device__ __forceinline__ V get(int d) const {
+    switch (d) { DDT_L16(DDT_GET) default: return v0; }
+  }
+  __device__ __forceinline__ void put(int d, V x) {
+    switch (d) { DDT_L16(DDT_PUT) default: break; }
+  }
+};
+template <typename V> struct RegStack<32, V> {
+  DDT_L32(DDT_DECL)
+  __device__ __forceinline__ V get(int d) const {
+    switch (d) { DDT_L32(DDT_GET) default: return v0; }
+  }
+  __device__ __forceinline__ void put(int d, V x) {
+    switch (d) { DDT_L32(DDT_PUT) default: break; }
+  }
+};
+#undef DDT_DECL
+#undef DDT_GET
+#undef DDT_PUT
+
+template <typename V, int N>
+__device__ __forceinline__ V load_vec(const float* p) {
+  V r;
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) {
+    const float4 w = reinterpret_cast<const float4*>(p)[j];
+    r[4 * j] = w.x; r[4 * j + 1] = w.y; r[4 * j + 2] = w.z; r[4 * j + 3] = w.w;
+  }
+  return r;
+}
+template <typename V, int N>
+__device__ __forceinline__ void store_vec(float* p, V x) {
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j)
+    reinterpret_cast<float4*>(p)[j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+}
+
+template <typename A, int DK, int CPT, int LMAX>
+__global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict__ qk, const float* __restrict__ kq,
+                                                        const A* __restrict__ v, const float* __restrict__ beta,
+                                                        const float* __restrict__ g, const float* __restrict__ S,
+                                                        float* __restrict__ S_scratch, A* __restrict__ o,
+                                                        const int32_t* __restrict__ parent, int Tn, int L, int H) {
+  typedef typename VecT<CPT>::type V;
   constexpr int DV = DK;
-  constexpr int LPR = DK / 4;              // lanes per state row
-  constexpr int R = kGdnThreads / LPR;     // state rows per block
+  constexpr int LPR = DK / CPT;          // lanes per state row
+  constexpr int R = 256 / LPR;           // state rows per block
   const int s = blockIdx.x / H, h = blockIdx.x % H;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int r = blockIdx.y * R + tid / LPR;
-  const int c0 = (tid % LPR) * 4;
-  const bool conv_writer = blockIdx.y == 0;
+  const int tid = threadIdx.x;
+  const int rl = tid / LPR;
+  const int r = blockIdx.y * R + rl;
+  const int c0 = (tid % LPR) * CPT;
 
-  extern __shared__ float4 stack[];        // [(L+1)][256]
-  __shared__ float qk[2][2 * DK];
-  __shared__ int par[kGdnMaxT], dep[kGdnMaxT], order[kGdnMaxT], first[kGdnMaxT], nxt[kGdnMaxT], stk[kGdnMaxT];
-  __shared__ int hrow[kGdnMaxT][kGdnMaxW];  // back b from node: tree row (>= 0) or -(1 + committed row)
-  __shared__ int n_order;
+  extern __shared__ float4 qk_s4[];      // [T][2*DK] floats: q then k of every node
+  float* qk_s = reinterpret_cast<float*>(qk_s4);
+  __shared__ float vv[kGdnMaxT][R];
+  __shared__ float gb[kGdnMaxT][3];      // g, beta, k.q
+  __shared__ int par[kGdnMaxT], dep[kGdnMaxT], sz[kGdnMaxT], esib[kGdnMaxT], order[kGdnMaxT];
 
-  for (int i = tid; i < Tn; i += kGdnThreads) {
-    par[i] = parent[(size_t)s * Tn + i];
-    first[i] = -1;
-    nxt[i] = -1;
+  // ---- inputs of every node into LDS (independent loads)
+  const float4* qk4 = reinterpret_cast<const float4*>(qk);
+  for (int idx = tid; idx < Tn * (2 * DK / 4); idx += 256) {
+    const int u = idx / (2 * DK / 4), c = idx % (2 * DK / 4);
+    qk_s4[idx] = qk4[(((size_t)s * Tn + u) * H + h) * (2 * DK / 4) + c];
   }
-  __syncthreads();
-  if (tid == 0) {
-    // child lists in increasing row order; a row whose parent is not an earlier row
-    // reads the committed state (the root, and rows left unused by the build)
-    for (int i = Tn - 1; i >= 1; --i) {
-      const int p = par[i];
-      if (p >= 0 && p < i) {
-        nxt[i] = first[p];
-        first[p] = i;
-      }
-    }
-    int cnt = 0;
-    for (int rt = 0; rt < Tn; ++rt) {
-      const int p = par[rt];
-      if (p >= 0 && p < rt) continue;
-      int sp = 0;
-      stk[sp++] = rt;
-      dep[rt] = 0;
-      for (int b = 1; b < W; ++b) hrow[rt][b] = -(1 + (W - 1 - b));
-      while (sp > 0) {
-        const int u = stk[--sp];
-        if (dep[u] > L) continue;  // deeper than the stated bound: not processed
-        order[cnt++] = u;
-        for (int c = first[u]; c >= 0; c = nxt[c]) {
-          dep[c] = dep[u] + 1;
-          hrow[c][1] = u;
-          for (int b = 2; b < W; ++b) hrow[c][b] = hrow[u][b - 1];
-          stk[sp++] = c;
-        }
-      }
-    }
-    n_order = cnt;
+  for (int idx = tid; idx < Tn * R; idx += 256) {
+    const int u = idx / R, j = idx % R;
+    vv[u][j] = Elem<A>::load(v, (((size_t)s * Tn + u) * H + h) * DV + blockIdx.y * R + j);
   }
-
-  // this thread's conv channel and taps (threads < 2*DK)
-  const bool conv_thread = tid < 2 * DK;
-  const int ch = tid < DK ? h * DK + tid : H * DK + h * DK + (tid - DK);
-  float wt[kGdnMaxW];
-#pragma unroll
-  for (int j = 0; j < kGdnMaxW; ++j) wt[j] = (conv_thread && j < W) ? conv_w[(size_t)ch * W + j] : 0.f;
+  for (int u = tid; u < Tn; u += 256) {
+    const size_t ti = ((size_t)s * Tn + u) * H + h;
+    gb[u][0] = g[ti];
+    gb[u][1] = beta[ti];
+    gb[u][2] = kq[ti];
+    par[u] = parent[(size_t)s * Tn + u];
+    sz[u] = 0;
+  }
+  // committed state slice of this thread (used by nodes at depth 0)
+  const V sc = load_vec<V, CPT>(&S[(((size_t)s * H + h) * DV + r) * DK + c0]);
   __syncthreads();
 
-  const float qscale = rsqrtf((float)DK);
-  const int norder = n_order;
-  for (int k = 0; k < norder; ++k) {
-    const int u = order[k];
-    const int d = dep[u];
-    const int buf = k & 1;
-    if (conv_thread) {
-      float acc = 0.f;
-      A win[kGdnMaxW];
-#pragma unroll
-      for (int j = 0; j < kGdnMaxW; ++j) {
-        if (j < W) {
-          const int back = W - 1 - j;
-          A val;
-          if (back == 0) {
-            val = x[((size_t)s * Tn + u) * C + ch];
-          } else {
-            const int hr = hrow[u][back];
-            val = hr >= 0 ? x[((size_t)s * Tn + hr) * C + ch]
-                          : conv_state[((size_t)s * (W - 1) + (-hr - 1)) * C + ch];
-          }
-          win[j] = val;
-          acc += wt[j] * Elem<A>::load(&val, 0);
-        }
-      }
-      qk[buf][tid] = acc / (1.f + __expf(-acc));
-      if (conv_writer) {
-#pragma unroll
-        for (int j = 1; j < kGdnMaxW; ++j)
-          if (j < W) conv_scratch[(((size_t)s * Tn + u) * (W - 1) + (j - 1)) * C + ch] = win[j];
-      }
+  // ---- depth-first order, computed in parallel over nodes
+  // a row whose parent is not an earlier row starts a tree of its own (reads the committed state)
+  int d_me = 0;
+  if (tid < Tn) {
+    int a = tid;
+    while (true) {
+      const int p = par[a];
+      atomicAdd(&sz[a], 1);
+      if (!(p >= 0 && p < a)) break;
+      a = p;
+      ++d_me;
     }
-    __syncthreads();
-
-    // |k|^2 and k.q over the head (every wave computes them)
-    float kk = 0.f, kq = 0.f;
-    for (int c = lane; c < DK; c += 64) {
-      const float kv = qk[buf][DK + c], qv = qk[buf][c];
-      kk += kv * kv;
-      kq += kv * qv;
+    dep[tid] = d_me;
+  }
+  __syncthreads();
+  if (tid < Tn) {
+    const int p = par[tid];
+    const int vp = (p >= 0 && p < tid) ? p : -1;
+    int e = 0;
+    for (int j = 0; j < tid; ++j) {
+      const int pj = par[j];
+      const int vpj = (pj >= 0 && pj < j) ? pj : -1;
+      if (vpj == vp) e += sz[j];
     }
-    kk = wave_sum(kk);
-    kq = wave_sum(kq);
-    const float rn = 1.f / sqrtf(kk + 1e-6f);
-    const float kqn = kq * rn * qscale;
+    esib[tid] = e;
+  }
+  __syncthreads();
+  if (tid < Tn) {
+    int pos = d_me, a = tid;
+    while (true) {
+      pos += esib[a];
+      const int p = par[a];
+      if (!(p >= 0 && p < a)) break;
+      a = p;
+    }
+    order[pos] = tid;
+  }
+  __syncthreads();
 
-    const float4 kr = *reinterpret_cast<const float4*>(&qk[buf][DK + c0]);
-    const float4 qr = *reinterpret_cast<const float4*>(&qk[buf][c0]);
-    const float k4[4] = {kr.x * rn, kr.y * rn, kr.z * rn, kr.w * rn};
-    const float q4[4] = {qr.x * qscale, qr.y * qscale, qr.z * qscale, qr.w * qscale};
-    const float4 spv = d == 0 ? *reinterpret_cast<const float4*>(&S[(((size_t)s * H + h) * DV + r) * DK + c0])
-                              : stack[(d - 1) * kGdnThreads + tid];
-    const float sp[4] = {spv.x, spv.y, spv.z, spv.w};
+  // ---- walk
+  RegStack<LMAX, V> stk;
+  for (int k = 0; k < Tn; ++k) {
+    const int u = __builtin_amdgcn_readfirstlane(order[k]);
+    const int d = __builtin_amdgcn_readfirstlane(dep[u]);
+    if (d > L) continue;  // deeper than the stated bound: not processed
+    const V qv = load_vec<V, CPT>(&qk_s[u * 2 * DK + c0]);
+    const V kv = load_vec<V, CPT>(&qk_s[u * 2 * DK + DK + c0]);
+    const V sp = d == 0 ? sc : stk.get(d - 1);
     float a = 0.f, b = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a += sp[e] * k4[e];
-      b += sp[e] * q4[e];
+    for (int e = 0; e < CPT; ++e) {
+      a += sp[e] * kv[e];
+      b += sp[e] * qv[e];
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) {
       a += __shfl_xor(a, off, 64);
       b += __shfl_xor(b, off, 64);
     }
+    const float gi = gb[u][0], bi = gb[u][1];
+    const float delta = bi * (vv[u][rl] - gi * a);
+    const V sn = gi * sp + delta * kv;
+    stk.put(d, sn);
     const size_t ti = ((size_t)s * Tn + u) * H + h;
-    const float gi = g[ti], bi = beta[ti];
-    const float vr = Elem<A>::load(v, ti * DV + r);
-    const float delta = bi * (vr - gi * a);
-    float4 sn;
-    sn.x = gi * sp[0] + delta * k4[0];
-    sn.y = gi * sp[1] + delta * k4[1];
-    sn.z = gi * sp[2] + delta * k4[2];
-    sn.w = gi * sp[3] + delta * k4[3];
-    stack[d * kGdnThreads + tid] = sn;
-    *reinterpret_cast<float4*>(&S_scratch[((ti * DV) + r) * DK + c0]) = sn;
-    if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * kqn);
+    store_vec<V, CPT>(&S_scratch[(ti * DV + r) * DK + c0], sn);
+    if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * gb[u][2]);
+  }
+}
+
+size_t gdn_workspace(int n, int T, int H, int dk) {
+  const size_t qk = (size_t)n * T * H * 2 * dk * sizeof(float);
+  const size_t kq = (size_t)n * T * H * sizeof(float);
+  return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256;
+}
+
+template <typename A, int DK>
+static void launch_gdn(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
+                       const float* beta, const float* g, const float* S, float* S_scratch, void* o,
+                       const int32_t* parent, int n, int T, int L, int H, int C, int W, void* ws, hipStream_t st) {
+  constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread, depth bound < 16
+  constexpr int R = 256 / (DK / CPT);
+  constexpr int R4 = 256 / (DK / 4);      // 4 columns per thread, depth bound < 32
+  float* qk = static_cast<float*>(ws);
+  float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                       ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256);
+  hipLaunchKernelGGL((gdn_conv_kernel<A, DK>), dim3(n * T, H), dim3(2 * DK), 0, st, static_cast<const A*>(x),
+                     conv_w, static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk,
+                     kq);
+  const size_t smem = (size_t)T * 2 * DK * sizeof(float);
+  if (L < 16) {
+    auto kern = gdn_state_kernel<A, DK, CPT, 16>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
+                       S_scratch, static_cast<A*>(o), parent, T, L, H);
+  } else {
+    auto kern = gdn_state_kernel<A, DK, 4, 32>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipLaunchKernelGGL(kern, dim3(n * H, DK / R4), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
+                       S_scratch, static_cast<A*>(o), parent, T, L, H);
   }
 }
 
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
                                 const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
                                 void* o, const int32_t* parent, int n, int T, int L, int H, int dk, int C, int W,
-                                int act_dt, hipStream_t st) {
-  const size_t smem = (size_t)(L + 1) * kGdnThreads * sizeof(float4);
-#define DDT_GDN(TY, DKV)                                                                                      \
-  do {                                                                                                        \
-    const dim3 grid(n * H, DKV / (kGdnThreads / (DKV / 4)));                                                  \
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_tree_kernel<TY, DKV>),                              \
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);                               \
-    hipLaunchKernelGGL((gdn_tree_kernel<TY, DKV>), grid, dim3(kGdnThreads), smem, st,                        \
-                       static_cast<const TY*>(x), conv_w, static_cast<const TY*>(conv_state),                \
-                       static_cast<TY*>(conv_scratch), static_cast<const TY*>(v), beta, g, S, S_scratch,      \
-                       static_cast<TY*>(o), parent, T, L, H, C, W);                                           \
-  } while (0)
+                                int act_dt, void* ws, hipStream_t st) {
+#define DDT_GDN(TY, DKV) \
+  launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, L, H, C, W, ws, st)
   if (act_dt == DDT_BF16) {
     if (dk == 32) DDT_GDN(uint16_t, 32);
     else if (dk == 64) DDT_GDN(uint16_t, 64);

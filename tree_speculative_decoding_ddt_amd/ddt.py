@@ -20,7 +20,7 @@ DDT_F32, DDT_BF16 = 0, 1
 EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_build_tree_workspace", "ddt_build_tree",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
-           "ddt_gdn_tree_step",
+           "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
            "ddt_commit")
 
@@ -64,7 +64,8 @@ def lib():
         "ddt_build_tree": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]),
         "ddt_tree_attn_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
-        "ddt_gdn_tree_step": (I, [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]),
+        "ddt_gdn_tree_step_workspace": (Z, [I, I, I, I]),
+        "ddt_gdn_tree_step": (I, [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P]),
         "ddt_tree_accept_workspace": (Z, [I, I, I]),
         "ddt_tree_accept": (I, [P, I, P, P, I, I, I, I, P, P, P, P, Z, P]),
         "ddt_commit": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, I, I,
@@ -131,6 +132,10 @@ def tree_attn_workspace(n, B, Hq, Hkv, D, Pmax, dtype):
     return lib().ddt_tree_attn_workspace(n, B, Hq, Hkv, D, Pmax, DDT_BF16 if dtype == torch.bfloat16 else DDT_F32)
 
 
+def gdn_tree_step_workspace(n, B, H, dk):
+    return lib().ddt_gdn_tree_step_workspace(n, B, H, dk)
+
+
 def tree_accept_workspace(n, B, V):
     return lib().ddt_tree_accept_workspace(n, B, V)
 
@@ -178,7 +183,7 @@ def tree_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, scale=0.0, w
     return out
 
 
-def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, out=None):
+def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=None):
     """x [n][T][C], conv_w [C][W] f32, conv_state [n][W-1][C], v [n][T][H][dv], beta, g [n][T][H] f32,
     S [n][H][dv][dk] f32, parent [n][T] int32 -> dict o, S_scratch, conv_scratch."""
     _gpu(x, conv_w, conv_state, v, beta, g, S, parent)
@@ -190,10 +195,11 @@ def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, out=None):
         out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev),
                "S_scratch": torch.empty(n, T, H, dv, dk, dtype=torch.float32, device=dev),
                "conv_scratch": torch.empty(n, T, W - 1, C, dtype=x.dtype, device=dev)}
+    w = _ws(lib().ddt_gdn_tree_step_workspace(n, T - 1, H, dk), dev, ws)
     _check("ddt_gdn_tree_step", lib().ddt_gdn_tree_step(
         _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(out["conv_scratch"]), _ptr(v), _ptr(beta), _ptr(g),
         _ptr(S), _ptr(out["S_scratch"]), _ptr(out["o"]), _ptr(parent), n, T - 1, L, H, dk, dv, C, W,
-        _dt(x), _stream(dev)))
+        _dt(x), _ptr(w), w.numel() * w.element_size(), _stream(dev)))
     return out
 
 

@@ -102,6 +102,7 @@ class HybridVerifyStep:
         self.ws_build = u8(ddt.build_tree_workspace(n, c.L, c.V, c.B, c.K))
         self.ws_attn = u8(ddt.tree_attn_workspace(n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, dt))
         self.ws_acc = u8(ddt.tree_accept_workspace(n, c.B, c.V))
+        self.ws_gdn = u8(ddt.gdn_tree_step_workspace(n, c.B, c.H, c.dk))
         self.pattern = c.layer_pattern()
 
     # ------------------------------------------------------------ the round
@@ -121,7 +122,7 @@ class HybridVerifyStep:
                 g = self.gdn[ig]
                 ig += 1
                 ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"], g["beta"], g["g"], g["S"],
-                                  self.tree["parent"], self.cfg.L, out=g["out"])
+                                  self.tree["parent"], self.cfg.L, ws=self.ws_gdn, out=g["out"])
 
     def accept(self):
         ddt.tree_accept(self.target_logits, self.tree["tok"], self.tree["parent"], self.cfg.L,
