@@ -69,13 +69,13 @@ def test_build_tree_validation():
 def test_tree_attn_validation():
     def args(**k):
         return [k.get("q", P), P, P, P, P, P, P, 1, k.get("B", 8), k.get("Hq", 2), k.get("Hkv", 1),
-                k.get("D", 64), 128, ctypes.c_float(0.0), k.get("dt", 0), P, k.get("ws", P), k.get("wsb", 1 << 30), None]
+                k.get("D", 64), k.get("Pmax", 128), ctypes.c_float(0.0), k.get("dt", 0), P, k.get("ws", P), k.get("wsb", 1 << 30), None]
     assert status("ddt_tree_attn", *args(q=None)) == ddt.DDT_ERR_ARG
     assert status("ddt_tree_attn", *args(B=65)) == ddt.DDT_ERR_ARG
     assert status("ddt_tree_attn", *args(Hq=3, Hkv=2)) == ddt.DDT_ERR_ARG
     assert status("ddt_tree_attn", *args(D=96)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_tree_attn", *args(dt=3)) == ddt.DDT_ERR_UNSUPPORTED
-    assert status("ddt_tree_attn", *args(dt=1, D=256, wsb=8)) == ddt.DDT_ERR_WORKSPACE
+    assert status("ddt_tree_attn", *args(dt=1, D=256, Pmax=65536, wsb=8)) == ddt.DDT_ERR_WORKSPACE
 
 
 def test_gdn_validation():

@@ -33,6 +33,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnNK = 32;  // keys per iteration (bf16 path)
 constexpr float kLazy = 8.f; // rescale threshold of the online softmax (log2 units)
+#ifndef DDT_ATTN_STAGES
+#define DDT_ATTN_STAGES 3
+#endif
+constexpr int kAttnStages = DDT_ATTN_STAGES; // LDS stages of K/V tiles (bf16 path)
+#ifndef DDT_HOIST_K
+#define DDT_HOIST_K 0           // read all K operands of a tile before its S^T products
+#endif
+#ifndef DDT_HOIST_V
+#define DDT_HOIST_V 0           // V^T operand blocks read before the softmax
+#endif
 
 // ------------------------------------------------------------------ scalar path
 template <typename T, int D>
@@ -110,6 +120,41 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
 }
 
 // ------------------------------------------------------------------ bf16 matrix-core path
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K and V tiles live in LDS row-major, one key per row of D bf16, with the 16-byte
+// chunks of row `key` permuted by chunk ^ (key mod chunks-per-row): 16 consecutive
+// keys then hit 16 different bank groups for both the row reads of K and the
+// transposing reads of V.
+template <int D>
+__device__ __forceinline__ int swz_off(int key, int chunk) {
+  constexpr int CH = D / 8;
+  return key * (D * 2) + ((chunk ^ (key & (CH - 1))) << 4);
+}
+
+// One 16-byte lane-slice per lane per instruction, straight from global memory into
+// LDS (no registers): instruction i of a tile covers LDS bytes [1024 i, 1024 i + 1024).
+// Rows past `rows` are clamped to the last valid row (finite data, masked later).
+template <int D, int NK>
+__device__ __forceinline__ void load_tile_async(uint8_t* lds, const uint16_t* src, int row0, int rows, int wave,
+                                                int lane) {
+  constexpr int ROWB = D * 2, CH = D / 8, INSTR = NK * ROWB / 1024;
+#pragma unroll
+  for (int i = wave; i < INSTR; i += 4) {
+    const int byte = i * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int chunk = (byte % ROWB) >> 4;
+    const int gchunk = chunk ^ (row & (CH - 1));
+    const int grow = row0 + (row < rows ? row : rows - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (size_t)grow * D + gchunk * 8),
+                                     reinterpret_cast<void*>(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// s_waitcnt with vmcnt = n (0..63) and the other counters left unconstrained.
+#define DDT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
 template <int D, int NT>
 __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
@@ -120,14 +165,14 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
                                                            const uint64_t* __restrict__ anc, int Tn, int Hq,
                                                            int Hkv, int Pmax, float scale_log2, int nwg,
                                                            int nsplit, int split_len, float* __restrict__ part_lse,
-                                                           float* __restrict__ part_o) {
+                                                           float* __restrict__ part_o, uint16_t* __restrict__ out) {
   constexpr int NK = kAttnNK;
-  constexpr int KPAD = D + 8;    // K tile row stride (bf16): keeps 16 consecutive rows on distinct banks
-  constexpr int VPAD = NK + 8;   // V^T row stride (bf16)
-  constexpr int DS = D / 32;     // contraction steps of S^T = K Q^T
-  constexpr int DB = D / 16;     // 16-wide blocks of d in O^T
-  __shared__ __align__(16) uint16_t Ks[NK * KPAD];
-  __shared__ __align__(16) uint16_t Vt[D * VPAD];
+  constexpr int NST = kAttnStages;              // LDS stages (tiles in flight = NST - 1)
+  constexpr int TILE = NK * D * 2;              // bytes of one K or V tile
+  constexpr int DS = D / 32;                    // contraction steps of S^T = K Q^T
+  constexpr int DB = D / 16;                    // 16-wide blocks of d in O^T
+  constexpr int DMA = 2 * (TILE / 1024) / 4;    // async load instructions per wave per tile
+  __shared__ __align__(1024) uint8_t lds[NST][2][TILE];  // [stage][K, V]
 
   const int G = Hq / Hkv;
   const int R = Tn * G;
@@ -138,24 +183,32 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
   const int kvh = bx % Hkv;
   const int s = bx / Hkv;
   const int split = blockIdx.y;
-  const bool is_tree = split == nsplit;
+  const bool last = split == nsplit - 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
 
-  int k_beg, k_end;
-  const uint16_t *Kb, *Vb;
-  if (is_tree) {
-    k_beg = 0;
-    k_end = Tn;
-    Kb = k_tree + (size_t)(s * Hkv + kvh) * Tn * D;
-    Vb = v_tree + (size_t)(s * Hkv + kvh) * Tn * D;
-  } else {
-    const int P = min(max(prefix_len[s], 0), Pmax);
-    k_beg = split * split_len;
-    k_end = min(P, k_beg + split_len);
-    Kb = k_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
-    Vb = v_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
-  }
+  // key tiles: this split's slice of the prefix, then (last split) the tree rows
+  const int P = min(max(prefix_len[s], 0), Pmax);
+  const int k_beg = min(split * split_len, P);
+  const int k_end = min(P, k_beg + split_len);
+  const int n_pre = (k_end - k_beg + NK - 1) / NK;
+  const int n_all = n_pre + (last ? (Tn + NK - 1) / NK : 0);
+  const uint16_t* Kp = k_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
+  const uint16_t* Vp = v_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
+  const uint16_t* Kt = k_tree + (size_t)(s * Hkv + kvh) * Tn * D;
+  const uint16_t* Vt = v_tree + (size_t)(s * Hkv + kvh) * Tn * D;
+  auto issue = [&](int it) {
+    const int stage = it % NST;
+    if (it < n_pre) {
+      const int r0 = k_beg + it * NK;
+      load_tile_async<D, NK>(lds[stage][0], Kp, r0, k_end - r0, wave, lane);
+      load_tile_async<D, NK>(lds[stage][1], Vp, r0, k_end - r0, wave, lane);
+    } else {
+      const int r0 = (it - n_pre) * NK;
+      load_tile_async<D, NK>(lds[stage][0], Kt, r0, Tn - r0, wave, lane);
+      load_tile_async<D, NK>(lds[stage][1], Vt, r0, Tn - r0, wave, lane);
+    }
+  };
 
   // this wave's tiles and Q fragments (B operand of S^T: row l16, d = 32*st + 8*q4 .. +7)
   int tile[NT];
@@ -174,8 +227,12 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
       uint4 w = ok ? *reinterpret_cast<const uint4*>(qp + 32 * st) : make_uint4(0, 0, 0, 0);
       Qf[j][st] = __builtin_bit_cast(bf16x8, w);
     }
-    arow[j] = (ok && is_tree) ? anc[(size_t)s * Tn + trow] : 0ull;
+    arow[j] = (ok && last) ? anc[(size_t)s * Tn + trow] : 0ull;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // Q in registers before the DMA counting starts
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < n_all) issue(i);
 
   f32x4 O[NT][DB];
   float m[NT], l[NT];
@@ -187,66 +244,91 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
     for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int kb = k_beg; kb < k_end; kb += NK) {
-    // K tile: rows kb..kb+NK-1 as-is
-    for (int v = tid; v < NK * (D / 8); v += 256) {
-      const int key = v / (D / 8), dc = (v % (D / 8)) * 8;
-      const int kk = kb + key;
-      const uint4 w = kk < k_end ? *reinterpret_cast<const uint4*>(Kb + (size_t)kk * D + dc) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&Ks[key * KPAD + dc]) = w;
-    }
-    // V tile transposed: Vt[d][pos(key)], keys 4g..4g+3 -> positions 8g.. (g<4) or 8(g-4)+4.. (g>=4)
-    for (int v = tid; v < (NK / 4) * (D / 8); v += 256) {
-      const int kg = v / (D / 8), dc = (v % (D / 8)) * 8;
-      uint32_t w[4][4];
+  // per-lane LDS offsets of the operands (the swizzle depends on the key row only)
+  int koff[2][DS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = kb + 4 * kg + i;
-        const uint4 x = kk < k_end ? *reinterpret_cast<const uint4*>(Vb + (size_t)kk * D + dc) : make_uint4(0, 0, 0, 0);
-        w[i][0] = x.x; w[i][1] = x.y; w[i][2] = x.z; w[i][3] = x.w;
-      }
-      const int pos = kg < 4 ? 8 * kg : 8 * (kg - 4) + 4;
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu, a1 = (w[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu, a3 = (w[3][e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(&Vt[(dc + e) * VPAD + pos]) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      }
-    }
+    for (int st = 0; st < DS; ++st) koff[b][st] = swz_off<D>(16 * b + l16, 4 * st + q4);
+  const int vkey = 4 * q4 + (l16 >> 2);
+  const int vintra = (l16 & 1) * 8;
+
+  for (int it = 0; it < n_all; ++it) {
+    // wait for tile `it` (later tiles may still be in flight), then make it visible
+    const int ahead = n_all - 1 - it;
+    if (ahead >= NST - 2) DDT_WAIT_VMCNT((NST - 2) * DMA);
+    else if (ahead == 1) DDT_WAIT_VMCNT(DMA);
+    else DDT_WAIT_VMCNT(0);
     __syncthreads();
+    if (it + NST - 1 < n_all) issue(it + NST - 1);  // refills the stage read in iteration it-1
+    const uint8_t* Ks = lds[it % NST][0];
+    const uint8_t* Vs = lds[it % NST][1];
+    const bool tree = it >= n_pre;
+    const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
+    const int kend = tree ? Tn : k_end;
+    const bool full = !tree && kb + NK <= kend;
 
     // S^T blocks: keys 16b + 4*q4 + e of row l16
     f32x4 Sacc[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) Sacc[j][0] = Sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#if DDT_HOIST_K
+    bf16x8 Ka[2][DS];
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
+    for (int st = 0; st < DS; ++st)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) Ka[b][st] = *reinterpret_cast<const bf16x8*>(Ks + koff[b][st]);
+#pragma unroll
+    for (int st = 0; st < DS; ++st)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          Sacc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[b][st], Qf[j][st], Sacc[j][b], 0, 0, 0);
+#else
+#pragma unroll
+    for (int st = 0; st < DS; ++st)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&Ks[(16 * b + l16) * KPAD + 32 * st + 8 * q4]);
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(Ks + koff[b][st]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) Sacc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qf[j][st], Sacc[j][b], 0, 0, 0);
+        for (int j = 0; j < NT; ++j)
+          Sacc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qf[j][st], Sacc[j][b], 0, 0, 0);
       }
+#endif
+
+    // V^T operands (d = 16*b + l16, keys 4*q4 + 0..3 and 16 + 4*q4 + 0..3), read now so
+    // that their latency overlaps the softmax
+    s16x4 Vlo[DB], Vhi[DB];
+#pragma unroll
+    for (int b = 0; b < DDT_HOIST_V; ++b) {
+      const int chunk = 2 * b + ((l16 & 3) >> 1);
+      Vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey, chunk) + vintra));
+      Vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey + 16, chunk) + vintra));
     }
 
     bf16x8 Pb[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       float sv[8];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kb + 16 * b + 4 * q4 + e;
-          bool vis = key < k_end;
-          if (is_tree) vis = vis && (key == 0 || ((arow[j] >> (key - 1)) & 1ull));
-          const float x = vis ? Sacc[j][b][e] * scale_log2 : -INFINITY;
-          sv[4 * b + e] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int e = 0; e < 4; ++e) sv[4 * b + e] = Sacc[j][b][e] * scale_log2;
+      if (!full) {  // tail of the prefix, or the tree under its ancestor mask
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kb + 16 * b + 4 * q4 + e;
+            bool vis = key < kend;
+            if (tree) vis = vis && (key == 0 || ((arow[j] >> (key - 1)) & 1ull));
+            if (!vis) sv[4 * b + e] = -INFINITY;
+          }
       }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // Lazy rescaling: the running reference m only moves when a row's max exceeds it
@@ -259,11 +341,11 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
 #pragma unroll
         for (int b = 0; b < DB; ++b) O[j][b] *= alpha;
       }
-      const float mref = m[j];
+      const float mref = m[j] == -INFINITY ? 0.f : m[j];
       float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mref);
+        const float p = exp2f(sv[e] - mref);  // exp2(-inf) = 0 for masked keys
         sv[e] = p;
         rs += p;
       }
@@ -274,28 +356,46 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
       for (int e = 0; e < 8; ++e) Pb[j][e] = static_cast<__bf16>(sv[e]);
     }
 
+    // O^T += V^T P^T
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(&Vt[(16 * b + l16) * VPAD + 8 * q4]);
+      if (b >= DDT_HOIST_V) {
+        const int chunk = 2 * b + ((l16 & 3) >> 1);
+        Vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey, chunk) + vintra));
+        Vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey + 16, chunk) + vintra));
+      }
+      // whole-vector join: the keys 4*q4+0..3 then 16+4*q4+0..3 of column d
+      const bf16x8 A = __builtin_bit_cast(bf16x8, __builtin_shufflevector(Vlo[b], Vhi[b], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pb[j], O[j][b], 0, 0, 0);
     }
-    __syncthreads();
   }
 
-  // partial results: lse (log2 domain) and O / l per row
+  // results: with one split the normalised output directly, else (lse, O/l) partials
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int r = tile[j] * 16 + l16;
     if (tile[j] >= ntiles || r >= R) continue;
-    const size_t base = ((size_t)(s * Hkv + kvh) * (nsplit + 1) + split) * R + r;
     const float lse = l[j] > 0.f ? m[j] + log2f(l[j]) : -INFINITY;
     const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
-    if (q4 == 0) part_lse[base] = lse;
+    if (nsplit == 1) {
+      const int trow = r / G, hl = r % G;
+      uint16_t* op = out + (((size_t)s * Tn + trow) * Hq + kvh * G + hl) * D;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const f32x4 o = O[j][b] * inv;
-      *reinterpret_cast<float4*>(&part_o[base * D + 16 * b + 4 * q4]) = make_float4(o[0], o[1], o[2], o[3]);
+      for (int b = 0; b < DB; ++b) {
+        const f32x4 o = O[j][b] * inv;
+        const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *reinterpret_cast<uint2*>(&op[16 * b + 4 * q4]) = make_uint2(lo, hi);
+      }
+    } else {
+      const size_t base = ((size_t)(s * Hkv + kvh) * nsplit + split) * R + r;
+      if (q4 == 0) part_lse[base] = lse;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const f32x4 o = O[j][b] * inv;
+        *reinterpret_cast<float4*>(&part_o[base * D + 16 * b + 4 * q4]) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
@@ -329,7 +429,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
   }
 }
 
-// 16-row tiles per wave: Q (2 VGPR/row at D=256) and O (4 AGPR/row) must stay in registers.
+// 16-row tiles per wave: Q (2 VGPR/row at D=256) and O (4 AGPR/row) stay in registers.
 constexpr int attn_nt(int D) { return D == 256 ? 2 : 3; }
 
 AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) {
@@ -341,15 +441,17 @@ AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) 
   p.ntiles = cdiv(p.R, 16);
   if (!p.mfma) return p;
   p.nwg = cdiv(p.ntiles, 4 * attn_nt(D));
+  // one block per CU: split the prefix so that the grid fills the 256 CUs once
   const int units = n * Hkv * p.nwg;
-  int ns = cdiv(256, units);
-  const int ns_max = Pmax / 512 > 1 ? Pmax / 512 : 1;
+  int ns = 256 / units;
+  const int ns_max = Pmax / 256 > 1 ? Pmax / 256 : 1;
   ns = ns < 1 ? 1 : (ns > ns_max ? ns_max : ns);
   int len = cdiv(Pmax > 0 ? Pmax : 1, ns);
   len = cdiv(len, kAttnNK) * kAttnNK;
   p.split_len = len;
   p.nsplit = cdiv(Pmax > 0 ? Pmax : 1, len);
-  const size_t rows = (size_t)n * Hkv * (p.nsplit + 1) * p.R;
+  if (p.nsplit == 1) return p;  // the kernel writes the output directly
+  const size_t rows = (size_t)n * Hkv * p.nsplit * p.R;
   p.off_lse = 0;
   p.off_o = (rows * sizeof(float) + 255) / 256 * 256;
   p.total = p.off_o + rows * D * sizeof(float);
@@ -378,25 +480,28 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
     return hipGetLastError();
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
-  float* part_lse = reinterpret_cast<float*>(w + plan.off_lse);
-  float* part_o = reinterpret_cast<float*>(w + plan.off_o);
+  float* part_lse = plan.total ? reinterpret_cast<float*>(w + plan.off_lse) : nullptr;
+  float* part_o = plan.total ? reinterpret_cast<float*>(w + plan.off_o) : nullptr;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid(n * Hkv * plan.nwg, plan.nsplit + 1);
+  const dim3 grid(n * Hkv * plan.nwg, plan.nsplit);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
   const auto* kt = static_cast<const uint16_t*>(k_tree);
   const auto* vt = static_cast<const uint16_t*>(v_tree);
+  auto* o16 = static_cast<uint16_t*>(out);
   if (D == 256) {
     hipLaunchKernelGGL((attn_mfma_kernel<256, attn_nt(256)>), grid, dim3(256), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o);
-    hipLaunchKernelGGL((attn_combine_kernel<256>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
-                       plan.nsplit + 1, static_cast<uint16_t*>(out));
+                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o, o16);
+    if (plan.nsplit > 1)
+      hipLaunchKernelGGL((attn_combine_kernel<256>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
+                         plan.nsplit, o16);
   } else {
     hipLaunchKernelGGL((attn_mfma_kernel<128, attn_nt(128)>), grid, dim3(256), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o);
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
-                       plan.nsplit + 1, static_cast<uint16_t*>(out));
+                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o, o16);
+    if (plan.nsplit > 1)
+      hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
+                         plan.nsplit, o16);
   }
   return hipGetLastError();
 }
