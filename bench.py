@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--n", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -133,6 +135,15 @@ def main():
               "(requested --gpus %d)" % a.gpus, file=sys.stderr)
         return 2
     import torch
+
+    if a.copy_probe:
+        x = torch.empty(a.copy_probe << 20, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print("copied %d MiB x3" % a.copy_probe, file=sys.stderr)
+        return 0
 
     from tree_speculative_decoding_ddt_amd import ddt
     from tree_speculative_decoding_ddt_amd.step import HybridConfig, HybridVerifyStep

@@ -28,6 +28,7 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
 struct AttnPlan {
   bool mfma;      // bf16 matrix-core path (else the scalar path, no workspace)
   int G, R, ntiles, nwg, nsplit, split_len;
+  int units, grid;  // (sequence, kv head, split) units; blocks launched
   size_t off_lse, off_o, total;
 };
 AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);

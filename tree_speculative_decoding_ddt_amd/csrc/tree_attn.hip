@@ -31,18 +31,14 @@ namespace ddt {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnNK = 32;  // keys per iteration (bf16 path)
-constexpr float kLazy = 8.f; // rescale threshold of the online softmax (log2 units)
-#ifndef DDT_ATTN_STAGES
-#define DDT_ATTN_STAGES 3
+constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
+constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
+constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, O) partials of a
+                                     // split cost about as much traffic as 400 keys of K/V
+#ifndef DDT_ATTN_SOFTMAX_FIRST
+#define DDT_ATTN_SOFTMAX_FIRST 1  // softmax of S(it) before P.V of tile it-1 (S dies earlier)
 #endif
-constexpr int kAttnStages = DDT_ATTN_STAGES; // LDS stages of K/V tiles (bf16 path)
-#ifndef DDT_HOIST_K
-#define DDT_HOIST_K 0           // read all K operands of a tile before its S^T products
-#endif
-#ifndef DDT_HOIST_V
-#define DDT_HOIST_V 0           // V^T operand blocks read before the softmax
-#endif
+constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
 
 // ------------------------------------------------------------------ scalar path
 template <typename T, int D>
@@ -123,68 +119,60 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// K and V tiles live in LDS row-major, one key per row of D bf16, with the 16-byte
-// chunks of row `key` permuted by chunk ^ (key mod chunks-per-row): 16 consecutive
-// keys then hit 16 different bank groups for both the row reads of K and the
-// transposing reads of V.
-template <int D>
-__device__ __forceinline__ int swz_off(int key, int chunk) {
-  constexpr int CH = D / 8;
-  return key * (D * 2) + ((chunk ^ (key & (CH - 1))) << 4);
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at LDS
+// byte address lds_addr + 16*l.  Written as inline asm so that the compiler does not
+// treat the in-flight copy as aliasing every later LDS read (it would wait for all
+// outstanding copies before each read); the kernel counts vmcnt itself.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
 }
-
-// One 16-byte lane-slice per lane per instruction, straight from global memory into
-// LDS (no registers): instruction i of a tile covers LDS bytes [1024 i, 1024 i + 1024).
-// Rows past `rows` are clamped to the last valid row (finite data, masked later).
-template <int D, int NK>
-__device__ __forceinline__ void load_tile_async(uint8_t* lds, const uint16_t* src, int row0, int rows, int wave,
-                                                int lane) {
-  constexpr int ROWB = D * 2, CH = D / 8, INSTR = NK * ROWB / 1024;
-#pragma unroll
-  for (int i = wave; i < INSTR; i += 4) {
-    const int byte = i * 1024 + lane * 16;
-    const int row = byte / ROWB;
-    const int chunk = (byte % ROWB) >> 4;
-    const int gchunk = chunk ^ (row & (CH - 1));
-    const int grow = row0 + (row < rows ? row : rows - 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (size_t)grow * D + gchunk * 8),
-                                     reinterpret_cast<void*>(lds + i * 1024), 16, 0, 0);
-  }
-}
-
+// Workgroup barrier without a memory fence: copies into other LDS stages stay in flight.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and the other counters left unconstrained.
 #define DDT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <int D, int NT>
-__global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
+// Block = 4 waves sharing one ring of K/V tiles in LDS; a wave owns NT 16-row tiles of
+// the flattened (tree row, q head) rows of one kv head.  The ring holds tile it-1
+// (its V still feeds P.V), tile it, and tiles it+1, it+2 whose copies are in flight.
+// Iteration it: S(it) = K(it) Q^T, then O += V(it-1)^T P(it-1)^T issued together with
+// the softmax of S(it), so the exp/max/sum work overlaps the matrix-core products.
+template <int D, int NT, int NW, int PK, int PV>
+__global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
                                                            const uint16_t* __restrict__ v_cache,
                                                            const int32_t* __restrict__ prefix_len,
                                                            const uint16_t* __restrict__ k_tree,
                                                            const uint16_t* __restrict__ v_tree,
                                                            const uint64_t* __restrict__ anc, int Tn, int Hq,
-                                                           int Hkv, int Pmax, float scale_log2, int nwg,
-                                                           int nsplit, int split_len, float* __restrict__ part_lse,
+                                                           int Hkv, int Pmax, float sl2, int nwg, int nsplit,
+                                                           int split_len, int units, float* __restrict__ part_lse,
                                                            float* __restrict__ part_o, uint16_t* __restrict__ out) {
-  constexpr int NK = kAttnNK;
-  constexpr int NST = kAttnStages;              // LDS stages (tiles in flight = NST - 1)
-  constexpr int TILE = NK * D * 2;              // bytes of one K or V tile
-  constexpr int DS = D / 32;                    // contraction steps of S^T = K Q^T
-  constexpr int DB = D / 16;                    // 16-wide blocks of d in O^T
-  constexpr int DMA = 2 * (TILE / 1024) / 4;    // async load instructions per wave per tile
-  __shared__ __align__(1024) uint8_t lds[NST][2][TILE];  // [stage][K, V]
+  constexpr int NK = kAttnNK, NST = kAttnStages;
+  constexpr int ROWB = D * 2, LPR = ROWB / 16;  // bytes of a key row, DMA lanes per key row
+  constexpr int RS = ROWB + 32;                 // LDS row stride (padded, see below)
+  constexpr int TILE = NK * RS;                 // bytes of one K (or V) tile in LDS
+  constexpr int RPW = NK / NW;                  // key rows each wave copies per K (or V) tile
+  constexpr int DS = D / 32, DB = D / 16;
+  __shared__ __align__(1024) uint8_t lds[NST * 2 * TILE];
 
-  const int G = Hq / Hkv;
-  const int R = Tn * G;
-  const int ntiles = (R + 15) / 16;
-  int bx = blockIdx.x;
-  const int grp = bx % nwg;
-  bx /= nwg;
-  const int kvh = bx % Hkv;
-  const int s = bx / Hkv;
-  const int split = blockIdx.y;
+  // XCD-aware placement: block ids are dealt to the 8 XCDs round-robin, so the nwg row
+  // groups of one (sequence, kv head, split) get ids 8 apart and share one L2.
+  const int jb = blockIdx.x >> 3;
+  const int grp = jb % nwg;
+  const int u = (jb / nwg) * 8 + (blockIdx.x & 7);
+  if (u >= units) return;
+  const int split = u % nsplit;
+  const int kvh = (u / nsplit) % Hkv;
+  const int s = u / (nsplit * Hkv);
   const bool last = split == nsplit - 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = Hq / Hkv, R = Tn * G, ntiles = (R + 15) / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
 
   // key tiles: this split's slice of the prefix, then (last split) the tree rows
@@ -193,30 +181,47 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
   const int k_end = min(P, k_beg + split_len);
   const int n_pre = (k_end - k_beg + NK - 1) / NK;
   const int n_all = n_pre + (last ? (Tn + NK - 1) / NK : 0);
-  const uint16_t* Kp = k_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
-  const uint16_t* Vp = v_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
-  const uint16_t* Kt = k_tree + (size_t)(s * Hkv + kvh) * Tn * D;
-  const uint16_t* Vt = v_tree + (size_t)(s * Hkv + kvh) * Tn * D;
+  const size_t hoff = (size_t)s * Hkv + kvh;
+  const uint16_t* Kp = k_cache + hoff * Pmax * D;
+  const uint16_t* Vp = v_cache + hoff * Pmax * D;
+  const uint16_t* Kt = k_tree + hoff * Tn * D;
+  const uint16_t* Vt = v_tree + hoff * Tn * D;
+
+  // LDS layout of a tile: key row r at r*RS, RS = row bytes + 32, so rows start 32 bytes
+  // apart modulo the 256 bytes the banks span; the 16-byte chunk c of row r is stored at
+  // chunk c ^ ((r >> 3) & 1).  Then the 16 keys of a K operand read (16 bytes each) and
+  // the 8 rows x 32 bytes of two transposing V reads both fall on distinct banks, and
+  // every read address is a per-lane base plus an immediate offset.
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto issue = [&](int it) {
-    const int stage = it % NST;
-    if (it < n_pre) {
-      const int r0 = k_beg + it * NK;
-      load_tile_async<D, NK>(lds[stage][0], Kp, r0, k_end - r0, wave, lane);
-      load_tile_async<D, NK>(lds[stage][1], Vp, r0, k_end - r0, wave, lane);
-    } else {
-      const int r0 = (it - n_pre) * NK;
-      load_tile_async<D, NK>(lds[stage][0], Kt, r0, Tn - r0, wave, lane);
-      load_tile_async<D, NK>(lds[stage][1], Vt, r0, Tn - r0, wave, lane);
+    const uint32_t kb = lds0 + (uint32_t)((it % NST) * 2 * TILE);
+    const bool pre = it < n_pre;
+    const int r0 = pre ? k_beg + it * NK : (it - n_pre) * NK;
+    const int rows = pre ? k_end - r0 : Tn - r0;  // rows past the end repeat the last one (masked later)
+    const uint16_t* Kg = pre ? Kp : Kt;
+    const uint16_t* Vg = pre ? Vp : Vt;
+    // the lane id is recomputed here: hoisted out of the loop it would be spilled, and a
+    // scratch reload waits for every outstanding copy (they share vmcnt)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    if (ln < LPR) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int row = wave + NW * k;
+        const size_t e = (size_t)(r0 + min(row, rows - 1)) * D + (ln ^ ((row >> 3) & 1)) * 8;
+        const uint32_t m = kb + (uint32_t)(row * RS);
+        dma16(Kg + e, m);
+        dma16(Vg + e, m + TILE);
+      }
     }
   };
 
   // this wave's tiles and Q fragments (B operand of S^T: row l16, d = 32*st + 8*q4 .. +7)
   int tile[NT];
   bf16x8 Qf[NT][DS];
-  uint64_t arow[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    tile[j] = grp + nwg * (wave + 4 * j);
+    tile[j] = grp + nwg * (wave + NW * j);
     const int r = tile[j] * 16 + l16;
     const bool ok = tile[j] < ntiles && r < R;
     const int trow = ok ? r / G : 0;
@@ -227,157 +232,228 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
       uint4 w = ok ? *reinterpret_cast<const uint4*>(qp + 32 * st) : make_uint4(0, 0, 0, 0);
       Qf[j][st] = __builtin_bit_cast(bf16x8, w);
     }
-    arow[j] = (ok && last) ? anc[(size_t)s * Tn + trow] : 0ull;
   }
-  __builtin_amdgcn_s_waitcnt(0);  // Q in registers before the DMA counting starts
+  __builtin_amdgcn_s_waitcnt(0);  // Q and masks in registers before the copy counting starts
+
+  // tile it must have landed (tile it+1 may stay in flight); the barrier also means
+  // every wave is done with iteration it-1, whose stage is refilled next
+  auto sync_tile = [&](int it) {
+    if (it + 1 < n_all) DDT_WAIT_VMCNT(2 * RPW);
+    else DDT_WAIT_VMCNT(0);
+    barrier_nofence();
+    if (it + 2 < n_all) issue(it + 2);
+  };
+
+  // per-lane LDS read bases inside a stage (K: key row 16h + l16, chunk 4*st + q4; V:
+  // row 16h + 4*q4 + l16/4 of a transposing read, chunk 2*b + (l16 & 3)/2); the step
+  // index enters as an immediate offset (64*st for K, 32*b for V)
+  int kbase[2], vbase[2];
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i)
-    if (i < n_all) issue(i);
+  for (int h = 0; h < 2; ++h) {
+    const int key = 16 * h + l16;
+    kbase[h] = key * RS + ((q4 ^ ((key >> 3) & 1)) << 4);
+    const int vkey = 16 * h + 4 * q4 + (l16 >> 2);
+    vbase[h] = TILE + vkey * RS + ((((l16 & 3) >> 1) ^ ((vkey >> 3) & 1)) << 4) + (l16 & 1) * 8;
+  }
 
   f32x4 O[NT][DB];
-  float m[NT], l[NT];
+  float m[NT];    // softmax reference of the row (log2 units), fixed for a pass
+  float l[NT];    // this lane's share of the row sum (8 of the row's keys per tile)
+  float mxs[NT];  // largest raw score this lane has seen (sets the reference of a redo)
+  bf16x8 Pp[NT];  // P of the previous tile, B operand of its P.V product
+
+  // S^T blocks: Sacc[j][h] lane (l16, q4) element e = key 16h + 4*q4 + e of row l16.
+  // The 2*DS operand reads are issued PK ahead of the products that use them (the
+  // sched_group_barrier sequence pins that order for the machine scheduler).
+  auto s_phase = [&](int stage, f32x4 (&Sacc)[NT][2]) {
+    const uint8_t* Ks = lds + stage * 2 * TILE;
+    constexpr int NOP = 2 * DS;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+    for (int j = 0; j < NT; ++j) Sacc[j][0] = Sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 Kop[NOP];
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) Kop[i] = *reinterpret_cast<const bf16x8*>(Ks + kbase[i & 1] + 64 * (i >> 1));
+#pragma unroll
+    for (int i = 0; i < NOP; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        Sacc[j][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kop[i], Qf[j][i >> 1], Sacc[j][i & 1], 0, 0, 0);
+    if constexpr (PK > 0) {  // PK = 0: leave the order to the scheduler
+      __builtin_amdgcn_sched_group_barrier(0x100, PK, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < NOP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);  // MFMA
+        if (i + PK < NOP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  // O^T += V^T P^T: A = V^T (d = 16b + l16; keys 4*q4 + 0..3, then 16 + 4*q4 + 0..3),
+  // two transposing reads per block issued PV blocks ahead of their products
+  auto pv_phase = [&](int stage) {
+    const uint8_t* Vs = lds + stage * 2 * TILE;
+    bf16x8 Vop[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[0] + 32 * b));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[1] + 32 * b));
+      Vop[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vop[b], Pp[j], O[j][b], 0, 0, 0);
+    if constexpr (PV > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV, 1);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 1);
+        if (b + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+    }
+  };
+  // ancestor mask of this lane's row in tile j (tree tiles only: read when needed)
+  auto anc_row = [&](int j) -> uint64_t {
+    const int r = tile[j] * 16 + l16;
+    return (tile[j] < ntiles && r < R) ? anc[(size_t)s * Tn + r / G] : 0ull;
+  };
+  // scores of tile j, invisible keys at -inf when masked (prefix tail or tree tile)
+  auto scores = [&](const f32x4 (&Sacc)[NT][2], int j, bool masked, bool tree, int kb, int kend, float (&sv)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = Sacc[j][h][e];
+        if (masked) {
+          const int key = kb + 16 * h + 4 * q4 + e;
+          bool vis = key < kend;
+          if (tree) vis = vis && (key == 0 || ((anc_row(j) >> (key - 1)) & 1ull));
+          x = vis ? x : -INFINITY;
+        }
+        sv[4 * h + e] = x;
+      }
+  };
+  // P = 2^(score*scale*log2e - m) against the fixed reference; `over` marks a score more
+  // than kOver above it (P could overflow: the pass is redone with a larger reference)
+  bool over = false;
+  auto softmax = [&](const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend, bf16x8 (&Pout)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      float sv[8];
+      scores(Sacc, j, masked, tree, kb, kend, sv);
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mxs[j] = fmaxf(mxs[j], mx);
+      over = over || (mx * sl2 > m[j] + kOver);
+      float r = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -m[j]));
+        r += p;
+        Pout[j][e] = static_cast<__bf16>(p);
+      }
+      l[j] += r;
+    }
+  };
+  // row max of the raw scores of tile j over the 4 lanes that hold the row
+  auto row_max = [&](float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+  };
+
+  // key tiles [0, n_full) need no mask; [n_full, n_all) are the prefix tail and the tree
+  const int n_full = (k_end - k_beg) / NK;
+  __shared__ int redo_vote;
+  if (threadIdx.x == 0) redo_vote = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {  // a split with no keys writes lse = -inf and O = 0
     m[j] = -INFINITY;
+    mxs[j] = -INFINITY;
     l[j] = 0.f;
 #pragma unroll
     for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // per-lane LDS offsets of the operands (the swizzle depends on the key row only)
-  int koff[2][DS];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int st = 0; st < DS; ++st) koff[b][st] = swz_off<D>(16 * b + l16, 4 * st + q4);
-  const int vkey = 4 * q4 + (l16 >> 2);
-  const int vintra = (l16 & 1) * 8;
-
-  for (int it = 0; it < n_all; ++it) {
-    // wait for tile `it` (later tiles may still be in flight), then make it visible
-    const int ahead = n_all - 1 - it;
-    if (ahead >= NST - 2) DDT_WAIT_VMCNT((NST - 2) * DMA);
-    else if (ahead == 1) DDT_WAIT_VMCNT(DMA);
-    else DDT_WAIT_VMCNT(0);
-    __syncthreads();
-    if (it + NST - 1 < n_all) issue(it + NST - 1);  // refills the stage read in iteration it-1
-    const uint8_t* Ks = lds[it % NST][0];
-    const uint8_t* Vs = lds[it % NST][1];
-    const bool tree = it >= n_pre;
-    const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
-    const int kend = tree ? Tn : k_end;
-    const bool full = !tree && kb + NK <= kend;
-
-    // S^T blocks: keys 16b + 4*q4 + e of row l16
-    f32x4 Sacc[NT][2];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) Sacc[j][0] = Sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#if DDT_HOIST_K
-    bf16x8 Ka[2][DS];
-#pragma unroll
-    for (int st = 0; st < DS; ++st)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) Ka[b][st] = *reinterpret_cast<const bf16x8*>(Ks + koff[b][st]);
-#pragma unroll
-    for (int st = 0; st < DS; ++st)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          Sacc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[b][st], Qf[j][st], Sacc[j][b], 0, 0, 0);
-#else
-#pragma unroll
-    for (int st = 0; st < DS; ++st)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(Ks + koff[b][st]);
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          Sacc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qf[j][st], Sacc[j][b], 0, 0, 0);
-      }
-#endif
-
-    // V^T operands (d = 16*b + l16, keys 4*q4 + 0..3 and 16 + 4*q4 + 0..3), read now so
-    // that their latency overlaps the softmax
-    s16x4 Vlo[DB], Vhi[DB];
-#pragma unroll
-    for (int b = 0; b < DDT_HOIST_V; ++b) {
-      const int chunk = 2 * b + ((l16 & 3) >> 1);
-      Vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey, chunk) + vintra));
-      Vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey + 16, chunk) + vintra));
-    }
-
-    bf16x8 Pb[NT];
+  for (int pass = 0; n_all > 0; ++pass) {
+    issue(0);  // every wave enters a pass with no copy in flight
+    if (n_all > 1) issue(1);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      float sv[8];
+      l[j] = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sv[4 * b + e] = Sacc[j][b][e] * scale_log2;
-      if (!full) {  // tail of the prefix, or the tree under its ancestor mask
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kb + 16 * b + 4 * q4 + e;
-            bool vis = key < kend;
-            if (tree) vis = vis && (key == 0 || ((arow[j] >> (key - 1)) & 1ull));
-            if (!vis) sv[4 * b + e] = -INFINITY;
-          }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescaling: the running reference m only moves when a row's max exceeds it
-      // by more than kLazy (log2 units), so P <= 2^kLazy and O, l are rescaled rarely.
-      if (__any(mx > m[j] + kLazy)) {
-        const float mn = fmaxf(m[j], mx);
-        const float alpha = (m[j] == -INFINITY) ? (mn == -INFINITY ? 1.f : 0.f) : exp2f(m[j] - mn);
-        l[j] *= alpha;
-        m[j] = mn;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) O[j][b] *= alpha;
-      }
-      const float mref = m[j] == -INFINITY ? 0.f : m[j];
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[e] - mref);  // exp2(-inf) = 0 for masked keys
-        sv[e] = p;
-        rs += p;
-      }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l[j] += rs;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Pb[j][e] = static_cast<__bf16>(sv[e]);
+      for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-    // O^T += V^T P^T
+    // tile 0: S, then (first pass) the reference from its exact row max
+    {
+      sync_tile(0);
+      const bool tree = 0 >= n_pre;
+      const int kb = tree ? 0 : k_beg;
+      const int kend = tree ? Tn : k_end;
+      const bool masked = tree || kb + NK > kend;
+      f32x4 Sacc[NT][2];
+      s_phase(0, Sacc);
+      if (pass == 0) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      if (b >= DDT_HOIST_V) {
-        const int chunk = 2 * b + ((l16 & 3) >> 1);
-        Vlo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey, chunk) + vintra));
-        Vhi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + swz_off<D>(vkey + 16, chunk) + vintra));
+        for (int j = 0; j < NT; ++j) {
+          float sv[8];
+          scores(Sacc, j, masked, tree, kb, kend, sv);
+          float mx = sv[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+          m[j] = row_max(mx) * sl2;  // every row sees at least one key of its first tile
+        }
       }
-      // whole-vector join: the keys 4*q4+0..3 then 16+4*q4+0..3 of column d
-      const bf16x8 A = __builtin_bit_cast(bf16x8, __builtin_shufflevector(Vlo[b], Vhi[b], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pb[j], O[j][b], 0, 0, 0);
+      softmax(Sacc, masked, tree, kb, kend, Pp);
     }
+    int it = 1;
+    for (; it < n_full; ++it) {
+      sync_tile(it);
+      f32x4 Sacc[NT][2];
+      s_phase(it % NST, Sacc);
+#if DDT_ATTN_SOFTMAX_FIRST
+      bf16x8 Pn[NT];  // softmax first: S dies before the P.V product, P(it) waits in Pn
+      softmax(Sacc, false, false, 0, 0, Pn);
+      pv_phase((it - 1) % NST);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) Pp[j] = Pn[j];
+#else
+      pv_phase((it - 1) % NST);
+      softmax(Sacc, false, false, 0, 0, Pp);
+#endif
+    }
+    for (; it < n_all; ++it) {
+      sync_tile(it);
+      const bool tree = it >= n_pre;
+      const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
+      const int kend = tree ? Tn : k_end;
+      f32x4 Sacc[NT][2];
+      s_phase(it % NST, Sacc);
+      pv_phase((it - 1) % NST);
+      softmax(Sacc, true, tree, kb, kend, Pp);
+    }
+    barrier_nofence();
+    pv_phase((n_all - 1) % NST);
+    // one block-wide vote per pass: redo with references at the true row maxima
+    if (__any(over)) redo_vote = pass + 1;
+    __syncthreads();
+    const bool redo = redo_vote == pass + 1;
+    __syncthreads();
+    if (!redo) break;
+    over = false;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) m[j] = fmaxf(m[j], row_max(mxs[j]) * sl2);
   }
+  // every wave reaches this point with no copy in flight (the last sync waited for all)
 
   // results: with one split the normalised output directly, else (lse, O/l) partials
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
+    float lt = l[j];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
     const int r = tile[j] * 16 + l16;
     if (tile[j] >= ntiles || r >= R) continue;
-    const float lse = l[j] > 0.f ? m[j] + log2f(l[j]) : -INFINITY;
-    const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+    const float lse = lt > 0.f ? m[j] + log2f(lt) : -INFINITY;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (nsplit == 1) {
       const int trow = r / G, hl = r % G;
       uint16_t* op = out + (((size_t)s * Tn + trow) * Hq + kvh * G + hl) * D;
@@ -400,37 +476,58 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(const uint16_t* __res
   }
 }
 
+// Merge of the split partials: one lane per 4 output columns of one (sequence, tree
+// row, q head); parts are weighted by 2^(lse_p - max lse) and renormalised.
 template <int D>
-__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ part_lse,
-                                                           const float* __restrict__ part_o, int Tn, int Hq,
-                                                           int Hkv, int nparts, uint16_t* __restrict__ out) {
-  const int s = blockIdx.x / Tn, t = blockIdx.x % Tn;
+__global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __restrict__ part_lse,
+                                                             const float* __restrict__ part_o, int Tn, int Hq,
+                                                             int Hkv, int nparts, uint16_t* __restrict__ out) {
+  const int hq = blockIdx.x % Hq;
+  const int t = (blockIdx.x / Hq) % Tn;
+  const int s = blockIdx.x / (Hq * Tn);
   const int G = Hq / Hkv, R = Tn * G;
-  for (int idx = threadIdx.x; idx < Hq * (D / 4); idx += blockDim.x) {
-    const int hq = idx / (D / 4), d4 = idx % (D / 4);
-    const int kvh = hq / G, r = t * G + hq % G;
-    const size_t base = (size_t)(s * Hkv + kvh) * nparts * R + r;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, part_lse[base + (size_t)p * R]);
-    float wsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p = 0; p < nparts; ++p) {
-      const float ls = part_lse[base + (size_t)p * R];
-      if (ls == -INFINITY) continue;
-      const float w = exp2f(ls - M);
-      const float4 o = *reinterpret_cast<const float4*>(&part_o[(base + (size_t)p * R) * D + 4 * d4]);
-      wsum += w;
-      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
-    }
-    const float inv = 1.f / wsum;
-    const uint32_t lo = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-    *reinterpret_cast<uint2*>(&out[(((size_t)s * Tn + t) * Hq + hq) * D + 4 * d4]) = make_uint2(lo, hi);
+  const int d4 = threadIdx.x;
+  const size_t base = (size_t)(s * Hkv + hq / G) * nparts * R + t * G + hq % G;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, part_lse[base + (size_t)p * R]);
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < nparts; ++p) {
+    const float ls = part_lse[base + (size_t)p * R];
+    if (ls == -INFINITY) continue;
+    const float w = exp2f(ls - M);
+    const float4 o = *reinterpret_cast<const float4*>(&part_o[(base + (size_t)p * R) * D + 4 * d4]);
+    wsum += w;
+    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
   }
+  const float inv = 1.f / wsum;
+  const uint32_t lo = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(&out[(((size_t)s * Tn + t) * Hq + hq) * D + 4 * d4]) = make_uint2(lo, hi);
 }
 
-// 16-row tiles per wave: Q (2 VGPR/row at D=256) and O (4 AGPR/row) stay in registers.
-constexpr int attn_nt(int D) { return D == 256 ? 2 : 3; }
+// Tiling of the bf16 path: NT 16-row tiles per wave, NW waves per block.  Q (DS*4
+// registers per tile) and the fp32 O accumulators (DB*4 per tile) stay in registers.
+#ifndef DDT_ATTN_NT256
+#define DDT_ATTN_NT256 2
+#endif
+#ifndef DDT_ATTN_NW256
+#define DDT_ATTN_NW256 8
+#endif
+#ifndef DDT_ATTN_NT128
+#define DDT_ATTN_NT128 4
+#endif
+#ifndef DDT_ATTN_NW128
+#define DDT_ATTN_NW128 8
+#endif
+#ifndef DDT_ATTN_PK
+#define DDT_ATTN_PK 0  // K operand reads pinned ahead of their products (0: scheduler's order)
+#endif
+#ifndef DDT_ATTN_PV
+#define DDT_ATTN_PV 0  // V operand blocks pinned ahead of their products (0: scheduler's order)
+#endif
+constexpr int attn_nt(int D) { return D == 256 ? DDT_ATTN_NT256 : DDT_ATTN_NT128; }
+constexpr int attn_nw(int D) { return D == 256 ? DDT_ATTN_NW256 : DDT_ATTN_NW128; }
 
 AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) {
   AttnPlan p = {};
@@ -440,16 +537,18 @@ AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) 
   p.R = T * p.G;
   p.ntiles = cdiv(p.R, 16);
   if (!p.mfma) return p;
-  p.nwg = cdiv(p.ntiles, 4 * attn_nt(D));
+  p.nwg = cdiv(p.ntiles, attn_nw(D) * attn_nt(D));
   // one block per CU: split the prefix so that the grid fills the 256 CUs once
-  const int units = n * Hkv * p.nwg;
-  int ns = 256 / units;
-  const int ns_max = Pmax / 256 > 1 ? Pmax / 256 : 1;
+  const int rowblocks = n * Hkv * p.nwg;
+  int ns = 256 / rowblocks;
+  const int ns_max = Pmax / kAttnMinSplit > 1 ? Pmax / kAttnMinSplit : 1;
   ns = ns < 1 ? 1 : (ns > ns_max ? ns_max : ns);
   int len = cdiv(Pmax > 0 ? Pmax : 1, ns);
   len = cdiv(len, kAttnNK) * kAttnNK;
   p.split_len = len;
   p.nsplit = cdiv(Pmax > 0 ? Pmax : 1, len);
+  p.units = n * Hkv * p.nsplit;
+  p.grid = cdiv(p.units, 8) * 8 * p.nwg;
   if (p.nsplit == 1) return p;  // the kernel writes the output directly
   const size_t rows = (size_t)n * Hkv * p.nsplit * p.R;
   p.off_lse = 0;
@@ -483,7 +582,7 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
   float* part_lse = plan.total ? reinterpret_cast<float*>(w + plan.off_lse) : nullptr;
   float* part_o = plan.total ? reinterpret_cast<float*>(w + plan.off_o) : nullptr;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid(n * Hkv * plan.nwg, plan.nsplit);
+  const dim3 grid(plan.grid);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
@@ -491,16 +590,18 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
   const auto* vt = static_cast<const uint16_t*>(v_tree);
   auto* o16 = static_cast<uint16_t*>(out);
   if (D == 256) {
-    hipLaunchKernelGGL((attn_mfma_kernel<256, attn_nt(256)>), grid, dim3(256), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o, o16);
+    hipLaunchKernelGGL((attn_mfma_kernel<256, attn_nt(256), attn_nw(256), DDT_ATTN_PK, DDT_ATTN_PV>), grid, dim3(64 * attn_nw(256)), 0, st, qq, kc, vc, prefix_len, kt, vt,
+                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, plan.units, part_lse,
+                       part_o, o16);
     if (plan.nsplit > 1)
-      hipLaunchKernelGGL((attn_combine_kernel<256>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
+      hipLaunchKernelGGL((attn_combine_kernel<256>), dim3(n * T * Hq), dim3(64), 0, st, part_lse, part_o, T, Hq, Hkv,
                          plan.nsplit, o16);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<128, attn_nt(128)>), grid, dim3(256), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, part_lse, part_o, o16);
+    hipLaunchKernelGGL((attn_mfma_kernel<128, attn_nt(128), attn_nw(128), DDT_ATTN_PK, DDT_ATTN_PV>), grid, dim3(64 * attn_nw(128)), 0, st, qq, kc, vc, prefix_len, kt, vt,
+                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, plan.units, part_lse,
+                       part_o, o16);
     if (plan.nsplit > 1)
-      hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(n * T), dim3(256), 0, st, part_lse, part_o, T, Hq, Hkv,
+      hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(n * T * Hq), dim3(32), 0, st, part_lse, part_o, T, Hq, Hkv,
                          plan.nsplit, o16);
   }
   return hipGetLastError();
