@@ -30,10 +30,12 @@ def make_tree(rng, n, B, L, kind="random"):
     return parents, anc
 
 
-def run_case(seed, n, B, L, Hq, Hkv, D, Pmax, prefix, dtype, kind="random", rows=None, scale=0.0):
+def run_case(seed, n, B, L, Hq, Hkv, D, Pmax, prefix, dtype, kind="random", rows=None, scale=0.0, tweak=None):
     rng = np.random.default_rng(seed)
     parents, anc = make_tree(rng, n, B, L, kind)
     x = synth.attention_inputs(rng, n, B + 1, Hq, Hkv, D, Pmax)
+    if tweak is not None:
+        tweak(x)
     dv = {k: up(v, dtype) for k, v in x.items()}
     pl = np.asarray(prefix, dtype=np.int64)
     out = ddt.tree_attn(dv["q"][0], dv["k_cache"][0], dv["v_cache"][0], up_int(pl), dv["k_tree"][0],
@@ -106,3 +108,28 @@ def test_bf16_long_context_lopsided():
     say("tree_attn bf16 P=131072 lopsided tree (sampled rows)")
     rows = [0, 2, 15, 16, 64]
     run_case(77, 1, 64, 15, 24, 4, 256, 131072, [131072], "bf16", kind="lopsided", rows=rows)
+
+
+def spikes(prefix_keys, tree_rows):
+    """Positive queries and a few keys of all 8s: their scores exceed every earlier
+    key of the split by far more than 2^64 in probability ratio."""
+    def tweak(x):
+        x["q"] = np.abs(x["q"])
+        for k in prefix_keys:
+            x["k_cache"][:, :, k, :] = 8.0
+        for r in tree_rows:
+            x["k_tree"][:, :, r, :] = 8.0
+    return tweak
+
+
+def test_bf16_late_dominant_keys():
+    # a key far above the first tile's maximum, inside a split (prefix and tree tiles)
+    say("tree_attn bf16 late dominant keys")
+    run_case(90, 2, 64, 15, 24, 4, 256, 2100, [2100, 1500], "bf16", tweak=spikes([700, 1600], [5]))
+    run_case(91, 1, 64, 15, 24, 4, 128, 777, [777], "bf16", tweak=spikes([40], [33]))
+
+
+def test_bf16_early_dominant_keys():
+    # the first tile holds the maximum: every later probability underflows gracefully
+    say("tree_attn bf16 early dominant key")
+    run_case(92, 2, 64, 15, 24, 4, 256, 1100, [1100, 1030], "bf16", tweak=spikes([3], []))

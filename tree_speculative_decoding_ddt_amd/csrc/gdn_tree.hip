@@ -16,7 +16,8 @@
 //             (exact copies), and leaves q (scaled), k (normalised) and k.q in fp32 in
 //             the workspace.  Every node is independent here.
 //  gdn_state  grid (n*H, dv/R): a block owns R rows of one head's [dv][dk] state, a
-//             thread CPT consecutive columns of one row.  The block loads every node's
+//             thread CPT columns of one row (groups of 4, so that a wave's 16-byte
+//             stores cover whole row segments).  The block loads every node's
 //             q, k, k.q, v, g, beta into LDS, orders the nodes depth-first (in parallel:
 //             subtree sizes and sibling offsets), then walks them with no barrier:
 //             the parent's state is the newest one at depth d-1, held in a register
@@ -136,21 +137,27 @@ template <typename V> struct RegStack<32, V> {
 #undef DDT_GET
 #undef DDT_PUT
 
-template <typename V, int N>
+// A thread's N columns of a row are N/4 groups of 4, the groups GS floats apart: with
+// GS = DK/(N/4), each 16-byte store instruction of a wave covers whole row segments.
+template <typename V, int N, int GS>
 __device__ __forceinline__ V load_vec(const float* p) {
   V r;
 #pragma unroll
   for (int j = 0; j < N / 4; ++j) {
-    const float4 w = reinterpret_cast<const float4*>(p)[j];
+    const float4 w = *reinterpret_cast<const float4*>(p + j * GS);
     r[4 * j] = w.x; r[4 * j + 1] = w.y; r[4 * j + 2] = w.z; r[4 * j + 3] = w.w;
   }
   return r;
 }
-template <typename V, int N>
-__device__ __forceinline__ void store_vec(float* p, V x) {
+// Streaming (non-temporal) stores: the per-node states are not read again in the round
+// (the commit reads one of them), so they bypass the cache's write-allocate path.
+template <typename V, int N, int GS>
+__device__ __forceinline__ void store_vec_nt(float* p, V x) {
 #pragma unroll
-  for (int j = 0; j < N / 4; ++j)
-    reinterpret_cast<float4*>(p)[j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+  for (int j = 0; j < N / 4; ++j) {
+    const fv4 w = {x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<fv4*>(p + j * GS));
+  }
 }
 
 template <typename A, int DK, int CPT, int LMAX>
@@ -167,7 +174,8 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
   const int tid = threadIdx.x;
   const int rl = tid / LPR;
   const int r = blockIdx.y * R + rl;
-  const int c0 = (tid % LPR) * CPT;
+  constexpr int GS = DK / (CPT / 4);      // stride between a thread's column groups
+  const int c0 = (tid % LPR) * 4;          // first column of the thread's first group
 
   extern __shared__ float4 qk_s4[];      // [T][2*DK] floats: q then k of every node
   float* qk_s = reinterpret_cast<float*>(qk_s4);
@@ -194,7 +202,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     sz[u] = 0;
   }
   // committed state slice of this thread (used by nodes at depth 0)
-  const V sc = load_vec<V, CPT>(&S[(((size_t)s * H + h) * DV + r) * DK + c0]);
+  const V sc = load_vec<V, CPT, GS>(&S[(((size_t)s * H + h) * DV + r) * DK + c0]);
   __syncthreads();
 
   // ---- depth-first order, computed in parallel over nodes
@@ -242,8 +250,8 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     const int u = __builtin_amdgcn_readfirstlane(order[k]);
     const int d = __builtin_amdgcn_readfirstlane(dep[u]);
     if (d > L) continue;  // deeper than the stated bound: not processed
-    const V qv = load_vec<V, CPT>(&qk_s[u * 2 * DK + c0]);
-    const V kv = load_vec<V, CPT>(&qk_s[u * 2 * DK + DK + c0]);
+    const V qv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + c0]);
+    const V kv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + DK + c0]);
     const V sp = d == 0 ? sc : stk.get(d - 1);
     float a = 0.f, b = 0.f;
 #pragma unroll
@@ -261,7 +269,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     const V sn = gi * sp + delta * kv;
     stk.put(d, sn);
     const size_t ti = ((size_t)s * Tn + u) * H + h;
-    store_vec<V, CPT>(&S_scratch[(ti * DV + r) * DK + c0], sn);
+    store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
     if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * gb[u][2]);
   }
 }
