@@ -43,6 +43,10 @@ __global__ void __launch_bounds__(2 * DK) gdn_conv_kernel(const A* __restrict__ 
   const int tid = threadIdx.x;
   const bool is_k = tid >= DK;
   const int ch = is_k ? H * DK + h * DK + (tid - DK) : h * DK + tid;
+  // the sequence's parent row, so that the window's chain walk is LDS-only
+  __shared__ int par_s[kGdnMaxT];
+  for (int i = tid; i < Tn; i += 2 * DK) par_s[i] = parent[(size_t)s * Tn + i];
+  __syncthreads();
 
   // Window rows newest first (back b = 0 is the node itself), walking the parent
   // chain; past the root come the committed conv-state rows, newest first.  Tap
@@ -55,7 +59,7 @@ __global__ void __launch_bounds__(2 * DK) gdn_conv_kernel(const A* __restrict__ 
       int r = u;
       if (b > 0) {
         if (in_tree) {
-          const int p = parent[(size_t)s * Tn + cur];
+          const int p = par_s[cur];
           if (p >= 0 && p < cur) cur = p;
           else in_tree = 0;
         }

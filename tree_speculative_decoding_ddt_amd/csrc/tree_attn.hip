@@ -35,6 +35,9 @@ constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
 constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
 constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, O) partials of a
                                      // split cost about as much traffic as 400 keys of K/V
+#ifndef DDT_ATTN_PRIO
+#define DDT_ATTN_PRIO 1  // raise the wave priority during the MFMA phases (the other wave of the SIMD runs its softmax)
+#endif
 #ifndef DDT_ATTN_SOFTMAX_FIRST
 #define DDT_ATTN_SOFTMAX_FIRST 1  // softmax of S(it) before P.V of tile it-1 (S dies earlier)
 #endif
@@ -408,11 +411,23 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     for (; it < n_full; ++it) {
       sync_tile(it);
       f32x4 Sacc[NT][2];
+#if DDT_ATTN_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
       s_phase(it % NST, Sacc);
+#if DDT_ATTN_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
 #if DDT_ATTN_SOFTMAX_FIRST
       bf16x8 Pn[NT];  // softmax first: S dies before the P.V product, P(it) waits in Pn
       softmax(Sacc, false, false, 0, 0, Pn);
+#if DDT_ATTN_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
       pv_phase((it - 1) % NST);
+#if DDT_ATTN_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
 #pragma unroll
       for (int j = 0; j < NT; ++j) Pp[j] = Pn[j];
 #else
