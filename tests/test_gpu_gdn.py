@@ -20,6 +20,10 @@ def run_case(seed, n, B, L, H, dk, W, dtype, kind="random", check_heads=None):
     rng = np.random.default_rng(seed)
     if kind == "lopsided":
         parents = np.stack([synth.lopsided_parents()[0]] * n)
+    elif kind == "chain":
+        parents = np.stack([np.arange(-1, B)] * n)  # row i's parent is row i-1: depth i
+    elif kind == "star":
+        parents = np.stack([np.r_[-1, np.zeros(B, dtype=np.int64)]] * n)  # every node a child of the root
     elif kind == "unused":
         parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
         parents[:, B - 3:] = -1  # rows left unused by the build read the committed state
@@ -74,3 +78,15 @@ def test_lopsided_and_unused_rows():
 def test_full_batch_sampled_heads():
     say("gdn bf16 n=8 H=32 dk=128 (heads 0, 17, 31 checked)")
     run_case(33, 8, 64, 15, 32, 128, 4, "bf16", check_heads=[0, 17, 31])
+
+
+def test_deep_chain_uses_the_long_stack():
+    # depth 31 (> 15): the walk keeps 32 stack levels of 4 columns per thread
+    say("gdn chain depth 31")
+    run_case(40, 2, 31, 31, 2, 128, 4, "bf16", kind="chain")
+    run_case(41, 1, 40, 31, 1, 64, 3, "f32")  # random tree, depth bound 31
+
+
+def test_star_and_root_only():
+    run_case(42, 2, 64, 1, 2, 128, 4, "bf16", kind="star")
+    run_case(43, 2, 0, 1, 2, 64, 4, "f32")    # B = 0: the root alone

@@ -11,10 +11,10 @@
 //   S_i = g S_p + beta (v - g S_p k) k^T;  o_i = S_i q = g (S_p q) + beta (v - g S_p k) (k.q)
 //
 // Two kernels:
-//  gdn_conv   grid (n*T, H), one thread per channel of the head's q|k (2*dk): gathers
-//             the node's conv window along its parent chain, writes the conv scratch
-//             (exact copies), and leaves q (scaled), k (normalised) and k.q in fp32 in
-//             the workspace.  Every node is independent here.
+//  gdn_conv   grid (n*T): one block per node, 8 lanes per head; gathers the node's conv
+//             window along its parent chain, writes the conv scratch (exact copies),
+//             and leaves q (scaled), k (normalised) and k.q in fp32 in the workspace.
+//             Every node is independent here.
 //  gdn_state  grid (n*H, dv/R): a block owns R rows of one head's [dv][dk] state, a
 //             thread CPT columns of one row (groups of 4, so that a wave's 16-byte
 //             stores cover whole row segments).  The block loads every node's
@@ -34,28 +34,66 @@ constexpr int kGdnMaxT = 128;
 constexpr int kGdnMaxW = 8;
 
 // ------------------------------------------------------------------ conv + q/k
-template <typename A, int DK>
-__global__ void __launch_bounds__(2 * DK) gdn_conv_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
-                                                          const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
-                                                          const int32_t* __restrict__ parent, int Tn, int H, int C, int W,
-                                                          float* __restrict__ qk, float* __restrict__ kq) {
-  const int s = blockIdx.x / Tn, u = blockIdx.x % Tn, h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const bool is_k = tid >= DK;
-  const int ch = is_k ? H * DK + h * DK + (tid - DK) : h * DK + tid;
-  // the sequence's parent row, so that the window's chain walk is LDS-only
-  __shared__ int par_s[kGdnMaxT];
-  for (int i = tid; i < Tn; i += 2 * DK) par_s[i] = parent[(size_t)s * Tn + i];
-  __syncthreads();
-
-  // Window rows newest first (back b = 0 is the node itself), walking the parent
-  // chain; past the root come the committed conv-state rows, newest first.  Tap
-  // W-1-b multiplies back b; backs 0..W-2 are the node's conv state (slot W-2-b).
-  float acc = 0.f;
-  int cur = u, in_tree = 1, beyond = 0;
+// N consecutive activations of one row as raw 32-bit words, moved in 16- or 8-byte chunks.
+template <typename A, int N>
+struct RowIO {
+  static constexpr int WORDS = N * (int)sizeof(A) / 4;
+  uint32_t w[WORDS];
+  __device__ __forceinline__ void load(const A* p) {
+    if constexpr (WORDS % 4 == 0) {
 #pragma unroll
-  for (int b = 0; b < kGdnMaxW; ++b) {
-    if (b < W) {
+      for (int i = 0; i < WORDS / 4; ++i) {
+        const uint4 c = reinterpret_cast<const uint4*>(p)[i];
+        w[4 * i] = c.x; w[4 * i + 1] = c.y; w[4 * i + 2] = c.z; w[4 * i + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS / 2; ++i) {
+        const uint2 c = reinterpret_cast<const uint2*>(p)[i];
+        w[2 * i] = c.x; w[2 * i + 1] = c.y;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(A* p) const {
+    if constexpr (WORDS % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < WORDS / 4; ++i)
+        reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS / 2; ++i) reinterpret_cast<uint2*>(p)[i] = make_uint2(w[2 * i], w[2 * i + 1]);
+    }
+  }
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (sizeof(A) == 2) {
+      const uint32_t x = w[e >> 1];
+      return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+    } else {
+      return __uint_as_float(w[e]);
+    }
+  }
+};
+
+// Block = one (sequence, node); 8 lanes per head, each lane NC = dk/8 q channels and
+// the same k channels of its head.  The window's rows (newest first: the node, its
+// parent, ... then committed conv-state rows) are resolved once per block.
+template <typename A, int DK>
+__global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
+                                                       const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
+                                                       const int32_t* __restrict__ parent, int Tn, int H, int C, int W,
+                                                       float* __restrict__ qk, float* __restrict__ kq) {
+  constexpr int LPH = 8, NC = DK / LPH;
+  const int s = blockIdx.x / Tn, u = blockIdx.x % Tn;
+  const int tid = threadIdx.x;
+  __shared__ int par_s[kGdnMaxT];
+  __shared__ int win[kGdnMaxW];  // back b: tree row (>= 0) or committed conv-state row j as -(1 + j)
+  for (int i = tid; i < Tn; i += 256) par_s[i] = parent[(size_t)s * Tn + i];
+  __syncthreads();
+  if (tid == 0) {
+    // back 0 is the node; then the parent chain; past the root come the committed
+    // conv-state rows, newest (row W-2) first
+    int cur = u, in_tree = 1, beyond = 0;
+    for (int b = 0; b < W; ++b) {
       int r = u;
       if (b > 0) {
         if (in_tree) {
@@ -65,40 +103,57 @@ __global__ void __launch_bounds__(2 * DK) gdn_conv_kernel(const A* __restrict__ 
         }
         r = in_tree ? cur : -(1 + (W - 1 - (++beyond)));
       }
-      const A val = r >= 0 ? x[((size_t)s * Tn + r) * C + ch] : conv_state[((size_t)s * (W - 1) + (-r - 1)) * C + ch];
-      acc += conv_w[(size_t)ch * W + (W - 1 - b)] * Elem<A>::load(&val, 0);
-      if (b <= W - 2) conv_scratch[(((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C + ch] = val;
+      win[b] = r;
     }
   }
-  const float y = acc / (1.f + __expf(-acc));
-
-  __shared__ float ys[2 * DK];
-  __shared__ float red[2][2 * DK / 64 + 1];
-  ys[tid] = y;
   __syncthreads();
-  float kk = 0.f, kqv = 0.f;
-  if (tid < DK) {
-    const float kv = ys[DK + tid];
-    kk = kv * kv;
-    kqv = kv * ys[tid];
-  }
-  kk = wave_sum(kk);
-  kqv = wave_sum(kqv);
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = kk;
-    red[1][tid >> 6] = kqv;
-  }
-  __syncthreads();
-  float skk = 0.f, skq = 0.f;
-  for (int w = 0; w < (2 * DK + 63) / 64; ++w) {
-    skk += red[0][w];
-    skq += red[1][w];
-  }
-  const float rn = 1.f / sqrtf(skk + 1e-6f);
   const float qs = rsqrtf((float)DK);
-  const size_t base = (((size_t)s * Tn + u) * H + h) * 2 * DK;
-  qk[base + tid] = is_k ? y * rn : y * qs;
-  if (tid == 0) kq[((size_t)s * Tn + u) * H + h] = skq * rn * qs;
+  for (int hp = tid / LPH; hp < H; hp += 256 / LPH) {
+    const int j0 = (tid % LPH) * NC;
+    const int cq = hp * DK + j0, ck = H * DK + hp * DK + j0;  // first q and k channel of this lane
+    float yq[NC], yk[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) yq[e] = yk[e] = 0.f;
+    for (int b = 0; b < W; ++b) {
+      const int r = win[b];
+      const A* src = r >= 0 ? x + ((size_t)s * Tn + r) * C : conv_state + ((size_t)s * (W - 1) + (-r - 1)) * C;
+      A* dst = conv_scratch + (((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C;  // slot of back b (b <= W-2)
+      const int tap = W - 1 - b;
+      RowIO<A, NC> vq, vk;
+      vq.load(src + cq);
+      vk.load(src + ck);
+      if (b <= W - 2) {
+        vq.store(dst + cq);
+        vk.store(dst + ck);
+      }
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        yq[e] += conv_w[(size_t)(cq + e) * W + tap] * vq.get(e);
+        yk[e] += conv_w[(size_t)(ck + e) * W + tap] * vk.get(e);
+      }
+    }
+    float kk = 0.f, kqv = 0.f;
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      yq[e] = yq[e] / (1.f + __expf(-yq[e]));
+      yk[e] = yk[e] / (1.f + __expf(-yk[e]));
+      kk += yk[e] * yk[e];
+      kqv += yk[e] * yq[e];
+    }
+#pragma unroll
+    for (int off = LPH / 2; off > 0; off >>= 1) {
+      kk += __shfl_xor(kk, off, 64);
+      kqv += __shfl_xor(kqv, off, 64);
+    }
+    const float rn = 1.f / sqrtf(kk + 1e-6f);
+    float* out = qk + (((size_t)s * Tn + u) * H + hp) * 2 * DK;
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      out[j0 + e] = yq[e] * qs;
+      out[DK + j0 + e] = yk[e] * rn;
+    }
+    if (tid % LPH == 0) kq[((size_t)s * Tn + u) * H + hp] = kqv * rn * qs;
+  }
 }
 
 // ------------------------------------------------------------------ state walk
@@ -185,7 +240,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
   float* qk_s = reinterpret_cast<float*>(qk_s4);
   __shared__ float vv[kGdnMaxT][R];
   __shared__ float gb[kGdnMaxT][3];      // g, beta, k.q
-  __shared__ int par[kGdnMaxT], dep[kGdnMaxT], sz[kGdnMaxT], esib[kGdnMaxT], order[kGdnMaxT];
+  __shared__ int par[kGdnMaxT], nch[kGdnMaxT], sz[kGdnMaxT], esib[kGdnMaxT], order[kGdnMaxT];
 
   // ---- inputs of every node into LDS (independent loads)
   const float4* qk4 = reinterpret_cast<const float4*>(qk);
@@ -204,6 +259,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     gb[u][2] = kq[ti];
     par[u] = parent[(size_t)s * Tn + u];
     sz[u] = 0;
+    nch[u] = 0;
   }
   // committed state slice of this thread (used by nodes at depth 0)
   const V sc = load_vec<V, CPT, GS>(&S[(((size_t)s * H + h) * DV + r) * DK + c0]);
@@ -218,10 +274,10 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
       const int p = par[a];
       atomicAdd(&sz[a], 1);
       if (!(p >= 0 && p < a)) break;
+      if (a == tid) atomicAdd(&nch[p], 1);
       a = p;
       ++d_me;
     }
-    dep[tid] = d_me;
   }
   __syncthreads();
   if (tid < Tn) {
@@ -244,19 +300,27 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
       if (!(p >= 0 && p < a)) break;
       a = p;
     }
-    order[pos] = tid;
+    // node, depth, and whether a later child will need this node's state from the stack
+    order[pos] = tid | (d_me << 16) | ((nch[tid] >= 2) << 24);
   }
   __syncthreads();
 
-  // ---- walk
+  // ---- walk (the next node's word is read while the current one is processed).  In
+  // depth-first order a node's parent is either the node just processed (its state is
+  // still in registers) or an earlier node with two or more children (kept on the stack).
   RegStack<LMAX, V> stk;
+  V sprev = sc;
+  int dprev = -1;
+  int nxt = order[0];
   for (int k = 0; k < Tn; ++k) {
-    const int u = __builtin_amdgcn_readfirstlane(order[k]);
-    const int d = __builtin_amdgcn_readfirstlane(dep[u]);
+    const int cur = __builtin_amdgcn_readfirstlane(nxt);
+    if (k + 1 < Tn) nxt = order[k + 1];
+    const int u = cur & 0xffff, d = (cur >> 16) & 0xff;
+    const bool save = (cur >> 24) & 1;
     if (d > L) continue;  // deeper than the stated bound: not processed
     const V qv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + c0]);
     const V kv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + DK + c0]);
-    const V sp = d == 0 ? sc : stk.get(d - 1);
+    const V sp = d == 0 ? sc : (d == dprev + 1 ? sprev : stk.get(d - 1));
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
@@ -271,7 +335,9 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     const float gi = gb[u][0], bi = gb[u][1];
     const float delta = bi * (vv[u][rl] - gi * a);
     const V sn = gi * sp + delta * kv;
-    stk.put(d, sn);
+    if (save) stk.put(d, sn);
+    sprev = sn;
+    dprev = d;
     const size_t ti = ((size_t)s * Tn + u) * H + h;
     store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
     if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * gb[u][2]);
@@ -294,7 +360,7 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   float* qk = static_cast<float*>(ws);
   float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                        ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256);
-  hipLaunchKernelGGL((gdn_conv_kernel<A, DK>), dim3(n * T, H), dim3(2 * DK), 0, st, static_cast<const A*>(x),
+  hipLaunchKernelGGL((gdn_conv_kernel<A, DK>), dim3(n * T), dim3(256), 0, st, static_cast<const A*>(x),
                      conv_w, static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk,
                      kq);
   const size_t smem = (size_t)T * 2 * DK * sizeof(float);
