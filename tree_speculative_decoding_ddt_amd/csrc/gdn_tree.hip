@@ -11,10 +11,10 @@
 //   S_i = g S_p + beta (v - g S_p k) k^T;  o_i = S_i q = g (S_p q) + beta (v - g S_p k) (k.q)
 //
 // Two kernels:
-//  gdn_conv   grid (n*T): one block per node, 8 lanes per head; gathers the node's conv
-//             window along its parent chain, writes the conv scratch (exact copies),
-//             and leaves q (scaled), k (normalised) and k.q in fp32 in the workspace.
-//             Every node is independent here.
+//  gdn_conv   grid (n*T, heads/HG): a block per node and group of heads, dk/4 lanes per
+//             head; gathers the node's conv window along its parent chain, writes the
+//             conv scratch (exact copies), and leaves q (scaled), k (normalised) and k.q
+//             in fp32 in the workspace.  Every node is independent here.
 //  gdn_state  grid (n*H, dv/R): a block owns R rows of one head's [dv][dk] state, a
 //             thread CPT columns of one row (groups of 4, so that a wave's 16-byte
 //             stores cover whole row segments).  The block loads every node's
@@ -74,15 +74,18 @@ struct RowIO {
   }
 };
 
-// Block = one (sequence, node); 8 lanes per head, each lane NC = dk/8 q channels and
-// the same k channels of its head.  The window's rows (newest first: the node, its
-// parent, ... then committed conv-state rows) are resolved once per block.
-template <typename A, int DK>
+// Block = (sequence, node, group of HG heads); LPH lanes per head, each lane NC = 4 q
+// channels and the same 4 k channels of its head.  The window's rows (newest first: the
+// node, its parent, ... then committed conv-state rows) are resolved once per block.
+// WT > 0 fixes the conv width at compile time: a lane's weights (4 channels x WT taps,
+// contiguous) then come in 16-byte loads and the tap loop unrolls.
+template <typename A, int DK, int WT>
 __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
                                                        const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
-                                                       const int32_t* __restrict__ parent, int Tn, int H, int C, int W,
-                                                       float* __restrict__ qk, float* __restrict__ kq) {
-  constexpr int LPH = 8, NC = DK / LPH;
+                                                       const int32_t* __restrict__ parent, int Tn, int H, int C,
+                                                       int W_rt, float* __restrict__ qk, float* __restrict__ kq) {
+  constexpr int NC = 4, LPH = DK / NC, HG = 256 / LPH;
+  const int W = WT > 0 ? WT : W_rt;
   const int s = blockIdx.x / Tn, u = blockIdx.x % Tn;
   const int tid = threadIdx.x;
   __shared__ int par_s[kGdnMaxT];
@@ -107,53 +110,86 @@ __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, 
     }
   }
   __syncthreads();
-  const float qs = rsqrtf((float)DK);
-  for (int hp = tid / LPH; hp < H; hp += 256 / LPH) {
-    const int j0 = (tid % LPH) * NC;
-    const int cq = hp * DK + j0, ck = H * DK + hp * DK + j0;  // first q and k channel of this lane
-    float yq[NC], yk[NC];
+  const int hp = blockIdx.y * HG + tid / LPH;
+  if (hp >= H) return;
+  const int j0 = (tid % LPH) * NC;
+  const int cq = hp * DK + j0, ck = H * DK + hp * DK + j0;  // first q and k channel of this lane
+  float yq[NC], yk[NC];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) yq[e] = yk[e] = 0.f;
-    for (int b = 0; b < W; ++b) {
-      const int r = win[b];
-      const A* src = r >= 0 ? x + ((size_t)s * Tn + r) * C : conv_state + ((size_t)s * (W - 1) + (-r - 1)) * C;
-      A* dst = conv_scratch + (((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C;  // slot of back b (b <= W-2)
-      const int tap = W - 1 - b;
-      RowIO<A, NC> vq, vk;
-      vq.load(src + cq);
-      vk.load(src + ck);
-      if (b <= W - 2) {
-        vq.store(dst + cq);
-        vk.store(dst + ck);
+  for (int e = 0; e < NC; ++e) yq[e] = yk[e] = 0.f;
+  auto tap_step = [&](int b, const float* wq, const float* wk) {  // wq/wk: this tap's weight per channel
+    const int r = win[b];
+    const A* src = r >= 0 ? x + ((size_t)s * Tn + r) * C : conv_state + ((size_t)s * (W - 1) + (-r - 1)) * C;
+    RowIO<A, NC> vq, vk;
+    vq.load(src + cq);
+    vk.load(src + ck);
+    if (b <= W - 2) {
+      A* dst = conv_scratch + (((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C;  // slot of back b
+      vq.store(dst + cq);
+      vk.store(dst + ck);
+    }
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      yq[e] += wq[e] * vq.get(e);
+      yk[e] += wk[e] * vk.get(e);
+    }
+  };
+  if constexpr (WT > 0) {
+    float wq[NC][WT], wk[NC][WT];  // [channel][tap]: contiguous in conv_w
+#pragma unroll
+    for (int i = 0; i < NC * WT; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(conv_w + (size_t)cq * WT + i);
+      const float4 c = *reinterpret_cast<const float4*>(conv_w + (size_t)ck * WT + i);
+      const float av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        wq[(i + t) / WT][(i + t) % WT] = av[t];
+        wk[(i + t) / WT][(i + t) % WT] = cv[t];
       }
+    }
+#pragma unroll
+    for (int b = 0; b < WT; ++b) {
+      float tq[NC], tk[NC];
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        yq[e] += conv_w[(size_t)(cq + e) * W + tap] * vq.get(e);
-        yk[e] += conv_w[(size_t)(ck + e) * W + tap] * vk.get(e);
+        tq[e] = wq[e][WT - 1 - b];
+        tk[e] = wk[e][WT - 1 - b];
       }
+      tap_step(b, tq, tk);
     }
-    float kk = 0.f, kqv = 0.f;
+  } else {
+    for (int b = 0; b < W; ++b) {
+      float tq[NC], tk[NC];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) {
-      yq[e] = yq[e] / (1.f + __expf(-yq[e]));
-      yk[e] = yk[e] / (1.f + __expf(-yk[e]));
-      kk += yk[e] * yk[e];
-      kqv += yk[e] * yq[e];
+      for (int e = 0; e < NC; ++e) {
+        tq[e] = conv_w[(size_t)(cq + e) * W + (W - 1 - b)];
+        tk[e] = conv_w[(size_t)(ck + e) * W + (W - 1 - b)];
+      }
+      tap_step(b, tq, tk);
     }
-#pragma unroll
-    for (int off = LPH / 2; off > 0; off >>= 1) {
-      kk += __shfl_xor(kk, off, 64);
-      kqv += __shfl_xor(kqv, off, 64);
-    }
-    const float rn = 1.f / sqrtf(kk + 1e-6f);
-    float* out = qk + (((size_t)s * Tn + u) * H + hp) * 2 * DK;
-#pragma unroll
-    for (int e = 0; e < NC; ++e) {
-      out[j0 + e] = yq[e] * qs;
-      out[DK + j0 + e] = yk[e] * rn;
-    }
-    if (tid % LPH == 0) kq[((size_t)s * Tn + u) * H + hp] = kqv * rn * qs;
   }
+  float kk = 0.f, kqv = 0.f;
+#pragma unroll
+  for (int e = 0; e < NC; ++e) {
+    yq[e] = yq[e] / (1.f + __expf(-yq[e]));
+    yk[e] = yk[e] / (1.f + __expf(-yk[e]));
+    kk += yk[e] * yk[e];
+    kqv += yk[e] * yq[e];
+  }
+#pragma unroll
+  for (int off = LPH / 2; off > 0; off >>= 1) {
+    kk += __shfl_xor(kk, off, 64);
+    kqv += __shfl_xor(kqv, off, 64);
+  }
+  const float rn = 1.f / sqrtf(kk + 1e-6f);
+  const float qs = rsqrtf((float)DK);
+  float* out = qk + (((size_t)s * Tn + u) * H + hp) * 2 * DK;
+#pragma unroll
+  for (int e = 0; e < NC; ++e) {
+    out[j0 + e] = yq[e] * qs;
+    out[DK + j0 + e] = yk[e] * rn;
+  }
+  if (tid % LPH == 0) kq[((size_t)s * Tn + u) * H + hp] = kqv * rn * qs;
 }
 
 // ------------------------------------------------------------------ state walk
@@ -360,9 +396,13 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   float* qk = static_cast<float*>(ws);
   float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                        ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256);
-  hipLaunchKernelGGL((gdn_conv_kernel<A, DK>), dim3(n * T), dim3(256), 0, st, static_cast<const A*>(x),
-                     conv_w, static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk,
-                     kq);
+  const dim3 cgrid(n * T, (H + 256 / (DK / 4) - 1) / (256 / (DK / 4)));
+  if (W == 4)
+    hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 4>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
+                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq);
+  else
+    hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 0>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
+                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq);
   const size_t smem = (size_t)T * 2 * DK * sizeof(float);
   if (L < 16) {
     auto kern = gdn_state_kernel<A, DK, CPT, 16>;
