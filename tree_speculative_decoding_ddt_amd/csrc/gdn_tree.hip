@@ -33,6 +33,53 @@ namespace ddt {
 constexpr int kGdnMaxT = 128;
 constexpr int kGdnMaxW = 8;
 
+// Depth-first (pre-)order of one sequence's tree, computed in parallel over nodes by a
+// block of >= Tn threads: subtree sizes, then each node's offset among its earlier
+// siblings, then its position.  A row whose parent is not an earlier row starts a tree
+// of its own (it reads the committed state).  Word k = node | depth << 16 | save << 24,
+// where save marks a node with two or more children (a later child takes its state
+// from the stack; a first child takes it from the node just before it).
+__device__ void dfs_order(const int* par, int Tn, int* sz, int* nch, int* esib, int32_t* out) {
+  const int tid = threadIdx.x;
+  for (int u = tid; u < Tn; u += blockDim.x) sz[u] = nch[u] = 0;
+  __syncthreads();
+  int d_me = 0;
+  if (tid < Tn) {
+    int a = tid;
+    while (true) {
+      const int p = par[a];
+      atomicAdd(&sz[a], 1);
+      if (!(p >= 0 && p < a)) break;
+      if (a == tid) atomicAdd(&nch[p], 1);
+      a = p;
+      ++d_me;
+    }
+  }
+  __syncthreads();
+  if (tid < Tn) {
+    const int p = par[tid];
+    const int vp = (p >= 0 && p < tid) ? p : -1;
+    int e = 0;
+    for (int j = 0; j < tid; ++j) {
+      const int pj = par[j];
+      const int vpj = (pj >= 0 && pj < j) ? pj : -1;
+      if (vpj == vp) e += sz[j];
+    }
+    esib[tid] = e;
+  }
+  __syncthreads();
+  if (tid < Tn) {
+    int pos = d_me, a = tid;
+    while (true) {
+      pos += esib[a];
+      const int p = par[a];
+      if (!(p >= 0 && p < a)) break;
+      a = p;
+    }
+    out[pos] = tid | (d_me << 16) | ((nch[tid] >= 2) << 24);
+  }
+}
+
 // ------------------------------------------------------------------ conv + q/k
 // N consecutive activations of one row as raw 32-bit words, moved in 16- or 8-byte chunks.
 template <typename A, int N>
@@ -83,7 +130,8 @@ template <typename A, int DK, int WT>
 __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
                                                        const A* __restrict__ conv_state, A* __restrict__ conv_scratch,
                                                        const int32_t* __restrict__ parent, int Tn, int H, int C,
-                                                       int W_rt, float* __restrict__ qk, float* __restrict__ kq) {
+                                                       int W_rt, float* __restrict__ qk, float* __restrict__ kq,
+                                                       int32_t* __restrict__ order) {
   constexpr int NC = 4, LPH = DK / NC, HG = 256 / LPH;
   const int W = WT > 0 ? WT : W_rt;
   const int s = blockIdx.x / Tn, u = blockIdx.x % Tn;
@@ -110,6 +158,10 @@ __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, 
     }
   }
   __syncthreads();
+  if (u == 0 && blockIdx.y == 0) {  // one block per sequence also orders its tree for the walk
+    __shared__ int sz[kGdnMaxT], nch[kGdnMaxT], esib[kGdnMaxT];
+    dfs_order(par_s, Tn, sz, nch, esib, order + (size_t)s * Tn);
+  }
   const int hp = blockIdx.y * HG + tid / LPH;
   if (hp >= H) return;
   const int j0 = (tid % LPH) * NC;
@@ -260,7 +312,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
                                                         const A* __restrict__ v, const float* __restrict__ beta,
                                                         const float* __restrict__ g, const float* __restrict__ S,
                                                         float* __restrict__ S_scratch, A* __restrict__ o,
-                                                        const int32_t* __restrict__ parent, int Tn, int L, int H) {
+                                                        const int32_t* __restrict__ order_g, int Tn, int L, int H) {
   typedef typename VecT<CPT>::type V;
   constexpr int DV = DK;
   constexpr int LPR = DK / CPT;          // lanes per state row
@@ -276,7 +328,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
   float* qk_s = reinterpret_cast<float*>(qk_s4);
   __shared__ float vv[kGdnMaxT][R];
   __shared__ float gb[kGdnMaxT][3];      // g, beta, k.q
-  __shared__ int par[kGdnMaxT], nch[kGdnMaxT], sz[kGdnMaxT], esib[kGdnMaxT], order[kGdnMaxT];
+  __shared__ int order[kGdnMaxT];
 
   // ---- inputs of every node into LDS (independent loads)
   const float4* qk4 = reinterpret_cast<const float4*>(qk);
@@ -293,52 +345,10 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     gb[u][0] = g[ti];
     gb[u][1] = beta[ti];
     gb[u][2] = kq[ti];
-    par[u] = parent[(size_t)s * Tn + u];
-    sz[u] = 0;
-    nch[u] = 0;
+    order[u] = order_g[(size_t)s * Tn + u];  // depth-first words from the conv kernel
   }
   // committed state slice of this thread (used by nodes at depth 0)
   const V sc = load_vec<V, CPT, GS>(&S[(((size_t)s * H + h) * DV + r) * DK + c0]);
-  __syncthreads();
-
-  // ---- depth-first order, computed in parallel over nodes
-  // a row whose parent is not an earlier row starts a tree of its own (reads the committed state)
-  int d_me = 0;
-  if (tid < Tn) {
-    int a = tid;
-    while (true) {
-      const int p = par[a];
-      atomicAdd(&sz[a], 1);
-      if (!(p >= 0 && p < a)) break;
-      if (a == tid) atomicAdd(&nch[p], 1);
-      a = p;
-      ++d_me;
-    }
-  }
-  __syncthreads();
-  if (tid < Tn) {
-    const int p = par[tid];
-    const int vp = (p >= 0 && p < tid) ? p : -1;
-    int e = 0;
-    for (int j = 0; j < tid; ++j) {
-      const int pj = par[j];
-      const int vpj = (pj >= 0 && pj < j) ? pj : -1;
-      if (vpj == vp) e += sz[j];
-    }
-    esib[tid] = e;
-  }
-  __syncthreads();
-  if (tid < Tn) {
-    int pos = d_me, a = tid;
-    while (true) {
-      pos += esib[a];
-      const int p = par[a];
-      if (!(p >= 0 && p < a)) break;
-      a = p;
-    }
-    // node, depth, and whether a later child will need this node's state from the stack
-    order[pos] = tid | (d_me << 16) | ((nch[tid] >= 2) << 24);
-  }
   __syncthreads();
 
   // ---- walk (the next node's word is read while the current one is processed).  In
@@ -383,7 +393,8 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
 size_t gdn_workspace(int n, int T, int H, int dk) {
   const size_t qk = (size_t)n * T * H * 2 * dk * sizeof(float);
   const size_t kq = (size_t)n * T * H * sizeof(float);
-  return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256;
+  const size_t ord = (size_t)n * T * sizeof(int32_t);
+  return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256 + (ord + 255) / 256 * 256;
 }
 
 template <typename A, int DK>
@@ -393,27 +404,29 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread, depth bound < 16
   constexpr int R = 256 / (DK / CPT);
   constexpr int R4 = 256 / (DK / 4);      // 4 columns per thread, depth bound < 32
+  const size_t qk_b = ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256;
+  const size_t kq_b = ((size_t)n * T * H * sizeof(float) + 255) / 256 * 256;
   float* qk = static_cast<float*>(ws);
-  float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
-                                       ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256);
+  float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + qk_b);
+  int32_t* ord = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + qk_b + kq_b);
   const dim3 cgrid(n * T, (H + 256 / (DK / 4) - 1) / (256 / (DK / 4)));
   if (W == 4)
     hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 4>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
-                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq);
+                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq, ord);
   else
     hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 0>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
-                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq);
+                       static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq, ord);
   const size_t smem = (size_t)T * 2 * DK * sizeof(float);
   if (L < 16) {
     auto kern = gdn_state_kernel<A, DK, CPT, 16>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
-                       S_scratch, static_cast<A*>(o), parent, T, L, H);
+                       S_scratch, static_cast<A*>(o), ord, T, L, H);
   } else {
     auto kern = gdn_state_kernel<A, DK, 4, 32>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     hipLaunchKernelGGL(kern, dim3(n * H, DK / R4), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
-                       S_scratch, static_cast<A*>(o), parent, T, L, H);
+                       S_scratch, static_cast<A*>(o), ord, T, L, H);
   }
 }
 
