@@ -119,3 +119,89 @@ def test_bf16_hybrid_step_reduced():
     say("step bf16 hybrid reduced: n=2 V=151936 L=15 B=64 prefix 640, 1 attn + 3 gdn")
     cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=32, n_attn=1, n_gdn=3)
     run_rounds(cfg, "bf16", seed=5, rounds=2)
+
+
+def test_full_size_hybrid_round_sampled():
+    """One round at the full hybrid shapes (8 sequences, vocab 151936, depth 15, B 64,
+    prefix 16384, 16 attention + 48 GDN layers), inputs drawn on the device as the
+    benchmark draws them; the oracle checks sampled outputs one by one."""
+    from oracle import accept as oacc
+    from oracle import attention as oattn
+    from oracle import gdn as ogdn
+
+    say("step full size: n=8 prefix 16384, 16 attn + 48 gdn (sampled oracle checks)")
+    cfg = HybridConfig(n=8, prefix=16384, extra_cap=64)
+    step = HybridVerifyStep(cfg)
+    step.fill_random(seed=11)
+    P0 = cfg.prefix
+    g0 = step.gdn[0]
+    S_before = down(g0["S"][0])
+    cs_before = down(g0["conv_state"][0])
+    tail_before = down(step.attn[3]["k_cache"][:, :, P0 + cfg.L + 1:P0 + cfg.L + 5])
+    step()
+    torch.cuda.synchronize()
+
+    z = down(step.draft_logits)
+    tree = {k: down(step.tree[k]) for k in ("tok", "parent", "depth")}
+    anc = anc_numpy(step.tree["anc"])
+    acc_rows, acc_len = down(step.acc["acc_rows"]), down(step.acc["acc_len"])
+    bonus, prefix = down(step.acc["bonus"]), down(step.prefix_len)
+
+    # tree topology, bit-exact, on the sequences whose draws keep the stated score gaps
+    checked = 0
+    for s in range(cfg.n):
+        if not gaps.gaps_ok(z[s], cfg.B):
+            continue
+        ref = otree.build_tree(z[s], cfg.B, 0)
+        for key in ("tok", "parent", "depth"):
+            np.testing.assert_array_equal(tree[key][s], ref[key], err_msg="%s seq %d" % (key, s))
+        np.testing.assert_array_equal(anc[s], ref["anc"], err_msg="anc seq %d" % s)
+        checked += 1
+    assert checked >= 1
+    say("tree checked on", checked, "sequences")
+
+    # walk against the target argmaxes, bit-exact (the bonus is the next root)
+    for s in (0, 3, 7):
+        y = down(step.target_logits[s])
+        rows, a, b = oacc.tree_accept(y, tree["tok"][s], tree["parent"][s], cfg.L)
+        np.testing.assert_array_equal(acc_rows[s], rows)
+        assert acc_len[s] == a and bonus[s] == b
+    np.testing.assert_array_equal(down(step.root_token), bonus)
+
+    # attention: sampled rows of the first and last layer (the commit only wrote rows >= P0)
+    for j in (0, cfg.n_attn - 1):
+        lay = step.attn[j]
+        for s in (0, 5):
+            kc, vc = down(lay["k_cache"][s]), down(lay["v_cache"][s])
+            kt, vt = down(lay["k_tree"][s]), down(lay["v_tree"][s])
+            q, out = down(lay["q"][s]), down(lay["out"][s])
+            for i in (0, 17, cfg.B):
+                ref = oattn.tree_attention_row(q[i], kc, vc, P0, kt, vt, anc[s][i])
+                assert_close(out[i], ref, "bf16", "attn layer %d seq %d row %d" % (j, s, i))
+
+    # GDN layer 0, sequence 0, every head, from the state before the commit
+    ro, rS, rc = ogdn.gdn_tree_step(down(g0["x"][0]), down(g0["conv_w"]), cs_before, down(g0["v"][0]),
+                                    down(g0["beta"][0]), down(g0["g"][0]), S_before, tree["parent"][0],
+                                    cfg.H, cfg.dk)
+    assert_close(down(g0["out"]["o"][0]), ro, "bf16", "gdn o")
+    assert_close(down(g0["out"]["S_scratch"][0]), rS, "f32", "gdn S_scratch")
+    np.testing.assert_array_equal(down(g0["out"]["conv_scratch"][0]), rc)
+
+    # commit: prefix growth, exact KV rows of the accepted path, deepest row's states
+    np.testing.assert_array_equal(prefix, P0 + acc_len + 1)
+    for j in (0, 3, cfg.n_attn - 1):
+        lay = step.attn[j]
+        for s in range(cfg.n):
+            a = int(acc_len[s])
+            rows = acc_rows[s][:a + 1].astype(np.int64)
+            for name, tree_name in (("k_cache", "k_tree"), ("v_cache", "v_tree")):
+                got = lay[name][s][:, P0:P0 + a + 1]
+                want = lay[tree_name][s][:, torch.as_tensor(rows, device=got.device)]
+                assert torch.equal(got, want), (name, j, s)
+    np.testing.assert_array_equal(down(step.attn[3]["k_cache"][:, :, P0 + cfg.L + 1:P0 + cfg.L + 5]), tail_before)
+    for j in (0, 24, cfg.n_gdn - 1):
+        g = step.gdn[j]
+        for s in range(cfg.n):
+            r = int(acc_rows[s][int(acc_len[s])])
+            assert torch.equal(g["S"][s], g["out"]["S_scratch"][s, r]), ("S", j, s)
+            assert torch.equal(g["conv_state"][s], g["out"]["conv_scratch"][s, r]), ("conv", j, s)
