@@ -536,7 +536,7 @@ __global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __rest
 #define DDT_ATTN_NW128 8
 #endif
 #ifndef DDT_ATTN_PK
-#define DDT_ATTN_PK 0  // K operand reads pinned ahead of their products (0: scheduler's order)
+#define DDT_ATTN_PK 4  // K operand reads pinned ahead of their products (0: scheduler's order)
 #endif
 #ifndef DDT_ATTN_PV
 #define DDT_ATTN_PV 0  // V operand blocks pinned ahead of their products (0: scheduler's order)
