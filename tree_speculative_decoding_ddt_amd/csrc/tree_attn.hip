@@ -35,6 +35,9 @@ constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
 constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
 constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, O) partials of a
                                      // split cost about as much traffic as 400 keys of K/V
+#ifndef DDT_ATTN_PVROLL
+#define DDT_ATTN_PVROLL 1  // transposing V reads issued two blocks ahead of their products
+#endif
 #ifndef DDT_ATTN_PRIO
 #define DDT_ATTN_PRIO 1  // raise the wave priority during the MFMA phases (the other wave of the SIMD runs its softmax)
 #endif
@@ -294,6 +297,28 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   // two transposing reads per block issued PV blocks ahead of their products
   auto pv_phase = [&](int stage) {
     const uint8_t* Vs = lds + stage * 2 * TILE;
+#if DDT_ATTN_PVROLL
+    // rolling prefetch: the transposing reads of block b+2 are issued before the
+    // products of block b (a sched_barrier after each block keeps that order)
+    s16x4 lo[3], hi[3];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      lo[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[0] + 32 * b));
+      hi[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[1] + 32 * b));
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      if (b + 2 < DB) {
+        lo[(b + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[0] + 32 * (b + 2)));
+        hi[(b + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[1] + 32 * (b + 2)));
+      }
+      const bf16x8 A =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[b % 3], hi[b % 3], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pp[j], O[j][b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#else
     bf16x8 Vop[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -313,6 +338,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         if (b + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
     }
+#endif
   };
   // ancestor mask of this lane's row in tile j (tree tiles only: read when needed)
   auto anc_row = [&](int j) -> uint64_t {
