@@ -8,6 +8,8 @@
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
  *   ddt_commit         copy only the accepted path into the committed buffers
+ *   ddt_gdn_replay     (alternative to storing node states) advance the committed GDN
+ *                      and conv state along the accepted path
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller; the library allocates
@@ -133,7 +135,11 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache,
  *   parent [n][T] int32: parent[i] < i, or < 0 for a row that reads the committed state
  *   L: upper bound on the tree depth (row depth by parent chain), L <= 31; rows deeper
  *      than L are not processed
- *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q in fp32)
+ *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q in fp32,
+ *       and the tree's depth-first order)
+ * S_scratch and conv_scratch may both be NULL: then no node state is stored (o is still
+ * written for every node) and the commit replays the accepted path with ddt_gdn_replay.
+ * x, conv_state, conv_scratch, S, S_scratch and ws must be 16-byte aligned.
  * Built: dk = dv in {32, 64, 128}; W in [2, 8]; C == 2*H*dk.
  */
 size_t ddt_gdn_tree_step_workspace(int n, int B, int H, int dk);
@@ -191,6 +197,38 @@ int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
                const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_dt,
                const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
                int act_dt, int n, int B, int L, void* stream);
+
+/* ---------------------------------------------------------------- GDN replay on commit
+ * [notes] "Where the next step is": scratch-buffer GDN and conv replay; [spec] "The
+ * DDTree Integration Challenge": recompute or compact the recurrent state instead of
+ * keeping a copy per branch.  For a round whose tree step stored no node state
+ * (ddt_gdn_tree_step with S_scratch = conv_scratch = NULL), advance each GDN layer's
+ * committed state along the accepted path.  Call it after ddt_commit of the same round
+ * (which sets acc_len to -1 where nothing may be written); sequences with acc_len < 0,
+ * or whose path rows are out of range, are left untouched.
+ * For every sequence s with a = acc_len[s] >= 0 and path rows r_j = acc_rows[s][j]:
+ *   for j = 0..a: window = [committed conv rows ..., x[r_0], ..., x[r_j]] (last W),
+ *                 k = normalised SiLU(conv) of the k channels (as in the tree step),
+ *                 S = g S + beta (v - g S k) k^T with the node's v, beta, g
+ *   conv_state[s] = the last W-1 rows of the window of r_a (exact copies)
+ * The result equals ddt_commit of stored states (S = S_scratch[r_a], conv_state =
+ * conv_scratch[r_a]) up to fp32 rounding order of S.  layers is a HOST array of n_layers
+ * entries of device pointers, each with the tree step's inputs of that layer.
+ * Built: dk = dv in {32, 64, 128}; W in [2, 8]; C == 2*H*dk; L <= 63.
+ */
+typedef struct {
+  const void* x;        /* [n][T][C] (act_dt), the tree step's input */
+  const float* conv_w;  /* [C][W] */
+  const void* v;        /* [n][T][H][dv] (act_dt) */
+  const float* beta;    /* [n][T][H] */
+  const float* g;       /* [n][T][H] */
+  float* S;             /* [n][H][dv][dk] committed state, advanced in place (16-byte aligned) */
+  void* conv_state;     /* [n][W-1][C] (act_dt) committed conv rows, replaced in place */
+} ddt_gdn_replay_layer;
+
+int ddt_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,
+                   int n_layers, int H, int dk, int dv, int C, int W, int act_dt, int n, int B, int L,
+                   void* stream);
 
 #ifdef __cplusplus
 }

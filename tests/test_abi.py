@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -109,6 +109,29 @@ def test_accept_and_commit_validation():
     c[6] = 60
     kv[0] = ddt.KVLayer(256, 256, 256, 256)
     assert status("ddt_commit", *c) == ddt.DDT_ERR_ARG        # D*2 bytes not a multiple of 16
+
+
+def test_gdn_replay_validation():
+    lay = (ddt.GDNReplayLayer * 1)(ddt.GDNReplayLayer(256, 256, 256, 256, 256, 256, 256))
+    #     rows acc  layers n_l H  dk  dv  C    W  dt n  B  L
+    r = [P, P, lay, 1, 2, 32, 32, 128, 4, 1, 1, 8, 4, None]
+    assert status("ddt_gdn_replay", *(r[:3] + [0] + r[4:])) == ddt.DDT_OK   # no layers: nothing to do
+    r2 = list(r); r2[0] = None
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_ARG                 # null acc_rows
+    r2 = list(r); r2[7] = 96
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_ARG                 # C != 2*H*dk
+    r2 = list(r); r2[5] = r2[6] = 48; r2[7] = 192
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_UNSUPPORTED         # dk not built
+    r2 = list(r); r2[8] = 9
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_UNSUPPORTED         # W > 8
+    r2 = list(r); r2[12] = 64
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_ARG                 # L > 63
+    r2 = list(r); r2[9] = 2
+    assert status("ddt_gdn_replay", *r2) == ddt.DDT_ERR_UNSUPPORTED         # dtype
+    lay[0] = ddt.GDNReplayLayer(256, 256, 256, None, 256, 256, 256)
+    assert status("ddt_gdn_replay", *r) == ddt.DDT_ERR_ARG                  # null beta
+    lay[0] = ddt.GDNReplayLayer(256, 256, 256, 256, 256, 260, 256)
+    assert status("ddt_gdn_replay", *r) == ddt.DDT_ERR_ARG                  # misaligned S
 
 
 def test_binding_refuses_cpu_tensors():

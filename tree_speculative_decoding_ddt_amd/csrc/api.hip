@@ -156,18 +156,46 @@ int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state
                       const float* beta, const float* g, const float* S, float* S_scratch, void* o,
                       const int32_t* parent, int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
                       void* ws, size_t ws_bytes, void* stream) {
-  DDT_NEED(x); DDT_NEED(conv_w); DDT_NEED(conv_state); DDT_NEED(conv_scratch); DDT_NEED(v);
-  DDT_NEED(beta); DDT_NEED(g); DDT_NEED(S); DDT_NEED(S_scratch); DDT_NEED(o); DDT_NEED(parent); DDT_NEED(ws);
+  DDT_NEED(x); DDT_NEED(conv_w); DDT_NEED(conv_state); DDT_NEED(v);
+  DDT_NEED(beta); DDT_NEED(g); DDT_NEED(S); DDT_NEED(o); DDT_NEED(parent); DDT_NEED(ws);
+  // S_scratch and conv_scratch may be NULL: nothing of the nodes' states is stored
+  // (the commit then replays the accepted path, ddt_gdn_replay)
   const int st = gdn_args(n, B, L, H, dk, dv, C, W, act_dt);
   if (st != DDT_OK) return st;
   const size_t need = ddt::gdn_workspace(n, B + 1, H, dk);
   DDT_CHECK(ws_bytes >= need, DDT_ERR_WORKSPACE, "ddt_gdn_tree_step: workspace %zu < %zu bytes", ws_bytes, need);
-  DDT_CHECK(aligned16(ws) && aligned16(S) && aligned16(S_scratch), DDT_ERR_ARG,
-            "ddt_gdn_tree_step: workspace and S buffers must be 16-byte aligned");
+  DDT_CHECK(aligned16(ws) && aligned16(S) && aligned16(S_scratch) && aligned16(x) && aligned16(conv_state) &&
+                aligned16(conv_scratch),
+            DDT_ERR_ARG, "ddt_gdn_tree_step: workspace, state and activation buffers must be 16-byte aligned");
   return hip_status(ddt::launch_gdn_tree_step(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o,
                                               parent, n, B + 1, L, H, dk, C, W, act_dt, ws,
                                               static_cast<hipStream_t>(stream)),
                     "ddt_gdn_tree_step");
+}
+
+// ---------------------------------------------------------------- GDN replay on commit
+int ddt_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,
+                   int n_layers, int H, int dk, int dv, int C, int W, int act_dt, int n, int B, int L,
+                   void* stream) {
+  DDT_NEED(acc_rows); DDT_NEED(acc_len);
+  DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && L >= 0 && L <= 63 && n_layers >= 0 && H >= 1, DDT_ERR_ARG,
+            "ddt_gdn_replay: need n>=1, 0<=B<=64, 0<=L<=63, n_layers>=0, H>=1");
+  DDT_CHECK(dt_ok(act_dt), DDT_ERR_UNSUPPORTED, "ddt_gdn_replay: dtype %d", act_dt);
+  DDT_CHECK(dk == dv && (dk == 32 || dk == 64 || dk == 128), DDT_ERR_UNSUPPORTED,
+            "ddt_gdn_replay: dk=%d dv=%d not built (dk == dv in {32, 64, 128})", dk, dv);
+  DDT_CHECK(W >= 2 && W <= 8, DDT_ERR_UNSUPPORTED, "ddt_gdn_replay: conv width W=%d not in [2, 8]", W);
+  DDT_CHECK(C == 2 * H * dk, DDT_ERR_ARG, "ddt_gdn_replay: C=%d must equal 2*H*dk=%d", C, 2 * H * dk);
+  if (n_layers == 0) return DDT_OK;
+  DDT_NEED(layers);
+  for (int i = 0; i < n_layers; ++i) {
+    const ddt_gdn_replay_layer& y = layers[i];
+    DDT_CHECK(y.x && y.conv_w && y.v && y.beta && y.g && y.S && y.conv_state, DDT_ERR_ARG,
+              "ddt_gdn_replay: null pointer in layer %d", i);
+    DDT_CHECK(aligned16(y.S), DDT_ERR_ARG, "ddt_gdn_replay: S of layer %d not 16-byte aligned", i);
+  }
+  return hip_status(ddt::launch_gdn_replay(acc_rows, acc_len, layers, n_layers, H, dk, C, W, act_dt, n, B + 1, L,
+                                           static_cast<hipStream_t>(stream)),
+                    "ddt_gdn_replay");
 }
 
 // ---------------------------------------------------------------- tree walk

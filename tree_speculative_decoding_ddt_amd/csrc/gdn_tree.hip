@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, 
     RowIO<A, NC> vq, vk;
     vq.load(src + cq);
     vk.load(src + ck);
-    if (b <= W - 2) {
+    if (b <= W - 2 && conv_scratch != nullptr) {
       A* dst = conv_scratch + (((size_t)s * Tn + u) * (W - 1) + (W - 2 - b)) * C;  // slot of back b
       vq.store(dst + cq);
       vk.store(dst + ck);
@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     sprev = sn;
     dprev = d;
     const size_t ti = ((size_t)s * Tn + u) * H + h;
-    store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
+    if (S_scratch != nullptr) store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
     if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * gb[u][2]);
   }
 }

@@ -46,6 +46,11 @@ hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* 
                                 const int32_t* parent, int n, int T, int L, int H, int dk, int C,
                                 int W, int act_dt, void* ws, hipStream_t st);
 
+// ---- GDN replay on commit
+hipError_t launch_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,
+                             int n_layers, int H, int dk, int C, int W, int act_dt, int n, int T, int L,
+                             hipStream_t st);
+
 // ---- tree walk
 struct AcceptPlan {
   int S;          // chunks per row for the argmax scan

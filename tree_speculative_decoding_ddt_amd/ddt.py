@@ -22,7 +22,7 @@ EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
            "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
-           "ddt_commit")
+           "ddt_commit", "ddt_gdn_replay")
 
 
 class DDTError(RuntimeError):
@@ -41,6 +41,12 @@ class KVLayer(ctypes.Structure):
 class GDNLayer(ctypes.Structure):
     _fields_ = [("S_scratch", ctypes.c_void_p), ("S", ctypes.c_void_p),
                 ("conv_scratch", ctypes.c_void_p), ("conv_state", ctypes.c_void_p)]
+
+
+class GDNReplayLayer(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("g", ctypes.c_void_p), ("S", ctypes.c_void_p),
+                ("conv_state", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,6 +76,7 @@ def lib():
         "ddt_tree_accept": (I, [P, I, P, P, I, I, I, I, P, P, P, P, Z, P]),
         "ddt_commit": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, I, I,
                            ctypes.POINTER(GDNLayer), I, I, I, I, I, I, I, I, I, I, P]),
+        "ddt_gdn_replay": (I, [P, P, ctypes.POINTER(GDNReplayLayer), I, I, I, I, I, I, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -183,18 +190,22 @@ def tree_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, scale=0.0, w
     return out
 
 
-def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=None):
+def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=None, store_states=True):
     """x [n][T][C], conv_w [C][W] f32, conv_state [n][W-1][C], v [n][T][H][dv], beta, g [n][T][H] f32,
-    S [n][H][dv][dk] f32, parent [n][T] int32 -> dict o, S_scratch, conv_scratch."""
+    S [n][H][dv][dk] f32, parent [n][T] int32 -> dict o, S_scratch, conv_scratch.
+    store_states=False stores no node state (S_scratch = conv_scratch = None; see gdn_replay)."""
     _gpu(x, conv_w, conv_state, v, beta, g, S, parent)
     n, T, C = x.shape
     W = conv_w.shape[1]
     H, dv, dk = S.shape[1], S.shape[2], S.shape[3]
     dev = x.device
     if out is None:
-        out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev),
-               "S_scratch": torch.empty(n, T, H, dv, dk, dtype=torch.float32, device=dev),
-               "conv_scratch": torch.empty(n, T, W - 1, C, dtype=x.dtype, device=dev)}
+        out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev)}
+        if store_states:
+            out["S_scratch"] = torch.empty(n, T, H, dv, dk, dtype=torch.float32, device=dev)
+            out["conv_scratch"] = torch.empty(n, T, W - 1, C, dtype=x.dtype, device=dev)
+    if not store_states:
+        out["S_scratch"] = out["conv_scratch"] = None
     w = _ws(lib().ddt_gdn_tree_step_workspace(n, T - 1, H, dk), dev, ws)
     _check("ddt_gdn_tree_step", lib().ddt_gdn_tree_step(
         _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(out["conv_scratch"]), _ptr(v), _ptr(beta), _ptr(g),
@@ -251,3 +262,22 @@ def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None):
     _check("ddt_commit", lib().ddt_commit(
         _ptr(acc_rows), _ptr(acc_len), _ptr(prefix_len), kv, len(kv_layers), Hkv, D, Pmax, kv_dt,
         gd, len(gdn_layers), H, dk, dv, C, W, act_dt, n, B, Lp1 - 1, _stream(dev)))
+
+
+def gdn_replay(acc_rows, acc_len, layers, B):
+    """Advance committed GDN/conv state along the accepted path (after commit of the round).
+    layers: sequence of (x, conv_w, v, beta, g, S, conv_state) of each GDN layer."""
+    _gpu(acc_rows, acc_len)
+    n, Lp1 = acc_rows.shape
+    dev = acc_rows.device
+    tab = (GDNReplayLayer * max(1, len(layers)))()
+    H = dk = dv = 1
+    C, W, act_dt = 2, 2, DDT_BF16
+    for i, (x, cw, v, beta, g, S, cst) in enumerate(layers):
+        _gpu(x, cw, v, beta, g, S, cst)
+        tab[i] = GDNReplayLayer(x.data_ptr(), cw.data_ptr(), v.data_ptr(), beta.data_ptr(), g.data_ptr(),
+                                S.data_ptr(), cst.data_ptr())
+        H, dv, dk = S.shape[1], S.shape[2], S.shape[3]
+        C, W, act_dt = x.shape[2], cw.shape[1], _dt(x)
+    _check("ddt_gdn_replay", lib().ddt_gdn_replay(
+        _ptr(acc_rows), _ptr(acc_len), tab, len(layers), H, dk, dv, C, W, act_dt, n, B, Lp1 - 1, _stream(dev)))

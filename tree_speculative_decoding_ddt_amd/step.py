@@ -40,6 +40,7 @@ class HybridConfig:
     W: int = 4
     dtype: torch.dtype = torch.bfloat16
     pattern: list = field(default_factory=list)  # "gdn"/"attn" per layer; default [gdn, gdn, gdn, attn]*
+    replay: bool = False       # store no per-node GDN state; the commit replays the accepted path
 
     def layer_pattern(self):
         if self.pattern:
@@ -90,8 +91,9 @@ class HybridVerifyStep:
         self.gdn = [dict(x=e(n, T, c.C), v=e(n, T, c.H, c.dk), beta=e(n, T, c.H, dtype=torch.float32),
                          g=e(n, T, c.H, dtype=torch.float32), S=e(n, c.H, c.dk, c.dk, dtype=torch.float32),
                          conv_state=e(n, c.W - 1, c.C), conv_w=e(c.C, c.W, dtype=torch.float32),
-                         out={"o": e(n, T, c.H, c.dk), "S_scratch": e(n, T, c.H, c.dk, c.dk, dtype=torch.float32),
-                              "conv_scratch": e(n, T, c.W - 1, c.C)})
+                         out=({"o": e(n, T, c.H, c.dk), "S_scratch": None, "conv_scratch": None} if c.replay else
+                              {"o": e(n, T, c.H, c.dk), "S_scratch": e(n, T, c.H, c.dk, c.dk, dtype=torch.float32),
+                               "conv_scratch": e(n, T, c.W - 1, c.C)}))
                     for _ in range(c.n_gdn)]
         self.tree = {"tok": e(n, T, dtype=torch.int32), "parent": e(n, T, dtype=torch.int32),
                      "depth": e(n, T, dtype=torch.int32), "score": e(n, T, dtype=torch.float32),
@@ -122,17 +124,26 @@ class HybridVerifyStep:
                 g = self.gdn[ig]
                 ig += 1
                 ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"], g["beta"], g["g"], g["S"],
-                                  self.tree["parent"], self.cfg.L, ws=self.ws_gdn, out=g["out"])
+                                  self.tree["parent"], self.cfg.L, ws=self.ws_gdn, out=g["out"],
+                                  store_states=not self.cfg.replay)
 
     def accept(self):
         ddt.tree_accept(self.target_logits, self.tree["tok"], self.tree["parent"], self.cfg.L,
                         ws=self.ws_acc, out=self.acc)
 
     def commit(self):
-        ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len,
-                   [(a["k_tree"], a["v_tree"], a["k_cache"], a["v_cache"]) for a in self.attn],
-                   [(g["out"]["S_scratch"], g["S"], g["out"]["conv_scratch"], g["conv_state"]) for g in self.gdn],
-                   B=self.cfg.B)
+        kv = [(a["k_tree"], a["v_tree"], a["k_cache"], a["v_cache"]) for a in self.attn]
+        if self.cfg.replay:
+            # KV rows are copied; the recurrent state is advanced along the accepted path
+            # after the commit has marked the sequences that may not be written
+            ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv, (), B=self.cfg.B)
+            ddt.gdn_replay(self.acc["acc_rows"], self.acc["acc_len"],
+                           [(g["x"], g["conv_w"], g["v"], g["beta"], g["g"], g["S"], g["conv_state"])
+                            for g in self.gdn], B=self.cfg.B)
+        else:
+            ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv,
+                       [(g["out"]["S_scratch"], g["S"], g["out"]["conv_scratch"], g["conv_state"])
+                        for g in self.gdn], B=self.cfg.B)
         # the bonus token of this round is the root of the next one
         self.root_token.copy_(self.acc["bonus"])
 
