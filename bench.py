@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--n", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-variant", action="store_true", help="skip the replay-on-commit variant")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -151,7 +152,7 @@ def main():
     ddt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(a.steps + a.warmup + 2) * 16 + 64)
+    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(2 * a.steps + a.warmup + 3) * 16 + 64)
     step = HybridVerifyStep(cfg, dev)
     step.fill_random(seed=a.seed)
     print("bench: inputs ready (%.1f GB on device)" % (torch.cuda.memory_allocated(dev) / 1e9),
@@ -185,7 +186,8 @@ def main():
                 ig += 1
                 timed("gdn_tree_step", lambda: ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"],
                                                                  g["beta"], g["g"], g["S"], step.tree["parent"],
-                                                                 cfg.L, ws=step.ws_gdn, out=g["out"]))
+                                                                 cfg.L, ws=step.ws_gdn, out=g["out"],
+                                                                 store_states=not cfg.replay))
         timed("tree_accept", step.accept)
         timed("commit", step.commit)
 
@@ -232,6 +234,26 @@ def main():
             "kv_frac_of_hbm_peak": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "TFLOPps": ka.get("TFLOPps"), "mfma_frac": ka.get("mfma_frac")}
 
+    # Variant: the same step with no per-node GDN state stored; the commit replays the
+    # accepted path on the committed state.  Reported beside the stored-state step.
+    variant = None
+    if not a.no_variant:
+        for k in names:
+            ev[k].clear()
+        cfg.replay = True
+        run_step(False)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            run_step(True)
+        torch.cuda.synchronize(dev)
+        dtv = time.perf_counter() - t0
+        cfg.replay = False
+        variant = {"gdn_replay_on_commit": {
+            "steps_per_s": round(a.steps / dtv, 3), "ms_per_step": round(dtv / a.steps * 1e3, 3),
+            "kernels_ms_per_step": {k: round(sum(s.elapsed_time(e) for s, e in ev[k]) / a.steps, 4)
+                                    for k in names}}}
+
     cpu = None
     if not a.no_cpu:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -249,7 +271,7 @@ def main():
                    "global_batch": cfg.n, "seq_len": a.prefix, "parallelism": "single GPU"},
         "roofline": roof, "tree_attn": attn, "kernels": kernels,
         "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p0, p1],
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu, "variants": variant,
     }
     print(json.dumps(line), flush=True)
     return 0

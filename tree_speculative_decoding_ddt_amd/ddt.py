@@ -193,23 +193,24 @@ def tree_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, scale=0.0, w
 def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=None, store_states=True):
     """x [n][T][C], conv_w [C][W] f32, conv_state [n][W-1][C], v [n][T][H][dv], beta, g [n][T][H] f32,
     S [n][H][dv][dk] f32, parent [n][T] int32 -> dict o, S_scratch, conv_scratch.
-    store_states=False stores no node state (S_scratch = conv_scratch = None; see gdn_replay)."""
+    store_states=False stores no node state (scratch pointers NULL; the commit then uses gdn_replay)."""
     _gpu(x, conv_w, conv_state, v, beta, g, S, parent)
     n, T, C = x.shape
     W = conv_w.shape[1]
     H, dv, dk = S.shape[1], S.shape[2], S.shape[3]
     dev = x.device
     if out is None:
-        out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev)}
+        out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev), "S_scratch": None, "conv_scratch": None}
         if store_states:
             out["S_scratch"] = torch.empty(n, T, H, dv, dk, dtype=torch.float32, device=dev)
             out["conv_scratch"] = torch.empty(n, T, W - 1, C, dtype=x.dtype, device=dev)
-    if not store_states:
-        out["S_scratch"] = out["conv_scratch"] = None
+    # without state storage the scratch pointers are NULL (a caller's out keeps its buffers)
+    Ssc = out["S_scratch"] if store_states else None
+    csc = out["conv_scratch"] if store_states else None
     w = _ws(lib().ddt_gdn_tree_step_workspace(n, T - 1, H, dk), dev, ws)
     _check("ddt_gdn_tree_step", lib().ddt_gdn_tree_step(
-        _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(out["conv_scratch"]), _ptr(v), _ptr(beta), _ptr(g),
-        _ptr(S), _ptr(out["S_scratch"]), _ptr(out["o"]), _ptr(parent), n, T - 1, L, H, dk, dv, C, W,
+        _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(csc), _ptr(v), _ptr(beta), _ptr(g),
+        _ptr(S), _ptr(Ssc), _ptr(out["o"]), _ptr(parent), n, T - 1, L, H, dk, dv, C, W,
         _dt(x), _ptr(w), w.numel() * w.element_size(), _stream(dev)))
     return out
 
