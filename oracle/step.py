@@ -18,15 +18,21 @@ from . import accept as _accept
 from . import attention as _attention
 from . import commit as _commit
 from . import gdn as _gdn
+from . import rope as _rope
 from . import tree as _tree
 
 
 def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_logits,
-                prefix_len, Pmax, H, dk, scale=None):
+                prefix_len, Pmax, H, dk, scale=None, rope=None):
     """Batch of n sequences.
 
     attn_layers: list of dicts q [n][T][Hq][D], k_tree, v_tree [n][Hkv][T][D],
                  k_cache, v_cache [n][Hkv][Pmax][D]
+                 With rope = (rot_dim, theta): q is before rotation and the tree rows'
+                 keys and values come as k_new, v_new [n][T][Hkv][D]; they are rotated
+                 at positions prefix_len + depth (the tree just built) and the
+                 rotated k_tree / v_tree are what the attention reads and the commit
+                 copies (returned as "attn_tree").
     gdn_layers:  list of dicts x [n][T][C], v [n][T][H][dv], beta, g [n][T][H],
                  S [n][H][dv][dk], conv_state [n][W-1][C], conv_w [C][W]
     Returns a dict with the tree, per-layer outputs, the walk and the
@@ -34,6 +40,17 @@ def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_log
     """
     n, L, _ = np.shape(draft_logits)
     tree = _tree.build_tree_batch(draft_logits, B, root_token)
+    attn_tree = None
+    if rope is not None:
+        rot_dim, theta = rope
+        attn_tree, rotated = [], []
+        for lay in attn_layers:
+            parts = [_rope.rope_tree_inputs(lay["q"][s], lay["k_new"][s], lay["v_new"][s], prefix_len[s],
+                                            tree["depth"][s], rot_dim, theta) for s in range(n)]
+            q, kt, vt = (np.stack([p[i] for p in parts]) for i in range(3))
+            attn_tree.append({"q": q, "k_tree": kt, "v_tree": vt})
+            rotated.append(dict(lay, q=q, k_tree=kt, v_tree=vt))
+        attn_layers = rotated
     attn_out = [_attention.tree_attention_batch(lay["q"], lay["k_cache"], lay["v_cache"],
                                                 prefix_len, lay["k_tree"], lay["v_tree"],
                                                 tree["anc"], scale)
@@ -62,7 +79,7 @@ def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_log
             gdn_after[j]["conv_state"].append(lay["conv_state"])
     kv_after = [{k: np.stack(v) for k, v in d.items()} for d in kv_after]
     gdn_after = [{k: np.stack(v) for k, v in d.items()} for d in gdn_after]
-    return {"tree": tree, "attn_out": attn_out,
+    return {"tree": tree, "attn_out": attn_out, "attn_tree": attn_tree,
             "gdn_o": [g[0] for g in gdn_out], "S_scratch": [g[1] for g in gdn_out],
             "conv_scratch": [g[2] for g in gdn_out],
             "acc_rows": acc_rows, "acc_len_walk": acc_len, "bonus": bonus,

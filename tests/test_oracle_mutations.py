@@ -14,10 +14,12 @@ import oracle.accept
 import oracle.attention
 import oracle.commit
 import oracle.gdn
+import oracle.rope
 import oracle.tree
 from tests import test_oracle_accept_commit as t_ac
 from tests import test_oracle_attention as t_attn
 from tests import test_oracle_gdn as t_gdn
+from tests import test_oracle_rope as t_rope
 from tests import test_oracle_tree as t_tree
 
 
@@ -51,6 +53,10 @@ GDN_PINS = [lambda: t_gdn.test_tree_matches_chain_replay(0), t_gdn.test_hand_com
 ACC_PINS = [lambda: t_ac.test_walk_matches_brute_force(0), t_ac.test_argmax_ties_take_lowest_id,
             lambda: t_ac.test_commit_copies_replay_and_decode(0)]
 
+ROPE_PINS = [t_rope.test_two_channels_is_a_plane_rotation, t_rope.test_four_channels_pair_layout_and_frequencies,
+             lambda: t_rope.test_complex_form(64, 16), t_rope.test_positions_follow_branch_depth,
+             t_rope.test_chain_tree_equals_sequential_decoding]
+
 CASES = [
     (oracle.tree, "build_tree", "int(ids[0, 0]), 0, 1, 0", "int(ids[0, 0]), 0, 1, 1", TREE_PINS),
     (oracle.tree, "build_tree", "score[p] + vals[d - 1, r + 1]", "score[p] + vals[d - 1, r]", TREE_PINS),
@@ -76,6 +82,15 @@ CASES = [
     (oracle.commit, "commit", 'lay["k_cache"][:, P + j, :] = lay["k_tree"][:, r, :]',
      'lay["k_cache"][:, P + j + 1, :] = lay["k_tree"][:, r, :]', ACC_PINS),
     (oracle.commit, "commit", "last = rows[-1]", "last = rows[0]", ACC_PINS),
+    (oracle.rope, "rope", "hi * c + lo * s", "hi * c - lo * s", ROPE_PINS),
+    (oracle.rope, "rope", "lo * c - hi * s", "lo * c + hi * s", ROPE_PINS),
+    (oracle.rope, "rope", "lo, hi = x[..., :half], x[..., half:rot_dim]",
+     "lo, hi = x[..., 0:rot_dim:2], x[..., 1:rot_dim:2]", ROPE_PINS),
+    (oracle.rope, "angles", "-2.0 * j / rot_dim", "-1.0 * j / rot_dim", ROPE_PINS),
+    (oracle.rope, "tree_positions", "return prefix_len + depth", "return prefix_len + depth + 1", ROPE_PINS),
+    # the mistake the pages warn of: positions by flattened row order instead of depth
+    (oracle.rope, "tree_positions", "prefix_len[:, None] + depth", "prefix_len[:, None] + np.arange(depth.shape[1])",
+     ROPE_PINS),
 ]
 
 

@@ -57,3 +57,36 @@ def test_tiny_step_wiring(seed):
                 p = np.exp(sc - sc.max())
                 np.testing.assert_allclose((p / p.sum()) @ vv, r["attn_out"][0][s][row, h],
                                            rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_step_with_rope_commits_keys_rotated_at_their_cache_position(seed):
+    # pre-rotation tree inputs: after the commit, the key at cache position P + j is the
+    # accepted row's key rotated at P + j, and a decode of the accepted row at position
+    # P + j over the committed cache reproduces its tree attention
+    from oracle import rope as orope
+    d = tiny_inputs(seed)
+    rng = np.random.default_rng(100 + seed)
+    n, T, D = 2, d["B"] + 1, 64
+    lay = dict(d["at"])
+    lay["k_new"] = rng.standard_normal((n, T, 1, D))
+    lay["v_new"] = rng.standard_normal((n, T, 1, D))
+    rot, theta = 32, 1e4
+    r = ostep.verify_step(d["z"], np.zeros(n, np.int64), d["B"], [lay], [dict(d["gi"])], d["y"],
+                          d["P"], d["Pmax"], H=1, dk=32, rope=(rot, theta))
+    for s in range(n):
+        a = r["acc_len"][s]
+        rows = r["acc_rows"][s, : a + 1]
+        P = d["P"][s]
+        kc = r["kv_after"][0]["k_cache"][s]
+        vc = r["kv_after"][0]["v_cache"][s]
+        for j, row in enumerate(rows):
+            np.testing.assert_allclose(kc[0, P + j], orope.rope(lay["k_new"][s][row], [P + j], rot, theta)[0],
+                                       atol=1e-12)
+            np.testing.assert_array_equal(vc[0, P + j], lay["v_new"][s][row, 0])
+            qr = orope.rope(lay["q"][s][row], np.full(2, P + j), rot, theta)
+            kk, vv = kc[0, : P + j + 1], vc[0, : P + j + 1]
+            for h in range(2):
+                sc = kk @ qr[h] / 8.0
+                p = np.exp(sc - sc.max())
+                np.testing.assert_allclose((p / p.sum()) @ vv, r["attn_out"][0][s][row, h], rtol=1e-10, atol=1e-12)
