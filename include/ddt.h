@@ -5,6 +5,8 @@
  * a short-conv state):
  *   ddt_build_tree     draft tree of B nodes from the drafter's per-depth logits
  *   ddt_tree_attn      tree-masked attention of every node over prefix + ancestors
+ *   ddt_tree_attn_rope the same, from pre-rotation q and tree K/V: RoPE at positions
+ *                      prefix + depth, tree K/V written to their scratch
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
  *   ddt_commit         copy only the accepted path into the committed buffers
@@ -117,6 +119,30 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* prefix_len, const void* k_tree, const void* v_tree,
                   const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, int Pmax,
                   float scale, int dt, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- tree attention with RoPE by depth
+ * [notes] "What broke along the way", "Where the next step is": positions and RoPE of
+ * the tree rows follow the branch depth; the tree's K/V go to scratch, never into the
+ * committed cache.  Same attention as ddt_tree_attn, from pre-rotation inputs:
+ *   pos[s][t] = prefix_len[s] + depth[s][t]   (depth as written by ddt_build_tree)
+ *   RoPE, rotate-half layout: for j < rot_dim/2 the channel pair (j, j + rot_dim/2) turns
+ *   by pos * theta^(-2j/rot_dim):  x_j' = x_j cos - x_{j+r/2} sin,
+ *   x_{j+r/2}' = x_{j+r/2} cos + x_j sin; channels >= rot_dim are unchanged.
+ *   q      [n][T][Hq][D]   queries before rotation (read only)
+ *   k_new  [n][T][Hkv][D]  the tree rows' keys before rotation, token-major (read only)
+ *   v_new  [n][T][Hkv][D]  the tree rows' values, token-major (read only)
+ *   k_tree, v_tree [n][Hkv][T][D]  WRITTEN: rotated keys / copied values, the layout
+ *                  ddt_tree_attn reads and ddt_commit copies into the cache
+ *   other arguments as ddt_tree_attn (k_cache/v_cache hold already-rotated keys).
+ * Angles are formed in fp64 and applied in fp32; rotated values are rounded to dt.
+ * ws: ddt_tree_attn_rope_workspace() bytes (the rotated queries, then the attention's
+ * own workspace); required.  Built: rot_dim a multiple of 16 in [16, D]; theta > 1.
+ */
+size_t ddt_tree_attn_rope_workspace(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);
+int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth, int rot_dim,
+                       float theta, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                       void* k_tree, void* v_tree, const uint64_t* anc, int n, int B, int Hq, int Hkv, int D,
+                       int Pmax, float scale, int dt, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- GDN tree step
  * [notes] "Why hybrid attention makes it hard": every node reads the Gated DeltaNet

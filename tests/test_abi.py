@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -76,6 +76,24 @@ def test_tree_attn_validation():
     assert status("ddt_tree_attn", *args(D=96)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_tree_attn", *args(dt=3)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_tree_attn", *args(dt=1, D=256, Pmax=65536, wsb=8)) == ddt.DDT_ERR_WORKSPACE
+
+
+def test_tree_attn_rope_validation():
+    def args(**k):
+        #       q             k_new v_new depth            rot                   theta
+        return [k.get("q", P), P, P, k.get("depth", P), k.get("rot", 64), ctypes.c_float(k.get("theta", 1e4)),
+                P, P, P, P, P, P, 1, k.get("B", 8), 2, 1, k.get("D", 64), 128, ctypes.c_float(0.0), k.get("dt", 0),
+                P, P, k.get("wsb", 1 << 30), None]
+    assert status("ddt_tree_attn_rope", *args(depth=None)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn_rope", *args(rot=24)) == ddt.DDT_ERR_UNSUPPORTED     # not a multiple of 16
+    assert status("ddt_tree_attn_rope", *args(rot=128)) == ddt.DDT_ERR_UNSUPPORTED    # > D
+    assert status("ddt_tree_attn_rope", *args(rot=0)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_tree_attn_rope", *args(theta=1.0)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn_rope", *args(theta=float("inf"))) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn_rope", *args(D=96)) == ddt.DDT_ERR_UNSUPPORTED
+    need = ddt.tree_attn_rope_workspace(1, 8, 2, 1, 64, 128, __import__("torch").float32)
+    assert need >= 1 * 9 * 2 * 64 * 4 > 0                                              # room for the rotated queries
+    assert status("ddt_tree_attn_rope", *args(wsb=need - 1)) == ddt.DDT_ERR_WORKSPACE
 
 
 def test_gdn_validation():

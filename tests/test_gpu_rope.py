@@ -1,0 +1,100 @@
+"""GPU parity of ddt_tree_attn_rope (RoPE at positions prefix + depth, then the tree
+attention) against the oracle's rotation and dense masked softmax.
+
+Checked per call: the rotated tree keys written to k_tree (fp32 1e-5; bf16 atol 2e-2
+/ rtol 1e-2), the values copied to v_tree (bit-exact), and the attention output o
+(same tolerances), in full for small cases and on rows sampled from every depth at
+the full shapes, including positions past 131072 where the slowest pair's angle is
+far beyond fp32's exact range.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from oracle import rope as orope
+from oracle import tree as otree
+from tests.gpu_util import anc_tensor, assert_close, down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(seed, n, B, L, Hq, Hkv, D, Pmax, prefix, dtype, rot, theta, kind="random", rows=None):
+    rng = np.random.default_rng(seed)
+    if kind == "chain":
+        parents = np.stack([np.arange(-1, B)] * n)
+    else:
+        parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    depth = np.zeros_like(parents)
+    for s in range(n):
+        for i in range(1, B + 1):
+            depth[s, i] = depth[s, parents[s, i]] + 1
+    anc = np.stack([otree.ancestor_masks(p) for p in parents])
+    T = B + 1
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    x = dict(q=f(n, T, Hq, D), k_new=f(n, T, Hkv, D), v_new=f(n, T, Hkv, D), k_cache=f(n, Hkv, Pmax, D),
+             v_cache=f(n, Hkv, Pmax, D))
+    dv = {k: up(v, dtype) for k, v in x.items()}
+    ex = {k: v[1] for k, v in dv.items()}
+    pl = np.asarray(prefix, dtype=np.int64)
+    out = ddt.tree_attn_rope(dv["q"][0], dv["k_new"][0], dv["v_new"][0], up_int(depth), rot, theta,
+                             dv["k_cache"][0], dv["v_cache"][0], up_int(pl), anc_tensor(anc))
+    torch.cuda.synchronize()
+    o, kt, vt = down(out["o"]), down(out["k_tree"]), down(out["v_tree"])
+    for s in range(n):
+        qr, kr, vr = orope.rope_tree_inputs(ex["q"][s], ex["k_new"][s], ex["v_new"][s], pl[s], depth[s], rot, theta)
+        assert_close(kt[s], kr, dtype, "rotated k_tree seq %d" % s)
+        np.testing.assert_array_equal(vt[s], vr, err_msg="v_tree seq %d" % s)
+        sel = rows(parents[s]) if callable(rows) else rows
+        if sel is None:
+            ref = oattn.tree_attention(qr, ex["k_cache"][s], ex["v_cache"][s], pl[s], kr, vr, anc[s])
+            assert_close(o[s], ref, dtype, "o seq %d" % s)
+        else:
+            for i in sel:
+                ref = oattn.tree_attention_row(qr[i], ex["k_cache"][s], ex["v_cache"][s], pl[s], kr, vr, anc[s][i])
+                assert_close(o[s][i], ref, dtype, "o seq %d row %d" % (s, i))
+
+
+def rows_by_depth(parents):
+    """The first row of every depth, and the last row."""
+    depth = np.zeros(len(parents), np.int64)
+    for i in range(1, len(parents)):
+        depth[i] = depth[parents[i]] + 1
+    return sorted({int(np.argmax(depth == d)) for d in range(depth.max() + 1)} | {len(parents) - 1})
+
+
+@pytest.mark.parametrize("rot", [16, 64])
+def test_tiny_fp32(rot):
+    say("rope tiny fp32 rot", rot)
+    run_case(rot, 2, 8, 4, 2, 1, 64, 160, [128, 77], "f32", rot, 10000.0)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp32_head_sizes_full_rotation(D):
+    say("rope fp32 D", D)
+    run_case(D, 2, 20, 6, 4, 2, D, 300, [300, 5], "f32", D, 1e6)
+
+
+def test_bf16_partial_rotation_full_compare():
+    # the workload's heads (24 q / 4 kv, D 256) with a quarter of the channels rotated
+    say("rope bf16 D256 rot64 full compare")
+    run_case(3, 2, 64, 15, 24, 4, 256, 1200, [1000, 1136], "bf16", 64, 1e7)
+
+
+def test_bf16_d128_chain():
+    say("rope bf16 D128 chain")
+    run_case(4, 2, 31, 31, 8, 2, 128, 700, [600, 7], "bf16", 128, 1e6, kind="chain")
+
+
+def test_bf16_long_positions_sampled():
+    # positions past 131072 (prefix 131100 + depth): the rotated keys in full, o on sampled rows
+    say("rope bf16 positions > 131072")
+    run_case(5, 1, 64, 15, 24, 4, 256, 131100, [131100], "bf16", 256, 1e4, rows=rows_by_depth)
+
+
+def test_empty_prefix_root_only():
+    # B = 0 and an empty prefix: the root sees only itself, at position 0 (no rotation)
+    say("rope root only")
+    run_case(6, 2, 0, 0, 2, 1, 64, 16, [0, 0], "f32", 64, 1e4)

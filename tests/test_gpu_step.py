@@ -36,6 +36,9 @@ def load_inputs(step, seed, dtype):
     ex = {"z": ze, "y": ye, "attn": [], "gdn": []}
     for a in step.attn:
         x = synth.attention_inputs(rng, c.n, c.T, c.Hq, c.Hkv, c.D, c.Pmax)
+        if c.rope:  # the tree rows' own keys/values come token-major, before rotation
+            x["k_new"] = np.ascontiguousarray(x.pop("k_tree").transpose(0, 2, 1, 3))
+            x["v_new"] = np.ascontiguousarray(x.pop("v_tree").transpose(0, 2, 1, 3))
         lay = {}
         for k, v in x.items():
             tt, ee = up(v, dtype)
@@ -74,7 +77,13 @@ def check_round(step, ex, ref, dtype, rows_only=None):
     np.testing.assert_array_equal(down(step.acc["acc_len"]), ref["acc_len"])
     np.testing.assert_array_equal(down(step.prefix_len), ref["prefix_len"])
     for j, a in enumerate(step.attn):
-        np.testing.assert_array_equal(down(a["k_cache"]), ref["kv_after"][j]["k_cache"])
+        if ref["attn_tree"] is not None:
+            # rotated on the GPU in fp32 and rounded to the storage dtype; values are copies
+            assert_close(down(a["k_tree"]), ref["attn_tree"][j]["k_tree"], dtype, "rotated k_tree layer %d" % j)
+            np.testing.assert_array_equal(down(a["v_tree"]), ref["attn_tree"][j]["v_tree"])
+            assert_close(down(a["k_cache"]), ref["kv_after"][j]["k_cache"], dtype, "k_cache layer %d" % j)
+        else:
+            np.testing.assert_array_equal(down(a["k_cache"]), ref["kv_after"][j]["k_cache"])
         np.testing.assert_array_equal(down(a["v_cache"]), ref["kv_after"][j]["v_cache"])
     for j, g in enumerate(step.gdn):
         assert_close(down(g["S"]), ref["gdn_after"][j]["S"], "f32", "committed S layer %d" % j)
@@ -93,7 +102,7 @@ def run_rounds(cfg, dtype, seed, rounds=2, rows_only=None):
         step()
         torch.cuda.synchronize()
         ref = ostep.verify_step(ex["z"], root, cfg.B, attn_in, gdn_in,
-                                ex["y"], prefix, cfg.Pmax, cfg.H, cfg.dk)
+                                ex["y"], prefix, cfg.Pmax, cfg.H, cfg.dk, rope=cfg.rope)
         check_round(step, ex, ref, dtype, rows_only)
         # next round: committed buffers, grown prefix, bonus as root
         root = ref["bonus"]
@@ -135,6 +144,23 @@ def test_bf16_hybrid_step_reduced_replay():
     say("step bf16 hybrid reduced replay: n=2 V=151936 L=15 B=64 prefix 640, 1 attn + 3 gdn")
     cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=32, n_attn=1, n_gdn=3, replay=True)
     run_rounds(cfg, "bf16", seed=5, rounds=3)
+
+
+def test_tiny_step_rope_two_rounds():
+    # pre-rotation attention inputs: RoPE at prefix + depth inside the attention call,
+    # the rotated tree keys committed at their positions, then a second round over them
+    say("step tiny fp32 rope")
+    cfg = HybridConfig(n=2, V=512, L=4, B=8, prefix=128, extra_cap=16, n_attn=2, n_gdn=1, Hq=2, Hkv=1, D=64,
+                       H=1, dk=32, W=4, dtype=torch.float32, rope=(32, 10000.0))
+    run_rounds(cfg, "f32", seed=6)
+
+
+def test_bf16_hybrid_step_reduced_rope_replay():
+    # the workload's layer shapes with RoPE on a quarter of the channels and GDN replay on commit
+    say("step bf16 hybrid reduced rope + replay")
+    cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=32, n_attn=1, n_gdn=3, replay=True,
+                       rope=(64, 1e7))
+    run_rounds(cfg, "bf16", seed=7, rounds=2)
 
 
 def test_replay_matches_stored_commit_on_overflow():

@@ -1,6 +1,7 @@
 // C ABI of libddt.so (declared in include/ddt.h): argument validation, workspace
 // sizing and dispatch to the kernel launchers.  Validation happens entirely on the
 // host and before any HIP call, so a rejected call touches no device state.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -132,6 +133,46 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache, const
   return hip_status(ddt::launch_tree_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, n, B + 1, Hq, Hkv, D,
                                           Pmax, sc, dt, out, plan, ws, static_cast<hipStream_t>(stream)),
                     "ddt_tree_attn");
+}
+
+// ---------------------------------------------------------------- tree attention with RoPE by depth
+static size_t rope_q_bytes(int n, int B, int Hq, int D, int dt) {
+  return ((size_t)n * (B + 1) * Hq * D * esize(dt) + 255) / 256 * 256;
+}
+
+size_t ddt_tree_attn_rope_workspace(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) {
+  if (attn_args(n, B, Hq, Hkv, D, Pmax, dt) != DDT_OK) return 0;
+  return rope_q_bytes(n, B, Hq, D, dt) + ddt::plan_tree_attn(n, B, Hq, Hkv, D, Pmax, dt).total;
+}
+
+int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth, int rot_dim,
+                       float theta, const void* k_cache, const void* v_cache, const int32_t* prefix_len, void* k_tree,
+                       void* v_tree, const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, int Pmax, float scale,
+                       int dt, void* out, void* ws, size_t ws_bytes, void* stream) {
+  DDT_NEED(q); DDT_NEED(k_new); DDT_NEED(v_new); DDT_NEED(depth); DDT_NEED(k_cache); DDT_NEED(v_cache);
+  DDT_NEED(prefix_len); DDT_NEED(k_tree); DDT_NEED(v_tree); DDT_NEED(anc); DDT_NEED(out); DDT_NEED(ws);
+  const int st = attn_args(n, B, Hq, Hkv, D, Pmax, dt);
+  if (st != DDT_OK) return st;
+  DDT_CHECK(rot_dim >= 16 && rot_dim <= D && rot_dim % 16 == 0, DDT_ERR_UNSUPPORTED,
+            "ddt_tree_attn_rope: rot_dim=%d must be a multiple of 16 in [16, D=%d]", rot_dim, D);
+  DDT_CHECK(theta > 1.f && isfinite(theta), DDT_ERR_ARG, "ddt_tree_attn_rope: theta=%g must be finite and > 1",
+            (double)theta);
+  const size_t qb = rope_q_bytes(n, B, Hq, D, dt);
+  const ddt::AttnPlan plan = ddt::plan_tree_attn(n, B, Hq, Hkv, D, Pmax, dt);
+  DDT_CHECK(ws_bytes >= qb + plan.total, DDT_ERR_WORKSPACE, "ddt_tree_attn_rope: workspace %zu < %zu bytes", ws_bytes,
+            qb + plan.total);
+  DDT_CHECK(aligned16(ws) && aligned16(q) && aligned16(k_new) && aligned16(v_new) && aligned16(k_cache) &&
+                aligned16(v_cache) && aligned16(k_tree) && aligned16(v_tree) && aligned16(out),
+            DDT_ERR_ARG, "ddt_tree_attn_rope: tensors and workspace must be 16-byte aligned");
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t* q_rot = static_cast<uint8_t*>(ws);
+  hipError_t e = ddt::launch_tree_rope(q, k_new, v_new, depth, prefix_len, n, B + 1, Hq, Hkv, D, rot_dim, theta, dt,
+                                       q_rot, k_tree, v_tree, hs);
+  if (e != hipSuccess) return hip_status(e, "ddt_tree_attn_rope");
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)D);
+  return hip_status(ddt::launch_tree_attn(q_rot, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, n, B + 1, Hq, Hkv,
+                                          D, Pmax, sc, dt, out, plan, plan.total > 0 ? q_rot + qb : nullptr, hs),
+                    "ddt_tree_attn_rope");
 }
 
 // ---------------------------------------------------------------- GDN tree step

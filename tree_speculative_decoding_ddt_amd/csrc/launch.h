@@ -38,6 +38,11 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
                             float scale, int dt, void* out, const AttnPlan& plan, void* ws,
                             hipStream_t st);
 
+// ---- RoPE of the tree rows at prefix + depth (queries to q_out, keys/values to the tree scratch)
+hipError_t launch_tree_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth,
+                            const int32_t* prefix_len, int n, int T, int Hq, int Hkv, int D, int rot, float theta,
+                            int dt, void* q_out, void* k_tree, void* v_tree, hipStream_t st);
+
 // ---- GDN tree step
 size_t gdn_workspace(int n, int T, int H, int dk);
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,

@@ -20,6 +20,7 @@ DDT_F32, DDT_BF16 = 0, 1
 EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_build_tree_workspace", "ddt_build_tree",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
+           "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope",
            "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
            "ddt_commit", "ddt_gdn_replay")
@@ -70,6 +71,8 @@ def lib():
         "ddt_build_tree": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]),
         "ddt_tree_attn_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
+        "ddt_tree_attn_rope_workspace": (Z, [I, I, I, I, I, I, I]),
+        "ddt_tree_attn_rope": (I, [P, P, P, P, I, F, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_gdn_tree_step_workspace": (Z, [I, I, I, I]),
         "ddt_gdn_tree_step": (I, [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P]),
         "ddt_tree_accept_workspace": (Z, [I, I, I]),
@@ -139,6 +142,10 @@ def tree_attn_workspace(n, B, Hq, Hkv, D, Pmax, dtype):
     return lib().ddt_tree_attn_workspace(n, B, Hq, Hkv, D, Pmax, DDT_BF16 if dtype == torch.bfloat16 else DDT_F32)
 
 
+def tree_attn_rope_workspace(n, B, Hq, Hkv, D, Pmax, dtype):
+    return lib().ddt_tree_attn_rope_workspace(n, B, Hq, Hkv, D, Pmax, DDT_BF16 if dtype == torch.bfloat16 else DDT_F32)
+
+
 def gdn_tree_step_workspace(n, B, H, dk):
     return lib().ddt_gdn_tree_step_workspace(n, B, H, dk)
 
@@ -187,6 +194,26 @@ def tree_attn(q, k_cache, v_cache, prefix_len, k_tree, v_tree, anc, scale=0.0, w
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc),
         n, T - 1, Hq, Hkv, D, Pmax, float(scale), dt, _ptr(out), _ptr(w), w.numel() * w.element_size(),
         _stream(dev)))
+    return out
+
+
+def tree_attn_rope(q, k_new, v_new, depth, rot_dim, theta, k_cache, v_cache, prefix_len, anc, scale=0.0, ws=None,
+                   out=None):
+    """Pre-rotation q [n][T][Hq][D], k_new/v_new [n][T][Hkv][D], depth [n][T] int32 ->
+    dict o [n][T][Hq][D], k_tree/v_tree [n][Hkv][T][D] (rotated keys / values, written)."""
+    _gpu(q, k_new, v_new, depth, k_cache, v_cache, prefix_len, anc)
+    n, T, Hq, D = q.shape
+    Hkv, Pmax = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    if out is None:
+        out = {"o": torch.empty_like(q), "k_tree": torch.empty(n, Hkv, T, D, dtype=q.dtype, device=dev),
+               "v_tree": torch.empty(n, Hkv, T, D, dtype=q.dtype, device=dev)}
+    dt = _dt(q)
+    w = _ws(lib().ddt_tree_attn_rope_workspace(n, T - 1, Hq, Hkv, D, Pmax, dt), dev, ws)
+    _check("ddt_tree_attn_rope", lib().ddt_tree_attn_rope(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(depth), int(rot_dim), float(theta), _ptr(k_cache), _ptr(v_cache),
+        _ptr(prefix_len), _ptr(out["k_tree"]), _ptr(out["v_tree"]), _ptr(anc), n, T - 1, Hq, Hkv, D, Pmax,
+        float(scale), dt, _ptr(out["o"]), _ptr(w), w.numel() * w.element_size(), _stream(dev)))
     return out
 
 

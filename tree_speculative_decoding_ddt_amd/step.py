@@ -41,6 +41,7 @@ class HybridConfig:
     dtype: torch.dtype = torch.bfloat16
     pattern: list = field(default_factory=list)  # "gdn"/"attn" per layer; default [gdn, gdn, gdn, attn]*
     replay: bool = False       # store no per-node GDN state; the commit replays the accepted path
+    rope: tuple = None         # (rot_dim, theta): attention inputs are pre-rotation, RoPE at prefix + depth
 
     def layer_pattern(self):
         if self.pattern:
@@ -88,6 +89,12 @@ class HybridVerifyStep:
         self.attn = [dict(q=e(n, T, c.Hq, c.D), k_tree=e(n, c.Hkv, T, c.D), v_tree=e(n, c.Hkv, T, c.D),
                           k_cache=e(n, c.Hkv, c.Pmax, c.D), v_cache=e(n, c.Hkv, c.Pmax, c.D),
                           out=e(n, T, c.Hq, c.D)) for _ in range(c.n_attn)]
+        if c.rope:
+            # the tree rows' keys and values as a projection writes them (token-major, before
+            # rotation); k_tree / v_tree become outputs of the attention call
+            for a in self.attn:
+                a["k_new"] = e(n, T, c.Hkv, c.D)
+                a["v_new"] = e(n, T, c.Hkv, c.D)
         self.gdn = [dict(x=e(n, T, c.C), v=e(n, T, c.H, c.dk), beta=e(n, T, c.H, dtype=torch.float32),
                          g=e(n, T, c.H, dtype=torch.float32), S=e(n, c.H, c.dk, c.dk, dtype=torch.float32),
                          conv_state=e(n, c.W - 1, c.C), conv_w=e(c.C, c.W, dtype=torch.float32),
@@ -102,7 +109,8 @@ class HybridVerifyStep:
                     "bonus": e(n, dtype=torch.int32)}
         u8 = lambda nb: torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         self.ws_build = u8(ddt.build_tree_workspace(n, c.L, c.V, c.B, c.K))
-        self.ws_attn = u8(ddt.tree_attn_workspace(n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, dt))
+        self.ws_attn = u8((ddt.tree_attn_rope_workspace if c.rope else ddt.tree_attn_workspace)(
+            n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, dt))
         self.ws_acc = u8(ddt.tree_accept_workspace(n, c.B, c.V))
         self.ws_gdn = u8(ddt.gdn_tree_step_workspace(n, c.B, c.H, c.dk))
         self.pattern = c.layer_pattern()
@@ -118,8 +126,14 @@ class HybridVerifyStep:
             if kind == "attn":
                 a = self.attn[ia]
                 ia += 1
-                ddt.tree_attn(a["q"], a["k_cache"], a["v_cache"], self.prefix_len, a["k_tree"], a["v_tree"],
-                              self.tree["anc"], ws=self.ws_attn, out=a["out"])
+                if self.cfg.rope:
+                    ddt.tree_attn_rope(a["q"], a["k_new"], a["v_new"], self.tree["depth"], self.cfg.rope[0],
+                                       self.cfg.rope[1], a["k_cache"], a["v_cache"], self.prefix_len,
+                                       self.tree["anc"], ws=self.ws_attn,
+                                       out={"o": a["out"], "k_tree": a["k_tree"], "v_tree": a["v_tree"]})
+                else:
+                    ddt.tree_attn(a["q"], a["k_cache"], a["v_cache"], self.prefix_len, a["k_tree"], a["v_tree"],
+                                  self.tree["anc"], ws=self.ws_attn, out=a["out"])
             else:
                 g = self.gdn[ig]
                 ig += 1
@@ -172,7 +186,8 @@ class HybridVerifyStep:
         self.draft_logits.copy_(z)
         del z, zi
         for a in self.attn:
-            for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache"):
+            for k in ("q", "k_new", "v_new", "k_cache", "v_cache") if c.rope else \
+                    ("q", "k_tree", "v_tree", "k_cache", "v_cache"):
                 a[k].copy_(rn(*a[k].shape))
         for g in self.gdn:
             g["x"].copy_(rn(*g["x"].shape))
