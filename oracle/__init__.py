@@ -14,6 +14,7 @@ Modules
   tree       -- per-depth log-softmax + top-K, best-first tree build, flatten
   attention  -- tree-masked attention as a dense masked softmax
   rope       -- rotary embedding of the tree rows at positions prefix + depth
+  paged      -- the committed cache in pages: gather, paged attention, paged commit
   gdn        -- short causal conv + gated delta rule over the tree
   accept     -- target argmax + greedy tree walk
   commit     -- copy of the accepted path into the committed buffers
@@ -23,4 +24,4 @@ Every function takes and returns NumPy arrays; floating-point inputs are
 promoted to float64 before any arithmetic.
 """
 
-from . import tree, attention, rope, gdn, accept, commit, step, gaps  # noqa: F401
+from . import tree, attention, rope, gdn, accept, commit, paged, step, gaps  # noqa: F401

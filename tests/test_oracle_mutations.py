@@ -14,11 +14,13 @@ import oracle.accept
 import oracle.attention
 import oracle.commit
 import oracle.gdn
+import oracle.paged
 import oracle.rope
 import oracle.tree
 from tests import test_oracle_accept_commit as t_ac
 from tests import test_oracle_attention as t_attn
 from tests import test_oracle_gdn as t_gdn
+from tests import test_oracle_paged as t_paged
 from tests import test_oracle_rope as t_rope
 from tests import test_oracle_tree as t_tree
 
@@ -57,6 +59,10 @@ ROPE_PINS = [t_rope.test_two_channels_is_a_plane_rotation, t_rope.test_four_chan
              lambda: t_rope.test_complex_form(64, 16), t_rope.test_positions_follow_branch_depth,
              t_rope.test_chain_tree_equals_sequential_decoding]
 
+PAGED_PINS = [t_paged.test_hand_example_two_pages, lambda: t_paged.test_identity_and_permuted_tables_equal_contiguous_attention(16),
+              lambda: t_paged.test_paged_commit_equals_contiguous_commit(14, 5),
+              lambda: t_paged.test_paged_commit_equals_contiguous_commit(58, 5), t_paged.test_paged_commit_overflow_leaves_pages]
+
 CASES = [
     (oracle.tree, "build_tree", "int(ids[0, 0]), 0, 1, 0", "int(ids[0, 0]), 0, 1, 1", TREE_PINS),
     (oracle.tree, "build_tree", "score[p] + vals[d - 1, r + 1]", "score[p] + vals[d - 1, r]", TREE_PINS),
@@ -88,6 +94,10 @@ CASES = [
      "lo, hi = x[..., 0:rot_dim:2], x[..., 1:rot_dim:2]", ROPE_PINS),
     (oracle.rope, "angles", "-2.0 * j / rot_dim", "-1.0 * j / rot_dim", ROPE_PINS),
     (oracle.rope, "tree_positions", "return prefix_len + depth", "return prefix_len + depth + 1", ROPE_PINS),
+    (oracle.paged, "gather", "[pos // ps], :, pos % ps", "[pos // ps - 1], :, pos % ps", PAGED_PINS),
+    (oracle.paged, "gather", "[pos // ps], :, pos % ps", "[pos // ps], :, (pos + 1) % ps", PAGED_PINS),
+    (oracle.paged, "scatter", "p = start + j", "p = start + j + 1", PAGED_PINS),
+    (oracle.paged, "commit_paged", "P + a + 1 > cap", "P + a > cap", PAGED_PINS),
     # the mistake the pages warn of: positions by flattened row order instead of depth
     (oracle.rope, "tree_positions", "prefix_len[:, None] + depth", "prefix_len[:, None] + np.arange(depth.shape[1])",
      ROPE_PINS),
