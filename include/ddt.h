@@ -7,9 +7,11 @@
  *   ddt_tree_attn      tree-masked attention of every node over prefix + ancestors
  *   ddt_tree_attn_rope the same, from pre-rotation q and tree K/V: RoPE at positions
  *                      prefix + depth, tree K/V written to their scratch
+ *   ddt_tree_attn_paged the same over a paged committed cache (block table + page pool)
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
  *   ddt_commit         copy only the accepted path into the committed buffers
+ *   ddt_commit_paged   the same with the KV rows scattered into a paged cache
  *   ddt_gdn_replay     (alternative to storing node states) advance the committed GDN
  *                      and conv state along the accepted path
  *
@@ -120,6 +122,33 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache,
                   const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, int Pmax,
                   float scale, int dt, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- paged committed cache
+ * [notes] "Why hybrid attention makes it hard", "Where the next step is": the
+ * ancestor-mask branch attention is to run over the serving engine's paged KV blocks.
+ * Paged layout of a layer's committed keys (values alike):
+ *   k_pages [num_pages][Hkv][page_size][D] (dt): a page holds page_size consecutive
+ *           positions of every kv head of one sequence;
+ *   block_table [n][max_blocks] int32 (device): position p of sequence s is slot
+ *           p % page_size of page block_table[s][p / page_size];
+ *   capacity max_blocks * page_size plays the role of Pmax.
+ * ddt_tree_attn_paged computes exactly ddt_tree_attn over the cache this table
+ * describes (same q, k_tree, v_tree, anc, out, scale, workspace rules; workspace size
+ * from ddt_tree_attn_paged_workspace).  Table entries for positions < prefix_len[s]
+ * must lie in [0, num_pages): an entry outside is clamped into the range (the output
+ * is then wrong, but no access leaves the pool).
+ * ddt_commit_paged is ddt_commit with the accepted KV rows written to positions
+ * P..P+a through the table; a sequence whose destination pages are not all in
+ * [0, num_pages), or that would pass the capacity, is not committed (acc_len = -1).
+ * Built: page_size a power of two in [1, 65536]; max_blocks * page_size <= 2^30.
+ */
+size_t ddt_tree_attn_paged_workspace(int n, int B, int Hq, int Hkv, int D, int max_blocks, int page_size,
+                                     int dt);
+int ddt_tree_attn_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                        int max_blocks, int page_size, int num_pages, const int32_t* prefix_len,
+                        const void* k_tree, const void* v_tree, const uint64_t* anc, int n, int B, int Hq,
+                        int Hkv, int D, float scale, int dt, void* out, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* ---------------------------------------------------------------- tree attention with RoPE by depth
  * [notes] "What broke along the way", "Where the next step is": positions and RoPE of
  * the tree rows follow the branch depth; the tree's K/V go to scratch, never into the
@@ -223,6 +252,12 @@ int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
                const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_dt,
                const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
                int act_dt, int n, int B, int L, void* stream);
+/* ddt_commit_paged: see "paged committed cache" above; kv[i].k_cache / v_cache are the
+ * layer's page pools. */
+int ddt_commit_paged(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv,
+                     int n_kv, int Hkv, int D, const int32_t* block_table, int max_blocks, int page_size,
+                     int num_pages, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv,
+                     int C, int W, int act_dt, int n, int B, int L, void* stream);
 
 /* ---------------------------------------------------------------- GDN replay on commit
  * [notes] "Where the next step is": scratch-buffer GDN and conv replay; [spec] "The

@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -94,6 +94,28 @@ def test_tree_attn_rope_validation():
     need = ddt.tree_attn_rope_workspace(1, 8, 2, 1, 64, 128, __import__("torch").float32)
     assert need >= 1 * 9 * 2 * 64 * 4 > 0                                              # room for the rotated queries
     assert status("ddt_tree_attn_rope", *args(wsb=need - 1)) == ddt.DDT_ERR_WORKSPACE
+
+
+def test_paged_validation():
+    def args(**k):
+        #       q  kp vp  table                  maxb                 ps                    npages
+        return [P, P, P, k.get("bt", P), k.get("maxb", 8), k.get("ps", 16), k.get("npages", 100), P, P, P, P,
+                1, 8, 2, 1, k.get("D", 64), ctypes.c_float(0.0), 0, P, P, k.get("wsb", 1 << 30), None]
+    assert status("ddt_tree_attn_paged", *args(bt=None)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn_paged", *args(ps=24)) == ddt.DDT_ERR_UNSUPPORTED      # not a power of two
+    assert status("ddt_tree_attn_paged", *args(ps=0)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_tree_attn_paged", *args(npages=0)) == ddt.DDT_ERR_ARG
+    assert status("ddt_tree_attn_paged", *args(maxb=1 << 20, ps=4096)) == ddt.DDT_ERR_ARG   # capacity > 2^30
+    assert status("ddt_tree_attn_paged", *args(D=96)) == ddt.DDT_ERR_UNSUPPORTED
+    assert ddt.tree_attn_paged_workspace(8, 64, 24, 4, 256, 2048, 16, __import__("torch").bfloat16) == \
+        ddt.tree_attn_workspace(8, 64, 24, 4, 256, 32768, __import__("torch").bfloat16)
+    kv = (ddt.KVLayer * 1)(ddt.KVLayer(256, 256, 256, 256))
+    gd = (ddt.GDNLayer * 1)()
+    c = [P, P, P, kv, 1, 2, 64, None, 8, 16, 100, 1, gd, 0, 1, 32, 32, 64, 4, 1, 1, 8, 4, None]
+    assert status("ddt_commit_paged", *c) == ddt.DDT_ERR_ARG                             # null block table
+    c[7] = P
+    c[9] = 48
+    assert status("ddt_commit_paged", *c) == ddt.DDT_ERR_UNSUPPORTED                     # page size
 
 
 def test_gdn_validation():

@@ -1,0 +1,131 @@
+"""GPU parity of the paged committed cache: ddt_tree_attn_paged against the oracle's
+tree attention over the page gather, and ddt_commit_paged against the oracle's paged
+commit (pages compared bit-exact, prefix lengths and acc_len exact).
+
+Pages of each sequence are scattered over a shared pool by a seeded permutation with
+spare pages; table entries past each prefix hold -7 (never read).  fp32 within 1e-5,
+bf16 within atol 2e-2 / rtol 1e-2.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged as opaged
+from oracle import tree as otree
+from tests.gpu_util import anc_tensor, assert_close, down, say, up, up_int
+from tree_speculative_decoding_ddt_amd import ddt, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def make_pool(rng, n, maxb, Hkv, ps, D, spare=5):
+    npages = n * maxb + spare
+    perm = rng.permutation(npages)[: n * maxb].reshape(n, maxb)
+    f = lambda: rng.standard_normal((npages, Hkv, ps, D)).astype(np.float32)
+    return perm, f(), f()
+
+
+def run_case(seed, n, B, L, Hq, Hkv, D, ps, maxb, prefix, dtype, rows=None):
+    rng = np.random.default_rng(seed)
+    parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    anc = np.stack([otree.ancestor_masks(p) for p in parents])
+    T = B + 1
+    bt, kp, vp = make_pool(rng, n, maxb, Hkv, ps, D)
+    pl = np.asarray(prefix, dtype=np.int64)
+    bt_dev = bt.copy()
+    for s in range(n):
+        bt_dev[s, (pl[s] + ps - 1) // ps:] = -7  # past the prefix: never read
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    q, kt, vt = f(n, T, Hq, D), f(n, Hkv, T, D), f(n, Hkv, T, D)
+    (qd, qe), (kpd, kpe), (vpd, vpe), (ktd, kte), (vtd, vte) = (up(a, dtype) for a in (q, kp, vp, kt, vt))
+    out = ddt.tree_attn_paged(qd, kpd, vpd, up_int(bt_dev), up_int(pl), ktd, vtd, anc_tensor(anc))
+    torch.cuda.synchronize()
+    got = down(out)
+    for s in range(n):
+        sel = rows(parents[s]) if callable(rows) else rows
+        if sel is None:
+            ref = opaged.tree_attention_paged(qe[s], kpe, vpe, bt[s], pl[s], kte[s], vte[s], anc[s])
+            assert_close(got[s], ref, dtype, "paged o seq %d" % s)
+        else:
+            kc, vc = opaged.gather(kpe, bt[s], pl[s]), opaged.gather(vpe, bt[s], pl[s])
+            from oracle import attention as oattn
+            for i in sel:
+                ref = oattn.tree_attention_row(qe[s][i], kc, vc, pl[s], kte[s], vte[s], anc[s][i])
+                assert_close(got[s][i], ref, dtype, "paged o seq %d row %d" % (s, i))
+
+
+def rows_by_depth(parents):
+    depth = np.zeros(len(parents), np.int64)
+    for i in range(1, len(parents)):
+        depth[i] = depth[parents[i]] + 1
+    return sorted({int(np.argmax(depth == d)) for d in range(depth.max() + 1)} | {len(parents) - 1})
+
+
+@pytest.mark.parametrize("ps", [1, 16])
+def test_fp32_scalar_path(ps):
+    say("paged fp32 page size", ps)
+    run_case(ps, 2, 8, 4, 2, 1, 64, ps, 160 // ps, [128, 77], "f32")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64])
+def test_bf16_d256_page_sizes(ps):
+    # the workload's heads; prefixes with ragged last pages
+    say("paged bf16 D256 page size", ps)
+    run_case(10 + ps, 2, 64, 15, 24, 4, 256, ps, 2048 // ps, [1000, 1777], "bf16")
+
+
+def test_bf16_d128_small_pages():
+    say("paged bf16 D128 page size 16")
+    run_case(3, 2, 40, 10, 16, 2, 128, 16, 64, [1023, 5], "bf16")
+
+
+def test_bf16_full_size_sampled():
+    # 8 sequences at prefix 8192 in pages of 16 (the split-K grid of the full workload)
+    say("paged bf16 n8 prefix 8192 sampled rows")
+    run_case(4, 8, 64, 15, 24, 4, 256, 16, 520, [8192] * 8, "bf16", rows=rows_by_depth)
+
+
+def test_empty_prefix():
+    say("paged empty prefix")
+    run_case(5, 2, 8, 4, 24, 4, 256, 16, 4, [0, 0], "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_commit_paged(dtype):
+    # sequences committing inside a page, across a page boundary, at the capacity edge,
+    # past the capacity (not committed), with an invalid destination page (not
+    # committed), and with acc_len = -1 from the walk
+    say("paged commit", dtype)
+    rng = np.random.default_rng(7)
+    n, Hkv, D, ps, maxb, B, L = 6, 2, 64, 16, 4, 8, 6
+    T = B + 1
+    bt, kp, vp = make_pool(rng, n, maxb, Hkv, ps, D)
+    prefix = np.array([3, 14, 59, 62, 20, 9])
+    acc_len = np.array([2, 5, 4, 4, 3, -1])
+    bt[4, 1] = 10 ** 6  # sequence 4 would write positions 20..23 into page entry 1
+    acc_rows = np.full((n, L + 1), -1, np.int64)
+    for s in range(n):
+        a = max(acc_len[s], 0)
+        acc_rows[s, : a + 1] = [0] + sorted(rng.choice(np.arange(1, T), a, replace=False).tolist())
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    kt, vt = f(n, Hkv, T, D), f(n, Hkv, T, D)
+    (kpd, kpe), (vpd, vpe), (ktd, kte), (vtd, vte) = (up(a, dtype) for a in (kp, vp, kt, vt))
+    pl_d, al_d = up_int(prefix), up_int(acc_len)
+    ddt.commit(up_int(acc_rows), al_d, pl_d, [(ktd, vtd, kpd, vpd)], (), B=B, block_table=up_int(bt))
+    torch.cuda.synchronize()
+    kp_ref, vp_ref = kpe, vpe
+    want_p, want_a = [], []
+    npages = kp.shape[0]
+    for s in range(n):
+        ok_pages = all(0 <= bt[s, b] < npages for b in range(prefix[s] // ps, min(maxb, (prefix[s] + max(acc_len[s], 0)) // ps + 1)))
+        if not ok_pages:   # the kernel refuses a sequence whose destination pages are invalid
+            want_p.append(prefix[s]); want_a.append(-1)
+            continue
+        p1, a1, kp_ref, vp_ref = opaged.commit_paged(acc_rows[s], acc_len[s], prefix[s], kte[s], vte[s], kp_ref,
+                                                     vp_ref, bt[s])
+        want_p.append(p1); want_a.append(a1)
+    np.testing.assert_array_equal(down(pl_d), want_p)
+    np.testing.assert_array_equal(down(al_d), want_a)
+    np.testing.assert_array_equal(down(kpd), kp_ref)
+    np.testing.assert_array_equal(down(vpd), vp_ref)

@@ -42,6 +42,8 @@ def load_inputs(step, seed, dtype):
         lay = {}
         for k, v in x.items():
             tt, ee = up(v, dtype)
+            if step.block_table is not None and k in ("k_cache", "v_cache"):
+                tt = to_pages(tt, step)  # the same cache, held in the step's pages
             a[k].copy_(tt)
             lay[k] = ee
         ex["attn"].append(lay)
@@ -55,6 +57,26 @@ def load_inputs(step, seed, dtype):
             lay[k] = ee
         ex["gdn"].append(lay)
     return ex
+
+
+def to_pages(cache, step):
+    """Contiguous [n][Hkv][Pmax][D] device tensor -> the step's page pool layout."""
+    ps = step.cfg.page_size
+    bt = step.block_table.cpu().numpy()
+    pool = torch.zeros(step.num_pages, cache.shape[1], ps, cache.shape[3], dtype=cache.dtype, device=cache.device)
+    for s in range(cache.shape[0]):
+        for b in range(bt.shape[1]):
+            pool[int(bt[s, b])] = cache[s, :, b * ps:(b + 1) * ps]
+    return pool
+
+
+def committed(step, t):
+    """A committed cache as contiguous [n][Hkv][Pmax][D] float64 (read through the pages if paged)."""
+    if step.block_table is None:
+        return down(t)
+    from oracle import paged as opaged
+    pool, bt = down(t), step.block_table.cpu().numpy()
+    return np.stack([opaged.gather(pool, bt[s], step.cfg.Pmax) for s in range(bt.shape[0])])
 
 
 def check_round(step, ex, ref, dtype, rows_only=None):
@@ -81,10 +103,10 @@ def check_round(step, ex, ref, dtype, rows_only=None):
             # rotated on the GPU in fp32 and rounded to the storage dtype; values are copies
             assert_close(down(a["k_tree"]), ref["attn_tree"][j]["k_tree"], dtype, "rotated k_tree layer %d" % j)
             np.testing.assert_array_equal(down(a["v_tree"]), ref["attn_tree"][j]["v_tree"])
-            assert_close(down(a["k_cache"]), ref["kv_after"][j]["k_cache"], dtype, "k_cache layer %d" % j)
+            assert_close(committed(step, a["k_cache"]), ref["kv_after"][j]["k_cache"], dtype, "k_cache layer %d" % j)
         else:
-            np.testing.assert_array_equal(down(a["k_cache"]), ref["kv_after"][j]["k_cache"])
-        np.testing.assert_array_equal(down(a["v_cache"]), ref["kv_after"][j]["v_cache"])
+            np.testing.assert_array_equal(committed(step, a["k_cache"]), ref["kv_after"][j]["k_cache"])
+        np.testing.assert_array_equal(committed(step, a["v_cache"]), ref["kv_after"][j]["v_cache"])
     for j, g in enumerate(step.gdn):
         assert_close(down(g["S"]), ref["gdn_after"][j]["S"], "f32", "committed S layer %d" % j)
         np.testing.assert_array_equal(down(g["conv_state"]), ref["gdn_after"][j]["conv_state"])
@@ -161,6 +183,21 @@ def test_bf16_hybrid_step_reduced_rope_replay():
     cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=32, n_attn=1, n_gdn=3, replay=True,
                        rope=(64, 1e7))
     run_rounds(cfg, "bf16", seed=7, rounds=2)
+
+
+def test_tiny_step_paged_two_rounds():
+    # the committed KV in pages of 16 scattered over a pool; the commit writes through the table
+    say("step tiny fp32 paged")
+    cfg = HybridConfig(n=2, V=512, L=4, B=8, prefix=128, extra_cap=32, n_attn=2, n_gdn=1, Hq=2, Hkv=1, D=64,
+                       H=1, dk=32, W=4, dtype=torch.float32, page_size=16)
+    run_rounds(cfg, "f32", seed=8)
+
+
+def test_bf16_hybrid_step_reduced_paged_replay():
+    say("step bf16 hybrid reduced paged + replay")
+    cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=64, n_attn=1, n_gdn=3, replay=True,
+                       page_size=32)
+    run_rounds(cfg, "bf16", seed=9, rounds=2)
 
 
 def test_replay_matches_stored_commit_on_overflow():

@@ -135,6 +135,54 @@ int ddt_tree_attn(const void* q, const void* k_cache, const void* v_cache, const
                     "ddt_tree_attn");
 }
 
+// ---------------------------------------------------------------- paged committed cache
+static int paged_args(const char* fn, const int32_t* bt, int max_blocks, int page_size, int num_pages,
+                      ddt::PagedKV& pg) {
+  DDT_CHECK(bt != nullptr, DDT_ERR_ARG, "%s: block_table is NULL", fn);
+  DDT_CHECK(page_size >= 1 && page_size <= 65536 && (page_size & (page_size - 1)) == 0, DDT_ERR_UNSUPPORTED,
+            "%s: page_size=%d must be a power of two in [1, 65536]", fn, page_size);
+  DDT_CHECK(max_blocks >= 1 && num_pages >= 1 && (long long)max_blocks * page_size <= (1ll << 30), DDT_ERR_ARG,
+            "%s: need max_blocks, num_pages >= 1 and max_blocks*page_size <= 2^30 (got %d, %d, %d)", fn, max_blocks,
+            num_pages, page_size);
+  int lps = 0;
+  while ((1 << lps) < page_size) ++lps;
+  pg = ddt::PagedKV{bt, max_blocks, lps, num_pages};
+  return DDT_OK;
+}
+
+size_t ddt_tree_attn_paged_workspace(int n, int B, int Hq, int Hkv, int D, int max_blocks, int page_size, int dt) {
+  if (max_blocks < 1 || page_size < 1 || (long long)max_blocks * page_size > (1ll << 30)) return 0;
+  return ddt_tree_attn_workspace(n, B, Hq, Hkv, D, max_blocks * page_size, dt);
+}
+
+int ddt_tree_attn_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                        int max_blocks, int page_size, int num_pages, const int32_t* prefix_len, const void* k_tree,
+                        const void* v_tree, const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, float scale,
+                        int dt, void* out, void* ws, size_t ws_bytes, void* stream) {
+  DDT_NEED(q); DDT_NEED(k_pages); DDT_NEED(v_pages); DDT_NEED(prefix_len);
+  DDT_NEED(k_tree); DDT_NEED(v_tree); DDT_NEED(anc); DDT_NEED(out);
+  ddt::PagedKV pg;
+  int st = paged_args("ddt_tree_attn_paged", block_table, max_blocks, page_size, num_pages, pg);
+  if (st != DDT_OK) return st;
+  const int Pmax = max_blocks * page_size;
+  st = attn_args(n, B, Hq, Hkv, D, Pmax, dt);
+  if (st != DDT_OK) return st;
+  const ddt::AttnPlan plan = ddt::plan_tree_attn(n, B, Hq, Hkv, D, Pmax, dt);
+  if (plan.total > 0) {
+    DDT_NEED(ws);
+    DDT_CHECK(ws_bytes >= plan.total, DDT_ERR_WORKSPACE, "ddt_tree_attn_paged: workspace %zu < %zu bytes", ws_bytes,
+              plan.total);
+    DDT_CHECK(aligned16(ws), DDT_ERR_ARG, "ddt_tree_attn_paged: workspace not 16-byte aligned");
+  }
+  DDT_CHECK(aligned16(q) && aligned16(k_pages) && aligned16(v_pages) && aligned16(k_tree) && aligned16(v_tree) &&
+                aligned16(out),
+            DDT_ERR_ARG, "ddt_tree_attn_paged: tensors must be 16-byte aligned");
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)D);
+  return hip_status(ddt::launch_tree_attn(q, k_pages, v_pages, prefix_len, k_tree, v_tree, anc, n, B + 1, Hq, Hkv, D,
+                                          Pmax, sc, dt, out, plan, ws, static_cast<hipStream_t>(stream), pg),
+                    "ddt_tree_attn_paged");
+}
+
 // ---------------------------------------------------------------- tree attention with RoPE by depth
 static size_t rope_q_bytes(int n, int B, int Hq, int D, int dt) {
   return ((size_t)n * (B + 1) * Hq * D * esize(dt) + 255) / 256 * 256;
@@ -263,9 +311,10 @@ int ddt_tree_accept(const void* target_logits, int dt, const int32_t* tok, const
 }
 
 // ---------------------------------------------------------------- commit
-int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv, int n_kv,
-               int Hkv, int D, int Pmax, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C,
-               int W, int act_dt, int n, int B, int L, void* stream) {
+static int commit_impl(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv,
+                       int n_kv, int Hkv, int D, int Pmax, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H,
+                       int dk, int dv, int C, int W, int act_dt, int n, int B, int L, void* stream,
+                       const ddt::PagedKV& pg) {
   DDT_NEED(acc_rows); DDT_NEED(acc_len); DDT_NEED(prefix_len);
   DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && L >= 0 && L <= 63 && n_kv >= 0 && n_gdn >= 0, DDT_ERR_ARG,
             "ddt_commit: need n>=1, 0<=B<=64, 0<=L<=63, n_kv,n_gdn>=0");
@@ -299,8 +348,26 @@ int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, c
   }
   return hip_status(ddt::launch_commit(acc_rows, acc_len, prefix_len, kv, n_kv, Hkv, D, Pmax, esize(kv_dt), gdn,
                                        n_gdn, H, dk, dv, C, W, esize(act_dt), n, B + 1, L,
-                                       static_cast<hipStream_t>(stream)),
+                                       static_cast<hipStream_t>(stream), pg),
                     "ddt_commit");
+}
+
+int ddt_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv, int n_kv,
+               int Hkv, int D, int Pmax, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C,
+               int W, int act_dt, int n, int B, int L, void* stream) {
+  return commit_impl(acc_rows, acc_len, prefix_len, kv, n_kv, Hkv, D, Pmax, kv_dt, gdn, n_gdn, H, dk, dv, C, W,
+                     act_dt, n, B, L, stream, ddt::PagedKV{nullptr, 0, 0, 0});
+}
+
+int ddt_commit_paged(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv,
+                     int n_kv, int Hkv, int D, const int32_t* block_table, int max_blocks, int page_size,
+                     int num_pages, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
+                     int act_dt, int n, int B, int L, void* stream) {
+  ddt::PagedKV pg;
+  const int st = paged_args("ddt_commit_paged", block_table, max_blocks, page_size, num_pages, pg);
+  if (st != DDT_OK) return st;
+  return commit_impl(acc_rows, acc_len, prefix_len, kv, n_kv, Hkv, D, max_blocks * page_size, kv_dt, gdn, n_gdn, H,
+                     dk, dv, C, W, act_dt, n, B, L, stream, pg);
 }
 
 }  // extern "C"

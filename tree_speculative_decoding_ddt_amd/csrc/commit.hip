@@ -30,21 +30,31 @@ struct GDNTable {
   uint8_t* conv_state[kLayersPerLaunch];
 };
 
+// Pmax is the capacity (max_blocks * page_size for a paged cache).  A paged cache also
+// needs a valid page for every destination position P .. P+a.
 __device__ __forceinline__ bool commit_ok(const int32_t* acc_len, const int32_t* prefix_len,
-                                          int s, int Pmax, int Lp1, int& a, int& P) {
+                                          int s, int Pmax, int Lp1, int& a, int& P,
+                                          const PagedKV& pg = PagedKV{nullptr, 0, 0, 0}) {
   a = acc_len[s];
   P = prefix_len[s];
-  return a >= 0 && a < Lp1 && P >= 0 && P + a + 1 <= Pmax;
+  if (!(a >= 0 && a < Lp1 && P >= 0 && P + a + 1 <= Pmax)) return false;
+  if (pg.bt != nullptr)
+    for (int b = P >> pg.lps; b <= (P + a) >> pg.lps; ++b) {
+      const int id = pg.bt[(size_t)s * pg.maxb + b];
+      if (id < 0 || id >= pg.npages) return false;
+    }
+  return true;
 }
 
 // grid (n, layers in this launch); row_vecs = D*esize/16 words per (head, row).
+// Contiguous cache [n][Hkv][Pmax][D], or (pg.bt set) the page pool [pages][Hkv][ps][D].
 __global__ void __launch_bounds__(256) commit_kv_kernel(KVTable tab, const int32_t* __restrict__ acc_rows,
                                                         const int32_t* __restrict__ acc_len,
                                                         const int32_t* __restrict__ prefix_len, int Hkv,
-                                                        int T, int Pmax, int row_vecs, int Lp1) {
+                                                        int T, int Pmax, int row_vecs, int Lp1, PagedKV pg) {
   const int s = blockIdx.x, layer = blockIdx.y;
   int a, P;
-  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P)) return;
+  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) return;
   const uint4* kt = reinterpret_cast<const uint4*>(tab.k_tree[layer]);
   const uint4* vt = reinterpret_cast<const uint4*>(tab.v_tree[layer]);
   uint4* kc = reinterpret_cast<uint4*>(tab.k_cache[layer]);
@@ -58,7 +68,7 @@ __global__ void __launch_bounds__(256) commit_kv_kernel(KVTable tab, const int32
     const int r = acc_rows[s * Lp1 + j];
     if (r < 0 || r >= T) continue;
     const size_t src = ((size_t)(s * Hkv + h) * T + r) * row_vecs + w;
-    const size_t dst = ((size_t)(s * Hkv + h) * Pmax + P + j) * row_vecs + w;
+    const size_t dst = (pg.bt != nullptr ? pg.row(s, h, Hkv, P + j) : (size_t)(s * Hkv + h) * Pmax + P + j) * row_vecs + w;
     kc[dst] = kt[src];
     vc[dst] = vt[src];
   }
@@ -69,10 +79,10 @@ __global__ void __launch_bounds__(256) commit_gdn_kernel(GDNTable tab, const int
                                                          const int32_t* __restrict__ acc_len,
                                                          const int32_t* __restrict__ prefix_len, int T,
                                                          int Pmax, long state_vecs, long conv_vecs,
-                                                         int Lp1) {
+                                                         int Lp1, PagedKV pg) {
   const int s = blockIdx.x, layer = blockIdx.y;
   int a, P;
-  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P)) return;
+  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) return;
   const int r = acc_rows[s * Lp1 + a];
   if (r < 0 || r >= T) return;
   const uint4* Ss = reinterpret_cast<const uint4*>(tab.S_scratch[layer]) + ((size_t)s * T + r) * state_vecs;
@@ -89,18 +99,19 @@ __global__ void __launch_bounds__(256) commit_gdn_kernel(GDNTable tab, const int
   }
 }
 
-__global__ void commit_finalize_kernel(int32_t* acc_len, int32_t* prefix_len, int n, int Pmax, int Lp1) {
+__global__ void commit_finalize_kernel(int32_t* acc_len, int32_t* prefix_len, int n, int Pmax, int Lp1,
+                                       PagedKV pg) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n) return;
   int a, P;
-  if (commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P)) prefix_len[s] = P + a + 1;
+  if (commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) prefix_len[s] = P + a + 1;
   else acc_len[s] = -1;
 }
 
 hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
                          const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_esize,
                          const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
-                         int act_esize, int n, int T, int L, hipStream_t st) {
+                         int act_esize, int n, int T, int L, hipStream_t st, const PagedKV& pg) {
   const int Lp1 = L + 1;
   for (int l0 = 0; l0 < n_kv; l0 += kLayersPerLaunch) {
     const int cnt = n_kv - l0 < kLayersPerLaunch ? n_kv - l0 : kLayersPerLaunch;
@@ -112,7 +123,7 @@ hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* pre
       tab.v_cache[j] = static_cast<uint8_t*>(kv[l0 + j].v_cache);
     }
     hipLaunchKernelGGL(commit_kv_kernel, dim3(n, cnt), dim3(256), 0, st, tab, acc_rows, acc_len,
-                       prefix_len, Hkv, T, Pmax, D * kv_esize / 16, Lp1);
+                       prefix_len, Hkv, T, Pmax, D * kv_esize / 16, Lp1, pg);
   }
   const long state_vecs = (long)H * dv * dk * 4 / 16;
   const long conv_vecs = (long)(W - 1) * C * act_esize / 16;
@@ -127,9 +138,9 @@ hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* pre
       tab.conv_state[j] = static_cast<uint8_t*>(gdn[l0 + j].conv_state);
     }
     hipLaunchKernelGGL(commit_gdn_kernel, dim3(n, cnt, chunks), dim3(256), 0, st, tab, acc_rows,
-                       acc_len, prefix_len, T, Pmax, state_vecs, conv_vecs, Lp1);
+                       acc_len, prefix_len, T, Pmax, state_vecs, conv_vecs, Lp1, pg);
   }
-  hipLaunchKernelGGL(commit_finalize_kernel, dim3(cdiv(n, 64)), dim3(64), 0, st, acc_len, prefix_len, n, Pmax, Lp1);
+  hipLaunchKernelGGL(commit_finalize_kernel, dim3(cdiv(n, 64)), dim3(64), 0, st, acc_len, prefix_len, n, Pmax, Lp1, pg);
   return hipGetLastError();
 }
 

@@ -32,11 +32,39 @@ struct AttnPlan {
   size_t off_lse, off_o, total;
 };
 AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);
+
+// Paged committed cache: pool [num_pages][Hkv][2^lps][D]; position p of sequence s is
+// slot p & (2^lps - 1) of page bt[s][p >> lps].  bt == nullptr: the contiguous cache.
+// A page id outside [0, npages) is clamped into it (wrong data, never an access outside
+// the pool); the commit refuses such a sequence instead.
+struct PagedKV {
+  const int32_t* bt;
+  int maxb, lps, npages;
+  __device__ __forceinline__ int page(int s, int p) const {
+    const int pgid = bt[(size_t)s * maxb + (p >> lps)];
+    return pgid < 0 ? 0 : (pgid >= npages ? npages - 1 : pgid);
+  }
+  // row index (in units of D elements) of position p of (s, kv head h) in the pool
+  __device__ __forceinline__ size_t row(int s, int h, int Hkv, int p) const {
+    return (((size_t)page(s, p) * Hkv + h) << lps) + (p & ((1 << lps) - 1));
+  }
+  // the same for a wave-uniform position: the table entry comes in through a scalar
+  // load (lgkmcnt), so it does not join the vector-memory count of copies in flight
+  __device__ __forceinline__ size_t row_uniform(int s, int h, int Hkv, int p) const {
+    const int pu = __builtin_amdgcn_readfirstlane(p);
+    const int32_t* e = bt + (size_t)s * maxb + (pu >> lps);
+    int pgid;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(pgid) : "s"(e));
+    pgid = pgid < 0 ? 0 : (pgid >= npages ? npages - 1 : pgid);
+    return (((size_t)pgid * Hkv + h) << lps) + (pu & ((1 << lps) - 1));
+  }
+};
+
 hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* prefix_len, const void* k_tree, const void* v_tree,
                             const uint64_t* anc, int n, int T, int Hq, int Hkv, int D, int Pmax,
                             float scale, int dt, void* out, const AttnPlan& plan, void* ws,
-                            hipStream_t st);
+                            hipStream_t st, const PagedKV& pg = PagedKV{nullptr, 0, 0, 0});
 
 // ---- RoPE of the tree rows at prefix + depth (queries to q_out, keys/values to the tree scratch)
 hipError_t launch_tree_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth,
@@ -72,6 +100,7 @@ hipError_t launch_tree_accept(const void* logits, int dt, const int32_t* tok,
 hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,
                          const ddt_kv_layer* kv, int n_kv, int Hkv, int D, int Pmax, int kv_esize,
                          const ddt_gdn_layer* gdn, int n_gdn, int H, int dk, int dv, int C, int W,
-                         int act_esize, int n, int T, int L, hipStream_t st);
+                         int act_esize, int n, int T, int L, hipStream_t st,
+                         const PagedKV& pg = PagedKV{nullptr, 0, 0, 0});
 
 }  // namespace ddt

@@ -47,13 +47,13 @@ constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, 
 constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
 
 // ------------------------------------------------------------------ scalar path
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q, const T* __restrict__ k_cache,
                                                          const T* __restrict__ v_cache,
                                                          const int32_t* __restrict__ prefix_len,
                                                          const T* __restrict__ k_tree, const T* __restrict__ v_tree,
                                                          const uint64_t* __restrict__ anc, int Tn, int Hq, int Hkv,
-                                                         int Pmax, float scale, T* __restrict__ out) {
+                                                         int Pmax, float scale, PagedKV pg, T* __restrict__ out) {
   constexpr int DPL = D / 64;
   const int bid = blockIdx.x;
   const int h = bid % Hq;
@@ -68,7 +68,12 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
 #pragma unroll
   for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
 
-  auto block = [&](float sc, const T* vbase, int vrow0) {
+  // element offset of prefix row `key` of this (sequence, kv head) in the cache or page pool
+  auto prow = [&](int key) -> size_t {
+    if constexpr (PAGED) return pg.row(s, kvh, Hkv, key) * D;
+    else return ((size_t)(s * Hkv + kvh) * Pmax + key) * D;
+  };
+  auto block = [&](float sc, const T* vbase, int vrow0, bool pre) {
     const float mb = wave_max(sc);
     const float mn = fmaxf(m, mb);
     if (mn == -INFINITY) return;
@@ -80,7 +85,7 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
     for (int u = 0; u < 64; ++u) {
       const float pu = __shfl(p, u, 64);
       if (pu != 0.f) {
-        const size_t rb = (size_t)(vrow0 + u) * D;
+        const size_t rb = pre ? prow(vrow0 + u) : (size_t)(vrow0 + u) * D;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) acc[j] += pu * Elem<T>::load(vbase, rb + lane + 64 * j);
       }
@@ -89,17 +94,16 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
   };
 
   const int P = min(max(prefix_len[s], 0), Pmax);
-  const T* kc = k_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
-  const T* vc = v_cache + (size_t)(s * Hkv + kvh) * Pmax * D;
   for (int k0 = 0; k0 < P; k0 += 64) {
     const int key = k0 + lane;
     float sc = -INFINITY;
     if (key < P) {
+      const size_t kr = prow(key);
       float d0 = 0.f;
-      for (int d = 0; d < D; ++d) d0 += qs[d] * Elem<T>::load(kc, (size_t)key * D + d);
+      for (int d = 0; d < D; ++d) d0 += qs[d] * Elem<T>::load(k_cache, kr + d);
       sc = d0;
     }
-    block(sc, vc, k0);
+    block(sc, v_cache, k0, true);
   }
   const uint64_t a = anc[(size_t)s * Tn + i];
   const T* kt = k_tree + (size_t)(s * Hkv + kvh) * Tn * D;
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
       for (int d = 0; d < D; ++d) d0 += qs[d] * Elem<T>::load(kt, (size_t)j * D + d);
       sc = d0;
     }
-    block(sc, vt, j0);
+    block(sc, vt, j0, false);
   }
   const float inv = 1.f / l;
 #pragma unroll
@@ -147,7 +151,7 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // (its V still feeds P.V), tile it, and tiles it+1, it+2 whose copies are in flight.
 // Iteration it: S(it) = K(it) Q^T, then O += V(it-1)^T P(it-1)^T issued together with
 // the softmax of S(it), so the exp/max/sum work overlaps the matrix-core products.
-template <int D, int NT, int NW, int PK, int PV>
+template <int D, int NT, int NW, int PK, int PV, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
                                                            const uint16_t* __restrict__ v_cache,
@@ -156,8 +160,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
                                                            const uint16_t* __restrict__ v_tree,
                                                            const uint64_t* __restrict__ anc, int Tn, int Hq,
                                                            int Hkv, int Pmax, float sl2, int nwg, int nsplit,
-                                                           int split_len, int units, float* __restrict__ part_lse,
-                                                           float* __restrict__ part_o, uint16_t* __restrict__ out) {
+                                                           int split_len, int units, PagedKV pg,
+                                                           float* __restrict__ part_lse, float* __restrict__ part_o,
+                                                           uint16_t* __restrict__ out) {
   constexpr int NK = kAttnNK, NST = kAttnStages;
   constexpr int ROWB = D * 2, LPR = ROWB / 16;  // bytes of a key row, DMA lanes per key row
   constexpr int RS = ROWB + 32;                 // LDS row stride (padded, see below)
@@ -188,8 +193,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   const int n_pre = (k_end - k_beg + NK - 1) / NK;
   const int n_all = n_pre + (last ? (Tn + NK - 1) / NK : 0);
   const size_t hoff = (size_t)s * Hkv + kvh;
-  const uint16_t* Kp = k_cache + hoff * Pmax * D;
-  const uint16_t* Vp = v_cache + hoff * Pmax * D;
+  // contiguous: this (sequence, kv head)'s rows; paged: the pool (rows found per page)
+  const uint16_t* Kp = PAGED ? k_cache : k_cache + hoff * Pmax * D;
+  const uint16_t* Vp = PAGED ? v_cache : v_cache + hoff * Pmax * D;
   const uint16_t* Kt = k_tree + hoff * Tn * D;
   const uint16_t* Vt = v_tree + hoff * Tn * D;
 
@@ -214,7 +220,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int row = wave + NW * k;
-        const size_t e = (size_t)(r0 + min(row, rows - 1)) * D + (ln ^ ((row >> 3) & 1)) * 8;
+        const int key = r0 + min(row, rows - 1);  // wave-uniform: a paged lookup is one scalar load
+        size_t e = (size_t)key * D;
+        if constexpr (PAGED)
+          if (pre) e = pg.row_uniform(s, kvh, Hkv, key) * D;
+        e += (ln ^ ((row >> 3) & 1)) * 8;
         const uint32_t m = kb + (uint32_t)(row * RS);
         dma16(Kg + e, m);
         dma16(Vg + e, m + TILE);
@@ -601,14 +611,20 @@ AttnPlan plan_tree_attn(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt) 
 hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
                             const void* k_tree, const void* v_tree, const uint64_t* anc, int n, int T, int Hq,
                             int Hkv, int D, int Pmax, float scale, int dt, void* out, const AttnPlan& plan,
-                            void* ws, hipStream_t st) {
+                            void* ws, hipStream_t st, const PagedKV& pg) {
+  const bool paged = pg.bt != nullptr;
   if (!plan.mfma) {
     const dim3 grid(n * T * Hq);
-#define DDT_SCALAR(TY, DD)                                                                                   \
-  hipLaunchKernelGGL((attn_scalar_kernel<TY, DD>), grid, dim3(64), 0, st, static_cast<const TY*>(q),          \
+#define DDT_SCALAR1(TY, DD, PG)                                                                              \
+  hipLaunchKernelGGL((attn_scalar_kernel<TY, DD, PG>), grid, dim3(64), 0, st, static_cast<const TY*>(q),      \
                      static_cast<const TY*>(k_cache), static_cast<const TY*>(v_cache), prefix_len,           \
                      static_cast<const TY*>(k_tree), static_cast<const TY*>(v_tree), anc, T, Hq, Hkv, Pmax,  \
-                     scale, static_cast<TY*>(out))
+                     scale, pg, static_cast<TY*>(out))
+#define DDT_SCALAR(TY, DD)            \
+  do {                                \
+    if (paged) DDT_SCALAR1(TY, DD, true);  \
+    else DDT_SCALAR1(TY, DD, false);       \
+  } while (0)
     if (dt == DDT_F32) {
       if (D == 64) DDT_SCALAR(float, 64);
       else if (D == 128) DDT_SCALAR(float, 128);
@@ -617,6 +633,7 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
       DDT_SCALAR(uint16_t, 64);
     }
 #undef DDT_SCALAR
+#undef DDT_SCALAR1
     return hipGetLastError();
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -630,21 +647,24 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
   const auto* kt = static_cast<const uint16_t*>(k_tree);
   const auto* vt = static_cast<const uint16_t*>(v_tree);
   auto* o16 = static_cast<uint16_t*>(out);
+#define DDT_MFMA(DD, PG)                                                                                     \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, attn_nt(DD), attn_nw(DD), DDT_ATTN_PK, DDT_ATTN_PV, PG>), grid,      \
+                     dim3(64 * attn_nw(DD)), 0, st, qq, kc, vc, prefix_len, kt, vt, anc, T, Hq, Hkv, Pmax, sl2, \
+                     plan.nwg, plan.nsplit, plan.split_len, plan.units, pg, part_lse, part_o, o16)
   if (D == 256) {
-    hipLaunchKernelGGL((attn_mfma_kernel<256, attn_nt(256), attn_nw(256), DDT_ATTN_PK, DDT_ATTN_PV>), grid, dim3(64 * attn_nw(256)), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, plan.units, part_lse,
-                       part_o, o16);
+    if (paged) DDT_MFMA(256, true);
+    else DDT_MFMA(256, false);
     if (plan.nsplit > 1)
       hipLaunchKernelGGL((attn_combine_kernel<256>), dim3(n * T * Hq), dim3(64), 0, st, part_lse, part_o, T, Hq, Hkv,
                          plan.nsplit, o16);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<128, attn_nt(128), attn_nw(128), DDT_ATTN_PK, DDT_ATTN_PV>), grid, dim3(64 * attn_nw(128)), 0, st, qq, kc, vc, prefix_len, kt, vt,
-                       anc, T, Hq, Hkv, Pmax, sl2, plan.nwg, plan.nsplit, plan.split_len, plan.units, part_lse,
-                       part_o, o16);
+    if (paged) DDT_MFMA(128, true);
+    else DDT_MFMA(128, false);
     if (plan.nsplit > 1)
       hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(n * T * Hq), dim3(32), 0, st, part_lse, part_o, T, Hq, Hkv,
                          plan.nsplit, o16);
   }
+#undef DDT_MFMA
   return hipGetLastError();
 }
 

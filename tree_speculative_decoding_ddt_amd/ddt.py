@@ -21,6 +21,7 @@ EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_build_tree_workspace", "ddt_build_tree",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
            "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope",
+           "ddt_tree_attn_paged_workspace", "ddt_tree_attn_paged", "ddt_commit_paged",
            "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
            "ddt_commit", "ddt_gdn_replay")
@@ -72,6 +73,10 @@ def lib():
         "ddt_tree_attn_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_tree_attn_rope_workspace": (Z, [I, I, I, I, I, I, I]),
+        "ddt_tree_attn_paged_workspace": (Z, [I, I, I, I, I, I, I, I]),
+        "ddt_tree_attn_paged": (I, [P, P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, F, I, P, P, Z, P]),
+        "ddt_commit_paged": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, P, I, I, I, I,
+                                 ctypes.POINTER(GDNLayer), I, I, I, I, I, I, I, I, I, I, P]),
         "ddt_tree_attn_rope": (I, [P, P, P, P, I, F, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_gdn_tree_step_workspace": (Z, [I, I, I, I]),
         "ddt_gdn_tree_step": (I, [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P]),
@@ -146,6 +151,11 @@ def tree_attn_rope_workspace(n, B, Hq, Hkv, D, Pmax, dtype):
     return lib().ddt_tree_attn_rope_workspace(n, B, Hq, Hkv, D, Pmax, DDT_BF16 if dtype == torch.bfloat16 else DDT_F32)
 
 
+def tree_attn_paged_workspace(n, B, Hq, Hkv, D, max_blocks, page_size, dtype):
+    return lib().ddt_tree_attn_paged_workspace(n, B, Hq, Hkv, D, max_blocks, page_size,
+                                               DDT_BF16 if dtype == torch.bfloat16 else DDT_F32)
+
+
 def gdn_tree_step_workspace(n, B, H, dk):
     return lib().ddt_gdn_tree_step_workspace(n, B, H, dk)
 
@@ -217,6 +227,25 @@ def tree_attn_rope(q, k_new, v_new, depth, rot_dim, theta, k_cache, v_cache, pre
     return out
 
 
+def tree_attn_paged(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc, scale=0.0, ws=None, out=None):
+    """q [n][T][Hq][D], k/v_pages [num_pages][Hkv][page_size][D], block_table [n][max_blocks] int32,
+    prefix_len [n] int32, k/v_tree [n][Hkv][T][D], anc [n][T] int64 -> out [n][T][Hq][D]."""
+    _gpu(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc)
+    n, T, Hq, D = q.shape
+    num_pages, Hkv, ps = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    maxb = block_table.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dt(q)
+    w = _ws(lib().ddt_tree_attn_paged_workspace(n, T - 1, Hq, Hkv, D, maxb, ps, dt), dev, ws)
+    _check("ddt_tree_attn_paged", lib().ddt_tree_attn_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), maxb, ps, num_pages, _ptr(prefix_len),
+        _ptr(k_tree), _ptr(v_tree), _ptr(anc), n, T - 1, Hq, Hkv, D, float(scale), dt, _ptr(out), _ptr(w),
+        w.numel() * w.element_size(), _stream(dev)))
+    return out
+
+
 def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=None, store_states=True):
     """x [n][T][C], conv_w [C][W] f32, conv_state [n][W-1][C], v [n][T][H][dv], beta, g [n][T][H] f32,
     S [n][H][dv][dk] f32, parent [n][T] int32 -> dict o, S_scratch, conv_scratch.
@@ -260,9 +289,11 @@ def tree_accept(target_logits, tok, parent, L, ws=None, out=None):
     return out
 
 
-def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None):
+def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None, block_table=None):
     """In-place commit.  kv_layers: sequence of (k_tree, v_tree, k_cache, v_cache);
-    gdn_layers: sequence of (S_scratch, S, conv_scratch, conv_state)."""
+    gdn_layers: sequence of (S_scratch, S, conv_scratch, conv_state).
+    With block_table [n][max_blocks] int32, k_cache / v_cache are page pools
+    [num_pages][Hkv][page_size][D] (ddt_commit_paged)."""
     _gpu(acc_rows, acc_len, prefix_len)
     n, Lp1 = acc_rows.shape
     dev = acc_rows.device
@@ -287,6 +318,15 @@ def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None):
         if T is None:
             raise ValueError("commit needs B when no layer is given")
         B = T - 1
+    if block_table is not None:
+        _gpu(block_table)
+        ps = kv_layers[0][2].shape[2] if len(kv_layers) else 1
+        num_pages = kv_layers[0][2].shape[0] if len(kv_layers) else 1
+        _check("ddt_commit_paged", lib().ddt_commit_paged(
+            _ptr(acc_rows), _ptr(acc_len), _ptr(prefix_len), kv, len(kv_layers), Hkv, D, _ptr(block_table),
+            block_table.shape[1], ps, num_pages, kv_dt, gd, len(gdn_layers), H, dk, dv, C, W, act_dt, n, B,
+            Lp1 - 1, _stream(dev)))
+        return
     _check("ddt_commit", lib().ddt_commit(
         _ptr(acc_rows), _ptr(acc_len), _ptr(prefix_len), kv, len(kv_layers), Hkv, D, Pmax, kv_dt,
         gd, len(gdn_layers), H, dk, dv, C, W, act_dt, n, B, Lp1 - 1, _stream(dev)))

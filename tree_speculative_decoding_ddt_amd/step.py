@@ -42,6 +42,7 @@ class HybridConfig:
     pattern: list = field(default_factory=list)  # "gdn"/"attn" per layer; default [gdn, gdn, gdn, attn]*
     replay: bool = False       # store no per-node GDN state; the commit replays the accepted path
     rope: tuple = None         # (rot_dim, theta): attention inputs are pre-rotation, RoPE at prefix + depth
+    page_size: int = 0         # > 0: the committed KV lives in pages of this many positions (block table)
 
     def layer_pattern(self):
         if self.pattern:
@@ -86,9 +87,22 @@ class HybridVerifyStep:
         self.target_logits = e(n, T, c.V)
         self.root_token = torch.zeros(n, dtype=torch.int32, device=dev)
         self.prefix_len = torch.full((n,), c.prefix, dtype=torch.int32, device=dev)
+        self.block_table = None
+        if c.page_size:
+            # pages of every sequence scattered over a shared pool (a seeded permutation,
+            # with spare pages), as a serving engine's allocator would leave them
+            assert c.Pmax % c.page_size == 0, "capacity must be whole pages"
+            maxb = c.Pmax // c.page_size
+            self.num_pages = n * maxb + 8
+            g = torch.Generator()
+            g.manual_seed(1234)
+            perm = torch.randperm(self.num_pages, generator=g)[: n * maxb]
+            self.block_table = perm.view(n, maxb).to(torch.int32).to(dev)
+            cache = lambda: e(self.num_pages, c.Hkv, c.page_size, c.D)
+        else:
+            cache = lambda: e(n, c.Hkv, c.Pmax, c.D)
         self.attn = [dict(q=e(n, T, c.Hq, c.D), k_tree=e(n, c.Hkv, T, c.D), v_tree=e(n, c.Hkv, T, c.D),
-                          k_cache=e(n, c.Hkv, c.Pmax, c.D), v_cache=e(n, c.Hkv, c.Pmax, c.D),
-                          out=e(n, T, c.Hq, c.D)) for _ in range(c.n_attn)]
+                          k_cache=cache(), v_cache=cache(), out=e(n, T, c.Hq, c.D)) for _ in range(c.n_attn)]
         if c.rope:
             # the tree rows' keys and values as a projection writes them (token-major, before
             # rotation); k_tree / v_tree become outputs of the attention call
@@ -109,11 +123,39 @@ class HybridVerifyStep:
                     "bonus": e(n, dtype=torch.int32)}
         u8 = lambda nb: torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         self.ws_build = u8(ddt.build_tree_workspace(n, c.L, c.V, c.B, c.K))
+        assert not (c.rope and c.page_size), "RoPE inside the call is built for the contiguous cache"
         self.ws_attn = u8((ddt.tree_attn_rope_workspace if c.rope else ddt.tree_attn_workspace)(
             n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, dt))
         self.ws_acc = u8(ddt.tree_accept_workspace(n, c.B, c.V))
         self.ws_gdn = u8(ddt.gdn_tree_step_workspace(n, c.B, c.H, c.dk))
         self.pattern = c.layer_pattern()
+
+    def set_mode(self, replay=None, rope=False):
+        """Switch the GDN commit mode (replay) and/or the attention input mode (rope:
+        None for post-rotation inputs, (rot_dim, theta) for RoPE inside the call).  Buffers
+        a mode needs are allocated here; a newly needed k_new / v_new takes the current
+        tree keys / values (token-major), so the data stays that of the workload."""
+        c = self.cfg
+        if replay is not None:
+            c.replay = bool(replay)
+            if not c.replay:
+                for g in self.gdn:
+                    if g["out"]["S_scratch"] is None:
+                        g["out"]["S_scratch"] = torch.empty(c.n, c.T, c.H, c.dk, c.dk, dtype=torch.float32,
+                                                            device=self.dev)
+                        g["out"]["conv_scratch"] = torch.empty(c.n, c.T, c.W - 1, c.C, dtype=c.dtype, device=self.dev)
+        if rope is not False:
+            assert not (rope and c.page_size), "RoPE inside the call is built for the contiguous cache"
+            c.rope = rope
+            if rope:
+                for a in self.attn:
+                    if "k_new" not in a:
+                        a["k_new"] = a["k_tree"].transpose(1, 2).contiguous()
+                        a["v_new"] = a["v_tree"].transpose(1, 2).contiguous()
+            nb = (ddt.tree_attn_rope_workspace if c.rope else ddt.tree_attn_workspace)(
+                c.n, c.B, c.Hq, c.Hkv, c.D, c.Pmax, c.dtype)
+            if self.ws_attn.numel() < nb:
+                self.ws_attn = torch.empty(nb, dtype=torch.uint8, device=self.dev)
 
     # ------------------------------------------------------------ the round
     def build(self):
@@ -131,6 +173,9 @@ class HybridVerifyStep:
                                        self.cfg.rope[1], a["k_cache"], a["v_cache"], self.prefix_len,
                                        self.tree["anc"], ws=self.ws_attn,
                                        out={"o": a["out"], "k_tree": a["k_tree"], "v_tree": a["v_tree"]})
+                elif self.block_table is not None:
+                    ddt.tree_attn_paged(a["q"], a["k_cache"], a["v_cache"], self.block_table, self.prefix_len,
+                                        a["k_tree"], a["v_tree"], self.tree["anc"], ws=self.ws_attn, out=a["out"])
                 else:
                     ddt.tree_attn(a["q"], a["k_cache"], a["v_cache"], self.prefix_len, a["k_tree"], a["v_tree"],
                                   self.tree["anc"], ws=self.ws_attn, out=a["out"])
@@ -150,14 +195,15 @@ class HybridVerifyStep:
         if self.cfg.replay:
             # KV rows are copied; the recurrent state is advanced along the accepted path
             # after the commit has marked the sequences that may not be written
-            ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv, (), B=self.cfg.B)
+            ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv, (), B=self.cfg.B,
+                       block_table=self.block_table)
             ddt.gdn_replay(self.acc["acc_rows"], self.acc["acc_len"],
                            [(g["x"], g["conv_w"], g["v"], g["beta"], g["g"], g["S"], g["conv_state"])
                             for g in self.gdn], B=self.cfg.B)
         else:
             ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv,
                        [(g["out"]["S_scratch"], g["S"], g["out"]["conv_scratch"], g["conv_state"])
-                        for g in self.gdn], B=self.cfg.B)
+                        for g in self.gdn], B=self.cfg.B, block_table=self.block_table)
         # the bonus token of this round is the root of the next one
         self.root_token.copy_(self.acc["bonus"])
 
