@@ -152,7 +152,7 @@ def main():
     ddt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(2 * a.steps + a.warmup + 3) * 16 + 64)
+    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(3 * a.steps + a.warmup + 4) * 16 + 64)
     step = HybridVerifyStep(cfg, dev)
     step.fill_random(seed=a.seed)
     print("bench: inputs ready (%.1f GB on device)" % (torch.cuda.memory_allocated(dev) / 1e9),
@@ -168,6 +168,19 @@ def main():
         e.record()
         ev[name].append((s, e))
 
+    def attn_call(lay):
+        if step.block_table is not None:
+            return lambda: ddt.tree_attn_paged(lay["q"], lay["k_cache"], lay["v_cache"], step.block_table,
+                                               step.prefix_len, lay["k_tree"], lay["v_tree"], step.tree["anc"],
+                                               ws=step.ws_attn, out=lay["out"])
+        if cfg.rope:
+            return lambda: ddt.tree_attn_rope(lay["q"], lay["k_new"], lay["v_new"], step.tree["depth"], cfg.rope[0],
+                                              cfg.rope[1], lay["k_cache"], lay["v_cache"], step.prefix_len,
+                                              step.tree["anc"], ws=step.ws_attn,
+                                              out={"o": lay["out"], "k_tree": lay["k_tree"], "v_tree": lay["v_tree"]})
+        return lambda: ddt.tree_attn(lay["q"], lay["k_cache"], lay["v_cache"], step.prefix_len, lay["k_tree"],
+                                     lay["v_tree"], step.tree["anc"], ws=step.ws_attn, out=lay["out"])
+
     def run_step(record):
         if not record:
             step()
@@ -178,9 +191,7 @@ def main():
             if kind == "attn":
                 lay = step.attn[ia]
                 ia += 1
-                timed("tree_attn", lambda: ddt.tree_attn(lay["q"], lay["k_cache"], lay["v_cache"], step.prefix_len,
-                                                         lay["k_tree"], lay["v_tree"], step.tree["anc"],
-                                                         ws=step.ws_attn, out=lay["out"]))
+                timed("tree_attn", attn_call(lay))
             else:
                 g = step.gdn[ig]
                 ig += 1
@@ -236,23 +247,39 @@ def main():
 
     # Variant: the same step with no per-node GDN state stored; the commit replays the
     # accepted path on the committed state.  Reported beside the stored-state step.
+    # Second variant: also RoPE at prefix + depth inside the attention call (pre-rotation
+    # q and tree K/V in; rotate-half over all 256 channels, theta 10000).
+    # Third variant: the committed KV in pages of 16 positions scattered over a pool (a
+    # fresh step object with GDN replay, built after the others are released).
     variant = None
     if not a.no_variant:
-        for k in names:
-            ev[k].clear()
-        cfg.replay = True
-        run_step(False)
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
-        for _ in range(a.steps):
-            run_step(True)
-        torch.cuda.synchronize(dev)
-        dtv = time.perf_counter() - t0
-        cfg.replay = False
-        variant = {"gdn_replay_on_commit": {
-            "steps_per_s": round(a.steps / dtv, 3), "ms_per_step": round(dtv / a.steps * 1e3, 3),
-            "kernels_ms_per_step": {k: round(sum(s.elapsed_time(e) for s, e in ev[k]) / a.steps, 4)
-                                    for k in names}}}
+        variant = {}
+
+        def time_variant(vname):
+            for k in names:
+                ev[k].clear()
+            run_step(False)
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            for _ in range(a.steps):
+                run_step(True)
+            torch.cuda.synchronize(dev)
+            dtv = time.perf_counter() - t0
+            variant[vname] = {
+                "steps_per_s": round(a.steps / dtv, 3), "ms_per_step": round(dtv / a.steps * 1e3, 3),
+                "kernels_ms_per_step": {k: round(sum(s.elapsed_time(e) for s, e in ev[k]) / a.steps, 4)
+                                        for k in names}}
+
+        for vname, mode in (("gdn_replay_on_commit", dict(replay=True)),
+                            ("gdn_replay_and_rope_attention", dict(replay=True, rope=(cfg.D, 10000.0)))):
+            step.set_mode(**mode)
+            time_variant(vname)
+        step = None
+        torch.cuda.empty_cache()
+        cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=cfg.extra_cap, replay=True, page_size=16)
+        step = HybridVerifyStep(cfg, dev)
+        step.fill_random(seed=a.seed)
+        time_variant("paged16_gdn_replay")
 
     cpu = None
     if not a.no_cpu:
