@@ -7,6 +7,7 @@
  *   ddt_tree_attn      tree-masked attention of every node over prefix + ancestors
  *   ddt_tree_attn_rope the same, from pre-rotation q and tree K/V: RoPE at positions
  *                      prefix + depth, tree K/V written to their scratch
+ *   ddt_tree_rope      the rotation step alone (for ddt_tree_attn_paged callers)
  *   ddt_tree_attn_paged the same over a paged committed cache (block table + page pool)
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
@@ -168,6 +169,12 @@ int ddt_tree_attn_paged(const void* q, const void* k_pages, const void* v_pages,
  * own workspace); required.  Built: rot_dim a multiple of 16 in [16, D]; theta > 1.
  */
 size_t ddt_tree_attn_rope_workspace(int n, int B, int Hq, int Hkv, int D, int Pmax, int dt);
+/* The rotation step alone (the first kernel of ddt_tree_attn_rope): rotated queries
+ * to q_out [n][T][Hq][D], rotated keys / copied values to k_tree / v_tree.  For callers
+ * that then attend with ddt_tree_attn_paged.  Same arguments and limits as above. */
+int ddt_tree_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth,
+                  const int32_t* prefix_len, int rot_dim, float theta, int n, int B, int Hq, int Hkv, int D,
+                  int dt, void* q_out, void* k_tree, void* v_tree, void* stream);
 int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth, int rot_dim,
                        float theta, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
                        void* k_tree, void* v_tree, const uint64_t* anc, int n, int B, int Hq, int Hkv, int D,

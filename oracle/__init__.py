@@ -17,6 +17,7 @@ Modules
   paged      -- the committed cache in pages: gather, paged attention, paged commit
   gdn        -- short causal conv + gated delta rule over the tree
   accept     -- target argmax + greedy tree walk
+  sampled    -- the walk over sampled target tokens (Gumbel-max, noise as input)
   commit     -- copy of the accepted path into the committed buffers
   step       -- the whole verify step composed from the above
 
@@ -24,4 +25,4 @@ Every function takes and returns NumPy arrays; floating-point inputs are
 promoted to float64 before any arithmetic.
 """
 
-from . import tree, attention, rope, gdn, accept, commit, paged, step, gaps  # noqa: F401
+from . import tree, attention, rope, gdn, accept, commit, paged, sampled, step, gaps  # noqa: F401

@@ -23,8 +23,12 @@ def argmax_lowest(row):
 
 def tree_accept(target_logits, tok, parent, L):
     """target_logits [T][V], tok/parent [T] -> (acc_rows [L+1], a, bonus)."""
+    return walk([argmax_lowest(target_logits[i]) for i in range(len(tok))], tok, parent, L)
+
+
+def walk(t, tok, parent, L):
+    """The walk given the target's token t[i] of every row -> (acc_rows [L+1], a, bonus)."""
     T = len(tok)
-    t = [argmax_lowest(target_logits[i]) for i in range(T)]
     path = [0]
     cur = 0
     while True:

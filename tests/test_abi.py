@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -94,6 +94,13 @@ def test_tree_attn_rope_validation():
     need = ddt.tree_attn_rope_workspace(1, 8, 2, 1, 64, 128, __import__("torch").float32)
     assert need >= 1 * 9 * 2 * 64 * 4 > 0                                              # room for the rotated queries
     assert status("ddt_tree_attn_rope", *args(wsb=need - 1)) == ddt.DDT_ERR_WORKSPACE
+    r = [P, P, P, P, P, 64, ctypes.c_float(1e4), 1, 8, 2, 1, 64, 0, P, P, P, None]
+    r2 = list(r); r2[3] = None
+    assert status("ddt_tree_rope", *r2) == ddt.DDT_ERR_ARG
+    r2 = list(r); r2[5] = 72
+    assert status("ddt_tree_rope", *r2) == ddt.DDT_ERR_UNSUPPORTED
+    r2 = list(r); r2[11] = 96
+    assert status("ddt_tree_rope", *r2) == ddt.DDT_ERR_UNSUPPORTED
 
 
 def test_paged_validation():

@@ -129,3 +129,32 @@ def test_commit_paged(dtype):
     np.testing.assert_array_equal(down(al_d), want_a)
     np.testing.assert_array_equal(down(kpd), kp_ref)
     np.testing.assert_array_equal(down(vpd), vp_ref)
+
+
+def test_rope_then_paged_attention():
+    # the rotation as its own call, then the paged attention on its outputs
+    from oracle import rope as orope
+    say("paged attention after ddt_tree_rope")
+    rng = np.random.default_rng(21)
+    n, B, L, Hq, Hkv, D, ps, maxb = 2, 64, 15, 24, 4, 256, 32, 40
+    parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    depth = np.zeros_like(parents)
+    for s in range(n):
+        for i in range(1, B + 1):
+            depth[s, i] = depth[s, parents[s, i]] + 1
+    anc = np.stack([otree.ancestor_masks(p) for p in parents])
+    T = B + 1
+    bt, kp, vp = make_pool(rng, n, maxb, Hkv, ps, D)
+    pl = np.array([1200, 333])
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    q, kn, vn = f(n, T, Hq, D), f(n, T, Hkv, D), f(n, T, Hkv, D)
+    (qd, qe), (knd, kne), (vnd, vne), (kpd, kpe), (vpd, vpe) = (up(a, "bf16") for a in (q, kn, vn, kp, vp))
+    r = ddt.tree_rope(qd, knd, vnd, up_int(depth), up_int(pl), 64, 1e6)
+    out = ddt.tree_attn_paged(r["q"], kpd, vpd, up_int(bt), up_int(pl), r["k_tree"], r["v_tree"], anc_tensor(anc))
+    torch.cuda.synchronize()
+    got, kt = down(out), down(r["k_tree"])
+    for s in range(n):
+        qr, kr, vr = orope.rope_tree_inputs(qe[s], kne[s], vne[s], pl[s], depth[s], 64, 1e6)
+        assert_close(kt[s], kr, "bf16", "rotated keys seq %d" % s)
+        ref = opaged.tree_attention_paged(qr, kpe, vpe, bt[s], pl[s], kr, vr, anc[s])
+        assert_close(got[s], ref, "bf16", "o seq %d" % s)

@@ -16,12 +16,14 @@ import oracle.commit
 import oracle.gdn
 import oracle.paged
 import oracle.rope
+import oracle.sampled
 import oracle.tree
 from tests import test_oracle_accept_commit as t_ac
 from tests import test_oracle_attention as t_attn
 from tests import test_oracle_gdn as t_gdn
 from tests import test_oracle_paged as t_paged
 from tests import test_oracle_rope as t_rope
+from tests import test_oracle_sampled as t_smp
 from tests import test_oracle_tree as t_tree
 
 
@@ -63,6 +65,10 @@ PAGED_PINS = [t_paged.test_hand_example_two_pages, lambda: t_paged.test_identity
               lambda: t_paged.test_paged_commit_equals_contiguous_commit(14, 5),
               lambda: t_paged.test_paged_commit_equals_contiguous_commit(58, 5), t_paged.test_paged_commit_overflow_leaves_pages]
 
+SMP_PINS = [lambda: t_smp.test_draws_follow_the_tempered_softmax(0.5), t_smp.test_zero_temperature_and_zero_noise_are_greedy,
+            t_smp.test_power_of_two_rescaling_is_exact, t_smp.test_sampled_tokens_decide_the_path,
+            t_smp.test_walk_emits_target_samples_along_a_chain]
+
 CASES = [
     (oracle.tree, "build_tree", "int(ids[0, 0]), 0, 1, 0", "int(ids[0, 0]), 0, 1, 1", TREE_PINS),
     (oracle.tree, "build_tree", "score[p] + vals[d - 1, r + 1]", "score[p] + vals[d - 1, r]", TREE_PINS),
@@ -84,7 +90,7 @@ CASES = [
     (oracle.gdn, "split_qk", "+ K_NORM_EPS)", "+ 1.0)", GDN_PINS),
     (oracle.gdn, "split_qk", "* dk ** -0.5", "* 1.0", GDN_PINS),
     (oracle.accept, "argmax_lowest", "[0])", "[-1])", ACC_PINS),
-    (oracle.accept, "tree_accept", "tok[c] == t[cur]", "tok[c] == t[c]", ACC_PINS),
+    (oracle.accept, "walk", "tok[c] == t[cur]", "tok[c] == t[c]", ACC_PINS),
     (oracle.commit, "commit", 'lay["k_cache"][:, P + j, :] = lay["k_tree"][:, r, :]',
      'lay["k_cache"][:, P + j + 1, :] = lay["k_tree"][:, r, :]', ACC_PINS),
     (oracle.commit, "commit", "last = rows[-1]", "last = rows[0]", ACC_PINS),
@@ -98,6 +104,10 @@ CASES = [
     (oracle.paged, "gather", "[pos // ps], :, pos % ps", "[pos // ps], :, (pos + 1) % ps", PAGED_PINS),
     (oracle.paged, "scatter", "p = start + j", "p = start + j + 1", PAGED_PINS),
     (oracle.paged, "commit_paged", "P + a + 1 > cap", "P + a > cap", PAGED_PINS),
+    (oracle.sampled, "sample_token", "* inv", "* np.float32(temperature)", SMP_PINS),
+    (oracle.sampled, "sample_token", "key + np.asarray(g_row", "key - np.asarray(g_row", SMP_PINS),
+    (oracle.sampled, "sample_token", "if temperature <= 0:", "if temperature < 0:", SMP_PINS),
+    (oracle.sampled, "tree_accept_sampled", "gumbel[i], temperature)", "gumbel[0], temperature)", SMP_PINS),
     # the mistake the pages warn of: positions by flattened row order instead of depth
     (oracle.rope, "tree_positions", "prefix_len[:, None] + depth", "prefix_len[:, None] + np.arange(depth.shape[1])",
      ROPE_PINS),

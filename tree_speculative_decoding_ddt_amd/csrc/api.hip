@@ -193,6 +193,27 @@ size_t ddt_tree_attn_rope_workspace(int n, int B, int Hq, int Hkv, int D, int Pm
   return rope_q_bytes(n, B, Hq, D, dt) + ddt::plan_tree_attn(n, B, Hq, Hkv, D, Pmax, dt).total;
 }
 
+int ddt_tree_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth, const int32_t* prefix_len,
+                  int rot_dim, float theta, int n, int B, int Hq, int Hkv, int D, int dt, void* q_out, void* k_tree,
+                  void* v_tree, void* stream) {
+  DDT_NEED(q); DDT_NEED(k_new); DDT_NEED(v_new); DDT_NEED(depth); DDT_NEED(prefix_len);
+  DDT_NEED(q_out); DDT_NEED(k_tree); DDT_NEED(v_tree);
+  DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && Hq >= 1 && Hkv >= 1, DDT_ERR_ARG,
+            "ddt_tree_rope: need n>=1, 0<=B<=64, Hq,Hkv>=1");
+  DDT_CHECK(dt_ok(dt), DDT_ERR_UNSUPPORTED, "ddt_tree_rope: dtype %d", dt);
+  DDT_CHECK(D == 64 || D == 128 || D == 256, DDT_ERR_UNSUPPORTED, "ddt_tree_rope: head size D=%d not built", D);
+  DDT_CHECK(rot_dim >= 16 && rot_dim <= D && rot_dim % 16 == 0, DDT_ERR_UNSUPPORTED,
+            "ddt_tree_rope: rot_dim=%d must be a multiple of 16 in [16, D=%d]", rot_dim, D);
+  DDT_CHECK(theta > 1.f && isfinite(theta), DDT_ERR_ARG, "ddt_tree_rope: theta=%g must be finite and > 1",
+            (double)theta);
+  DDT_CHECK(aligned16(q) && aligned16(k_new) && aligned16(v_new) && aligned16(q_out) && aligned16(k_tree) &&
+                aligned16(v_tree),
+            DDT_ERR_ARG, "ddt_tree_rope: tensors must be 16-byte aligned");
+  return hip_status(ddt::launch_tree_rope(q, k_new, v_new, depth, prefix_len, n, B + 1, Hq, Hkv, D, rot_dim, theta,
+                                          dt, q_out, k_tree, v_tree, static_cast<hipStream_t>(stream)),
+                    "ddt_tree_rope");
+}
+
 int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, const int32_t* depth, int rot_dim,
                        float theta, const void* k_cache, const void* v_cache, const int32_t* prefix_len, void* k_tree,
                        void* v_tree, const uint64_t* anc, int n, int B, int Hq, int Hkv, int D, int Pmax, float scale,

@@ -20,7 +20,7 @@ DDT_F32, DDT_BF16 = 0, 1
 EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_build_tree_workspace", "ddt_build_tree",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
-           "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope",
+           "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope", "ddt_tree_rope",
            "ddt_tree_attn_paged_workspace", "ddt_tree_attn_paged", "ddt_commit_paged",
            "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
@@ -74,6 +74,7 @@ def lib():
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_tree_attn_rope_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn_paged_workspace": (Z, [I, I, I, I, I, I, I, I]),
+        "ddt_tree_rope": (I, [P, P, P, P, P, I, F, I, I, I, I, I, I, P, P, P, P]),
         "ddt_tree_attn_paged": (I, [P, P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_commit_paged": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, P, I, I, I, I,
                                  ctypes.POINTER(GDNLayer), I, I, I, I, I, I, I, I, I, I, P]),
@@ -224,6 +225,21 @@ def tree_attn_rope(q, k_new, v_new, depth, rot_dim, theta, k_cache, v_cache, pre
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(depth), int(rot_dim), float(theta), _ptr(k_cache), _ptr(v_cache),
         _ptr(prefix_len), _ptr(out["k_tree"]), _ptr(out["v_tree"]), _ptr(anc), n, T - 1, Hq, Hkv, D, Pmax,
         float(scale), dt, _ptr(out["o"]), _ptr(w), w.numel() * w.element_size(), _stream(dev)))
+    return out
+
+
+def tree_rope(q, k_new, v_new, depth, prefix_len, rot_dim, theta, out=None):
+    """Rotation alone: -> dict q (rotated, [n][T][Hq][D]), k_tree/v_tree [n][Hkv][T][D]."""
+    _gpu(q, k_new, v_new, depth, prefix_len)
+    n, T, Hq, D = q.shape
+    Hkv = k_new.shape[2]
+    dev = q.device
+    if out is None:
+        out = {"q": torch.empty_like(q), "k_tree": torch.empty(n, Hkv, T, D, dtype=q.dtype, device=dev),
+               "v_tree": torch.empty(n, Hkv, T, D, dtype=q.dtype, device=dev)}
+    _check("ddt_tree_rope", lib().ddt_tree_rope(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(depth), _ptr(prefix_len), int(rot_dim), float(theta), n, T - 1, Hq,
+        Hkv, D, _dt(q), _ptr(out["q"]), _ptr(out["k_tree"]), _ptr(out["v_tree"]), _stream(dev)))
     return out
 
 
