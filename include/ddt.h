@@ -11,6 +11,7 @@
  *   ddt_tree_attn_paged the same over a paged committed cache (block table + page pool)
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
+ *   ddt_tree_accept_sampled  the walk over sampled target tokens (Gumbel-max draws)
  *   ddt_commit         copy only the accepted path into the committed buffers
  *   ddt_commit_paged   the same with the KV rows scattered into a paged cache
  *   ddt_gdn_replay     (alternative to storing node states) advance the committed GDN
@@ -226,6 +227,26 @@ size_t ddt_tree_accept_workspace(int n, int B, int V);
 int ddt_tree_accept(const void* target_logits, int dt, const int32_t* tok, const int32_t* parent,
                     int n, int B, int L, int V, int32_t* acc_rows, int32_t* acc_len,
                     int32_t* bonus, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- sampled walk
+ * [notes] "What broke along the way": the walk compares sampled tokens (greedy-only
+ * testing hid anomalies).  Same walk as ddt_tree_accept with each row's target token
+ * drawn from softmax(z / t) instead of the argmax, by Gumbel-max:
+ *   token(row) = argmax_v ( z[row][v] * (1/t) + gumbel[row][v] ),  ties to the lowest id
+ * with t = temperature[s] of the row's sequence; 1/t, the product and the sum are each
+ * one correctly rounded float32 operation (no fused multiply-add), so a host doing the
+ * same float32 operations reproduces every decision.  t <= 0: greedy (argmax of z).
+ * Every emitted token (accepted path and bonus) is then a draw of the target at its
+ * own row, whatever the drafter proposed.
+ *   gumbel      [n][T][V] f32 (device): the draws' noise, -log(-log U) of uniforms U,
+ *               finite; supplied by the caller (one fresh array per round)
+ *   temperature [n] f32 (device)
+ *   other arguments and the workspace (ddt_tree_accept_workspace) as ddt_tree_accept.
+ */
+int ddt_tree_accept_sampled(const void* target_logits, int dt, const float* gumbel, const float* temperature,
+                            const int32_t* tok, const int32_t* parent, int n, int B, int L, int V,
+                            int32_t* acc_rows, int32_t* acc_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* ---------------------------------------------------------------- commit
  * [notes] "Why hybrid attention makes it hard" and "Where the next step is": only

@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -179,6 +179,18 @@ def test_gdn_replay_validation():
     assert status("ddt_gdn_replay", *r) == ddt.DDT_ERR_ARG                  # null beta
     lay[0] = ddt.GDNReplayLayer(256, 256, 256, 256, 256, 260, 256)
     assert status("ddt_gdn_replay", *r) == ddt.DDT_ERR_ARG                  # misaligned S
+
+
+def test_accept_sampled_validation():
+    a = [P, 0, P, P, P, P, 1, 8, 4, 512, P, P, P, P, 1 << 30, None]
+    a2 = list(a); a2[2] = None
+    assert status("ddt_tree_accept_sampled", *a2) == ddt.DDT_ERR_ARG       # no noise
+    a2 = list(a); a2[3] = None
+    assert status("ddt_tree_accept_sampled", *a2) == ddt.DDT_ERR_ARG       # no temperatures
+    a2 = list(a); a2[14] = 8
+    assert status("ddt_tree_accept_sampled", *a2) == ddt.DDT_ERR_WORKSPACE
+    a2 = list(a); a2[1] = 5
+    assert status("ddt_tree_accept_sampled", *a2) == ddt.DDT_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,4 +1,4 @@
-// Target argmax + greedy tree walk.
+// Target argmax (or a Gumbel-max draw) + tree walk.
 // Source: "From DDTree to drafter training", section "The Architecture of DDTree":
 // after the verify pass, walk down from the root while the target's token at the
 // current node matches a child; "DDTree on vLLM: candid research notes", section
@@ -17,15 +17,36 @@
 
 namespace ddt {
 
-template <typename T, int VEC>
+// Sampled walk: the Gumbel-max key z * (1/t) + G with each operation rounded once
+// (no fused multiply-add), as IEEE float32 arithmetic written out does it.
+__device__ __forceinline__ float gumbel_key(float z, float inv, float g) {
+#pragma clang fp contract(off)
+  const float a = z * inv;
+  return a + g;
+}
+
+// SAMPLED: the key of element v is z_v * (1/t) + G_v (t = temperature of the row's
+// sequence; t <= 0 keeps z_v, the greedy argmax).
+template <typename T, int VEC, bool SAMPLED>
 __global__ void __launch_bounds__(256) argmax_partial_kernel(const T* __restrict__ logits, int V, int chunk,
+                                                             const float* __restrict__ gumbel,
+                                                             const float* __restrict__ temperature, int T_rows,
                                                              uint64_t* __restrict__ part) {
   const int row = blockIdx.x, c = blockIdx.y, S = gridDim.y;
   const int beg = c * chunk;
   const int end = min(V, beg + chunk);
   const T* p = logits + (size_t)row * V;
+  const float* gp = SAMPLED ? gumbel + (size_t)row * V : nullptr;
+  bool sample = false;
+  float inv = 1.f;
+  if constexpr (SAMPLED) {
+    const float t = temperature[row / T_rows];
+    sample = t > 0.f;
+    inv = sample ? 1.0f / t : 1.f;  // IEEE division (correctly rounded)
+  }
   uint64_t best = 0;
-  auto consider = [&](float v, int id) {
+  auto consider = [&](float v, float g, int id) {
+    if constexpr (SAMPLED) v = sample ? gumbel_key(v, inv, g) : v;
     const uint64_t k = (static_cast<uint64_t>(float_key(v)) << 32) | (0xffffffffu - (uint32_t)id);
     best = k > best ? k : best;
   };
@@ -35,22 +56,34 @@ __global__ void __launch_bounds__(256) argmax_partial_kernel(const T* __restrict
     for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
       const int e0 = beg + i * VEC;
       const uint4 w = *reinterpret_cast<const uint4*>(p + e0);
+      float g[VEC];
+      if constexpr (SAMPLED) {
+#pragma unroll
+        for (int j = 0; j < VEC / 4; ++j) {
+          const float4 q = reinterpret_cast<const float4*>(gp + e0)[j];
+          g[4 * j] = q.x; g[4 * j + 1] = q.y; g[4 * j + 2] = q.z; g[4 * j + 3] = q.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) g[j] = 0.f;
+      }
       if constexpr (sizeof(T) == 2) {
         const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          consider(bf16_to_f32(u[j] & 0xffffu), e0 + 2 * j);
-          consider(bf16_to_f32(u[j] >> 16), e0 + 2 * j + 1);
+          consider(bf16_to_f32(u[j] & 0xffffu), g[2 * j], e0 + 2 * j);
+          consider(bf16_to_f32(u[j] >> 16), g[2 * j + 1], e0 + 2 * j + 1);
         }
       } else {
-        consider(__uint_as_float(w.x), e0);
-        consider(__uint_as_float(w.y), e0 + 1);
-        consider(__uint_as_float(w.z), e0 + 2);
-        consider(__uint_as_float(w.w), e0 + 3);
+        consider(__uint_as_float(w.x), g[0], e0);
+        consider(__uint_as_float(w.y), g[1], e0 + 1);
+        consider(__uint_as_float(w.z), g[2], e0 + 2);
+        consider(__uint_as_float(w.w), g[3], e0 + 3);
       }
     }
   } else {
-    for (int i = beg + threadIdx.x; i < end; i += blockDim.x) consider(Elem<T>::load(p, i), i);
+    for (int i = beg + threadIdx.x; i < end; i += blockDim.x)
+      consider(Elem<T>::load(p, i), SAMPLED ? gp[i] : 0.f, i);
   }
   best = wave_max_u64(best);
   __shared__ uint64_t red[4];
@@ -131,23 +164,32 @@ AcceptPlan plan_tree_accept(int n, int B, int V) {
 
 hipError_t launch_tree_accept(const void* logits, int dt, const int32_t* tok, const int32_t* parent,
                               int n, int T, int L, int V, int32_t* acc_rows, int32_t* acc_len,
-                              int32_t* bonus, const AcceptPlan& plan, void* ws, hipStream_t st) {
+                              int32_t* bonus, const AcceptPlan& plan, void* ws, hipStream_t st,
+                              const float* gumbel, const float* temperature) {
   uint64_t* part = static_cast<uint64_t*>(ws);
   const dim3 grid(n * T, plan.S);
-  const bool aligned = (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
+  const bool sampled = gumbel != nullptr;
+  const bool aligned = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 &&
+                       (!sampled || (reinterpret_cast<uintptr_t>(gumbel) % 16) == 0);
+#define DDT_ARGMAX(TY, VEC)                                                                                       \
+  do {                                                                                                            \
+    if (sampled)                                                                                                  \
+      hipLaunchKernelGGL((argmax_partial_kernel<TY, VEC, true>), grid, dim3(256), 0, st, p, V, plan.chunk, gumbel, \
+                         temperature, T, part);                                                                   \
+    else                                                                                                          \
+      hipLaunchKernelGGL((argmax_partial_kernel<TY, VEC, false>), grid, dim3(256), 0, st, p, V, plan.chunk,        \
+                         nullptr, nullptr, T, part);                                                              \
+  } while (0)
   if (dt == DDT_BF16) {
     const uint16_t* p = static_cast<const uint16_t*>(logits);
-    if (aligned && V % 8 == 0)
-      hipLaunchKernelGGL((argmax_partial_kernel<uint16_t, 8>), grid, dim3(256), 0, st, p, V, plan.chunk, part);
-    else
-      hipLaunchKernelGGL((argmax_partial_kernel<uint16_t, 1>), grid, dim3(256), 0, st, p, V, plan.chunk, part);
+    if (aligned && V % 8 == 0) DDT_ARGMAX(uint16_t, 8);
+    else DDT_ARGMAX(uint16_t, 1);
   } else {
     const float* p = static_cast<const float*>(logits);
-    if (aligned && V % 4 == 0)
-      hipLaunchKernelGGL((argmax_partial_kernel<float, 4>), grid, dim3(256), 0, st, p, V, plan.chunk, part);
-    else
-      hipLaunchKernelGGL((argmax_partial_kernel<float, 1>), grid, dim3(256), 0, st, p, V, plan.chunk, part);
+    if (aligned && V % 4 == 0) DDT_ARGMAX(float, 4);
+    else DDT_ARGMAX(float, 1);
   }
+#undef DDT_ARGMAX
   hipLaunchKernelGGL(walk_kernel, dim3(n), dim3(64), 0, st, part, plan.S, tok, parent, T, L, acc_rows,
                      acc_len, bonus);
   return hipGetLastError();

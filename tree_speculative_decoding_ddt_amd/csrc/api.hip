@@ -331,6 +331,23 @@ int ddt_tree_accept(const void* target_logits, int dt, const int32_t* tok, const
                     "ddt_tree_accept");
 }
 
+int ddt_tree_accept_sampled(const void* target_logits, int dt, const float* gumbel, const float* temperature,
+                            const int32_t* tok, const int32_t* parent, int n, int B, int L, int V, int32_t* acc_rows,
+                            int32_t* acc_len, int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+  DDT_NEED(target_logits); DDT_NEED(gumbel); DDT_NEED(temperature); DDT_NEED(tok); DDT_NEED(parent);
+  DDT_NEED(acc_rows); DDT_NEED(acc_len); DDT_NEED(bonus); DDT_NEED(ws);
+  DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && L >= 0 && L <= 63 && V >= 1, DDT_ERR_ARG,
+            "ddt_tree_accept_sampled: need n>=1, 0<=B<=64, 0<=L<=63, V>=1 (got n=%d B=%d L=%d V=%d)", n, B, L, V);
+  DDT_CHECK(dt_ok(dt), DDT_ERR_UNSUPPORTED, "ddt_tree_accept_sampled: dtype %d", dt);
+  const ddt::AcceptPlan plan = ddt::plan_tree_accept(n, B, V);
+  DDT_CHECK(ws_bytes >= plan.total, DDT_ERR_WORKSPACE, "ddt_tree_accept_sampled: workspace %zu < %zu bytes",
+            ws_bytes, plan.total);
+  DDT_CHECK(aligned16(ws), DDT_ERR_ARG, "ddt_tree_accept_sampled: workspace not 16-byte aligned");
+  return hip_status(ddt::launch_tree_accept(target_logits, dt, tok, parent, n, B + 1, L, V, acc_rows, acc_len, bonus,
+                                            plan, ws, static_cast<hipStream_t>(stream), gumbel, temperature),
+                    "ddt_tree_accept_sampled");
+}
+
 // ---------------------------------------------------------------- commit
 static int commit_impl(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len, const ddt_kv_layer* kv,
                        int n_kv, int Hkv, int D, int Pmax, int kv_dt, const ddt_gdn_layer* gdn, int n_gdn, int H,

@@ -94,7 +94,8 @@ AcceptPlan plan_tree_accept(int n, int B, int V);
 hipError_t launch_tree_accept(const void* logits, int dt, const int32_t* tok,
                               const int32_t* parent, int n, int T, int L, int V,
                               int32_t* acc_rows, int32_t* acc_len, int32_t* bonus,
-                              const AcceptPlan& plan, void* ws, hipStream_t st);
+                              const AcceptPlan& plan, void* ws, hipStream_t st,
+                              const float* gumbel = nullptr, const float* temperature = nullptr);
 
 // ---- commit
 hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* prefix_len,

@@ -22,6 +22,7 @@ EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
            "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope", "ddt_tree_rope",
            "ddt_tree_attn_paged_workspace", "ddt_tree_attn_paged", "ddt_commit_paged",
+           "ddt_tree_accept_sampled",
            "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
            "ddt_commit", "ddt_gdn_replay")
@@ -74,6 +75,7 @@ def lib():
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_tree_attn_rope_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn_paged_workspace": (Z, [I, I, I, I, I, I, I, I]),
+        "ddt_tree_accept_sampled": (I, [P, I, P, P, P, P, I, I, I, I, P, P, P, P, Z, P]),
         "ddt_tree_rope": (I, [P, P, P, P, P, I, F, I, I, I, I, I, I, P, P, P, P]),
         "ddt_tree_attn_paged": (I, [P, P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_commit_paged": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, P, I, I, I, I,
@@ -302,6 +304,24 @@ def tree_accept(target_logits, tok, parent, L, ws=None, out=None):
         _ptr(target_logits), _dt(target_logits), _ptr(tok), _ptr(parent), n, T - 1, L, V,
         _ptr(out["acc_rows"]), _ptr(out["acc_len"]), _ptr(out["bonus"]), _ptr(w),
         w.numel() * w.element_size(), _stream(dev)))
+    return out
+
+
+def tree_accept_sampled(target_logits, gumbel, temperature, tok, parent, L, ws=None, out=None):
+    """As tree_accept with each row's target token a Gumbel-max draw: gumbel [n][T][V] f32,
+    temperature [n] f32 (<= 0: greedy)."""
+    _gpu(target_logits, gumbel, temperature, tok, parent)
+    n, T, V = target_logits.shape
+    dev = target_logits.device
+    if out is None:
+        out = {"acc_rows": torch.empty(n, L + 1, dtype=torch.int32, device=dev),
+               "acc_len": torch.empty(n, dtype=torch.int32, device=dev),
+               "bonus": torch.empty(n, dtype=torch.int32, device=dev)}
+    w = _ws(lib().ddt_tree_accept_workspace(n, T - 1, V), dev, ws)
+    _check("ddt_tree_accept_sampled", lib().ddt_tree_accept_sampled(
+        _ptr(target_logits), _dt(target_logits), _ptr(gumbel), _ptr(temperature), _ptr(tok), _ptr(parent), n, T - 1,
+        L, V, _ptr(out["acc_rows"]), _ptr(out["acc_len"]), _ptr(out["bonus"]), _ptr(w), w.numel() * w.element_size(),
+        _stream(dev)))
     return out
 
 
