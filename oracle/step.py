@@ -19,11 +19,12 @@ from . import attention as _attention
 from . import commit as _commit
 from . import gdn as _gdn
 from . import rope as _rope
+from . import sampled as _sampled
 from . import tree as _tree
 
 
 def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_logits,
-                prefix_len, Pmax, H, dk, scale=None, rope=None):
+                prefix_len, Pmax, H, dk, scale=None, rope=None, sample=None):
     """Batch of n sequences.
 
     attn_layers: list of dicts q [n][T][Hq][D], k_tree, v_tree [n][Hkv][T][D],
@@ -33,6 +34,8 @@ def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_log
                  at positions prefix_len + depth (the tree just built) and the
                  rotated k_tree / v_tree are what the attention reads and the commit
                  copies (returned as "attn_tree").
+    sample:      None for the greedy walk, or (gumbel [n][T][V], temperature [n]) for
+                 the walk over sampled target tokens.
     gdn_layers:  list of dicts x [n][T][C], v [n][T][H][dv], beta, g [n][T][H],
                  S [n][H][dv][dk], conv_state [n][W-1][C], conv_w [C][W]
     Returns a dict with the tree, per-layer outputs, the walk and the
@@ -58,8 +61,11 @@ def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_log
     gdn_out = [_gdn.gdn_tree_step_batch(lay["x"], lay["conv_w"], lay["conv_state"], lay["v"],
                                         lay["beta"], lay["g"], lay["S"], tree["parent"], H, dk)
                for lay in gdn_layers]
-    acc_rows, acc_len, bonus = _accept.tree_accept_batch(target_logits, tree["tok"],
-                                                         tree["parent"], L)
+    if sample is None:
+        acc_rows, acc_len, bonus = _accept.tree_accept_batch(target_logits, tree["tok"], tree["parent"], L)
+    else:
+        acc_rows, acc_len, bonus = _sampled.tree_accept_sampled_batch(target_logits, sample[0], sample[1],
+                                                                      tree["tok"], tree["parent"], L)
     new_prefix, new_acc = np.empty(n, np.int64), np.empty(n, np.int64)
     kv_after = [dict(k_cache=[], v_cache=[]) for _ in attn_layers]
     gdn_after = [dict(S=[], conv_state=[]) for _ in gdn_layers]

@@ -34,6 +34,12 @@ def load_inputs(step, seed, dtype):
     yt, ye = up(y, dtype)
     step.target_logits.copy_(yt)
     ex = {"z": ze, "y": ye, "attn": [], "gdn": []}
+    if c.sampled:
+        g = rng.gumbel(size=(c.n, c.T, c.V)).astype(np.float32)
+        temps = np.array([0.8, 0.0, 1.3, 2.0][: c.n] + [1.0] * max(0, c.n - 4), np.float32)
+        step.gumbel.copy_(torch.from_numpy(g))
+        step.temperature.copy_(torch.from_numpy(temps))
+        ex["sample"] = (g, temps)
     for a in step.attn:
         x = synth.attention_inputs(rng, c.n, c.T, c.Hq, c.Hkv, c.D, c.Pmax)
         if c.rope:  # the tree rows' own keys/values come token-major, before rotation
@@ -124,7 +130,8 @@ def run_rounds(cfg, dtype, seed, rounds=2, rows_only=None):
         step()
         torch.cuda.synchronize()
         ref = ostep.verify_step(ex["z"], root, cfg.B, attn_in, gdn_in,
-                                ex["y"], prefix, cfg.Pmax, cfg.H, cfg.dk, rope=cfg.rope)
+                                ex["y"], prefix, cfg.Pmax, cfg.H, cfg.dk, rope=cfg.rope,
+                                sample=ex.get("sample"))
         check_round(step, ex, ref, dtype, rows_only)
         # next round: committed buffers, grown prefix, bonus as root
         root = ref["bonus"]
@@ -198,6 +205,22 @@ def test_bf16_hybrid_step_reduced_paged_replay():
     cfg = HybridConfig(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=64, n_attn=1, n_gdn=3, replay=True,
                        page_size=32)
     run_rounds(cfg, "bf16", seed=9, rounds=2)
+
+
+def test_tiny_step_sampled_two_rounds():
+    # the walk over sampled target tokens (temperatures 0.8 and greedy), fp32
+    say("step tiny fp32 sampled")
+    cfg = HybridConfig(n=2, V=512, L=4, B=8, prefix=128, extra_cap=16, n_attn=1, n_gdn=1, Hq=2, Hkv=1, D=64,
+                       H=1, dk=32, W=4, dtype=torch.float32, sampled=True)
+    run_rounds(cfg, "f32", seed=10)
+
+
+def test_bf16_hybrid_step_reduced_all_next_paths():
+    # sampled walk + RoPE inside attention + GDN replay, at the workload's layer shapes
+    say("step bf16 hybrid reduced: sampled + rope + replay")
+    cfg = HybridConfig(n=4, V=151936, L=15, B=64, prefix=640, extra_cap=64, n_attn=1, n_gdn=2, replay=True,
+                       rope=(256, 10000.0), sampled=True)
+    run_rounds(cfg, "bf16", seed=12, rounds=2)
 
 
 def test_replay_matches_stored_commit_on_overflow():

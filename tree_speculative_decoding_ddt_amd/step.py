@@ -43,6 +43,7 @@ class HybridConfig:
     replay: bool = False       # store no per-node GDN state; the commit replays the accepted path
     rope: tuple = None         # (rot_dim, theta): attention inputs are pre-rotation, RoPE at prefix + depth
     page_size: int = 0         # > 0: the committed KV lives in pages of this many positions (block table)
+    sampled: bool = False      # the walk over sampled target tokens (gumbel noise + per-sequence temperature)
 
     def layer_pattern(self):
         if self.pattern:
@@ -121,6 +122,10 @@ class HybridVerifyStep:
                      "anc": e(n, T, dtype=torch.int64)}
         self.acc = {"acc_rows": e(n, c.L + 1, dtype=torch.int32), "acc_len": e(n, dtype=torch.int32),
                     "bonus": e(n, dtype=torch.int32)}
+        if c.sampled:
+            # the draws' noise for a round (the caller refreshes it between rounds) and temperatures
+            self.gumbel = e(n, T, c.V, dtype=torch.float32)
+            self.temperature = torch.ones(n, dtype=torch.float32, device=dev)
         u8 = lambda nb: torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         self.ws_build = u8(ddt.build_tree_workspace(n, c.L, c.V, c.B, c.K))
         assert not (c.rope and c.page_size), "RoPE inside the call is built for the contiguous cache"
@@ -187,8 +192,12 @@ class HybridVerifyStep:
                                   store_states=not self.cfg.replay)
 
     def accept(self):
-        ddt.tree_accept(self.target_logits, self.tree["tok"], self.tree["parent"], self.cfg.L,
-                        ws=self.ws_acc, out=self.acc)
+        if self.cfg.sampled:
+            ddt.tree_accept_sampled(self.target_logits, self.gumbel, self.temperature, self.tree["tok"],
+                                    self.tree["parent"], self.cfg.L, ws=self.ws_acc, out=self.acc)
+        else:
+            ddt.tree_accept(self.target_logits, self.tree["tok"], self.tree["parent"], self.cfg.L,
+                            ws=self.ws_acc, out=self.acc)
 
     def commit(self):
         kv = [(a["k_tree"], a["v_tree"], a["k_cache"], a["v_cache"]) for a in self.attn]
@@ -258,4 +267,8 @@ class HybridVerifyStep:
                     y[s, rows_d, top1[s, d]] = y[s, rows_d].amax(dim=-1) + 1.0
         self.target_logits.copy_(y)
         del y
+        if c.sampled:
+            u = ru(c.n, c.T, c.V).clamp_(1e-12, 1.0 - 1e-7)
+            self.gumbel.copy_(-torch.log(-torch.log(u)))
+            del u
         torch.cuda.synchronize(dev)
