@@ -249,8 +249,9 @@ def main():
     # accepted path on the committed state.  Reported beside the stored-state step.
     # Second variant: also RoPE at prefix + depth inside the attention call (pre-rotation
     # q and tree K/V in; rotate-half over all 256 channels, theta 10000).
-    # Third variant: the committed KV in pages of 16 positions scattered over a pool (a
-    # fresh step object with GDN replay, built after the others are released).
+    # Third variant: the committed KV in pages of 16 positions scattered over a pool and the
+    # walk over sampled target tokens (a fresh step object with GDN replay, built after the
+    # others are released; temperature 1, noise drawn once).
     variant = None
     if not a.no_variant:
         variant = {}
@@ -276,10 +277,10 @@ def main():
             time_variant(vname)
         step = None
         torch.cuda.empty_cache()
-        cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=cfg.extra_cap, replay=True, page_size=16)
+        cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=cfg.extra_cap, replay=True, page_size=16, sampled=True)
         step = HybridVerifyStep(cfg, dev)
         step.fill_random(seed=a.seed)
-        time_variant("paged16_gdn_replay")
+        time_variant("paged16_gdn_replay_sampled_walk")
 
     cpu = None
     if not a.no_cpu:
