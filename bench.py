@@ -13,7 +13,7 @@ Workload (one "step" = one verify round over the whole hot path):
 Output: one JSON line (metric, value = steps/s, per-kernel breakdown, roofline of
 the dominant kernel, tree-attention KV bandwidth, CPU-oracle baseline).
 
-    python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu] [--variants]
 """
 
 import argparse
@@ -46,7 +46,9 @@ def parse():
     ap.add_argument("--n", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--no-variant", action="store_true", help="skip the replay-on-commit variant")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the step with GDN replay, RoPE in attention, paged KV and the sampled walk "
+                         "(after the main measurement; reported under 'variants')")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -152,7 +154,7 @@ def main():
     ddt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=(3 * a.steps + a.warmup + 4) * 16 + 64)
+    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=((3 if a.variants else 1) * a.steps + a.warmup + 4) * 16 + 64)
     step = HybridVerifyStep(cfg, dev)
     step.fill_random(seed=a.seed)
     print("bench: inputs ready (%.1f GB on device)" % (torch.cuda.memory_allocated(dev) / 1e9),
@@ -253,7 +255,7 @@ def main():
     # walk over sampled target tokens (a fresh step object with GDN replay, built after the
     # others are released; temperature 1, noise drawn once).
     variant = None
-    if not a.no_variant:
+    if a.variants:
         variant = {}
 
         def time_variant(vname):

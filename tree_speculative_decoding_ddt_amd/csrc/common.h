@@ -65,6 +65,29 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Sum over aligned groups of N lanes (N in {4, 8, 16, 32}): every lane of a group ends
+// with the group's sum.  Steps inside a 16-lane row are DPP lane moves folded into the
+// adds (row rotations, half-row mirror, quad permutations), not LDS round trips; the
+// lanes of a group may differ in the last bit (each adds in its own order).
+#define DDT_DPP_F32(x, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), 0xf, 0xf, false))
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4, 8, 16 or 32 lanes");
+  if constexpr (N >= 16) {
+    x += DDT_DPP_F32(x, 0x128);  // row_ror:8
+    x += DDT_DPP_F32(x, 0x124);  // row_ror:4
+    x += DDT_DPP_F32(x, 0x122);  // row_ror:2
+    x += DDT_DPP_F32(x, 0x121);  // row_ror:1
+    if constexpr (N == 32) x += __shfl_xor(x, 16, 64);
+  } else {
+    if constexpr (N == 8) x += DDT_DPP_F32(x, 0x141);  // row_half_mirror: lane i + lane 7-i
+    x += DDT_DPP_F32(x, 0xB1);                         // quad_perm [1,0,3,2]
+    x += DDT_DPP_F32(x, 0x4E);                         // quad_perm [2,3,0,1]
+  }
+  return x;
+}
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace ddt

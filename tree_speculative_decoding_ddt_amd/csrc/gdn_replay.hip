@@ -122,8 +122,7 @@ __global__ void __launch_bounds__(256) replay_state_kernel(ReplayTable tab, cons
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) dot += st[e] * kv[e];
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    dot = group_sum<LPR>(dot);
     const size_t ti = ((size_t)s * Tn + u) * H + h;
     const float gi = g[ti], bi = beta[ti];
     const float delta = bi * (Elem<A>::load(v, ti * DV + r) - gi * dot);

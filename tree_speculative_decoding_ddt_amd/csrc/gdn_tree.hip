@@ -373,20 +373,17 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
       a += sp[e] * kv[e];
       b += sp[e] * qv[e];
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) {
-      a += __shfl_xor(a, off, 64);
-      b += __shfl_xor(b, off, 64);
-    }
-    const float gi = gb[u][0], bi = gb[u][1];
-    const float delta = bi * (vv[u][rl] - gi * a);
+    a = group_sum<LPR>(a);  // the row's LPR lanes: DPP lane moves, no LDS round trip
+    b = group_sum<LPR>(b);
+    const float gi = gb[u][0], bi = gb[u][1], kqi = gb[u][2], vi = vv[u][rl];
+    const float delta = bi * (vi - gi * a);
     const V sn = gi * sp + delta * kv;
     if (save) stk.put(d, sn);
     sprev = sn;
     dprev = d;
     const size_t ti = ((size_t)s * Tn + u) * H + h;
     if (S_scratch != nullptr) store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
-    if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * gb[u][2]);
+    if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * kqi);
   }
 }
 
