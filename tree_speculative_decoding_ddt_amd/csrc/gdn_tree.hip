@@ -414,14 +414,21 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
     hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 0>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
                        static_cast<const A*>(conv_state), static_cast<A*>(conv_scratch), parent, T, H, C, W, qk, kq, ord);
   const size_t smem = (size_t)T * 2 * DK * sizeof(float);
+  // the dynamic LDS limit is raised once per kernel, to the largest size any call uses
+  // (a host-side attribute, not a stream operation: calls stay capturable in a graph)
+  constexpr int kMaxSmem = 65 * 2 * DK * (int)sizeof(float);  // T <= 65 (B <= 64)
   if (L < 16) {
     auto kern = gdn_state_kernel<A, DK, CPT, 16>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxSmem) == hipSuccess;
+    (void)attr;
     hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
                        S_scratch, static_cast<A*>(o), ord, T, L, H);
   } else {
     auto kern = gdn_state_kernel<A, DK, 4, 32>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxSmem) == hipSuccess;
+    (void)attr;
     hipLaunchKernelGGL(kern, dim3(n * H, DK / R4), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
                        S_scratch, static_cast<A*>(o), ord, T, L, H);
   }

@@ -48,15 +48,27 @@ struct PagedKV {
   __device__ __forceinline__ size_t row(int s, int h, int Hkv, int p) const {
     return (((size_t)page(s, p) * Hkv + h) << lps) + (p & ((1 << lps) - 1));
   }
-  // the same for a wave-uniform position: the table entry comes in through a scalar
-  // load (lgkmcnt), so it does not join the vector-memory count of copies in flight
-  __device__ __forceinline__ size_t row_uniform(int s, int h, int Hkv, int p) const {
-    const int pu = __builtin_amdgcn_readfirstlane(p);
-    const int32_t* e = bt + (size_t)s * maxb + (pu >> lps);
-    int pgid;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(pgid) : "s"(e));
-    pgid = pgid < 0 ? 0 : (pgid >= npages ? npages - 1 : pgid);
-    return (((size_t)pgid * Hkv + h) << lps) + (pu & ((1 << lps) - 1));
+  // Rows of four wave-uniform positions: the four table entries come in through scalar
+  // loads (lgkmcnt, so they do not join the vector-memory count of copies in flight),
+  // all issued before one wait.
+  __device__ __forceinline__ void rows_uniform4(int s, int h, int Hkv, const int (&p)[4], size_t (&out)[4]) const {
+    const int32_t* e[4];
+    int pu[4], id[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pu[i] = __builtin_amdgcn_readfirstlane(p[i]);
+      e[i] = bt + (size_t)s * maxb + (pu[i] >> lps);
+    }
+    asm volatile(
+        "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\ts_load_dword %2, %6, 0x0\n\t"
+        "s_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
+        : "=&s"(id[0]), "=&s"(id[1]), "=&s"(id[2]), "=&s"(id[3])
+        : "s"(e[0]), "s"(e[1]), "s"(e[2]), "s"(e[3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = id[i] < 0 ? 0 : (id[i] >= npages ? npages - 1 : id[i]);
+      out[i] = (((size_t)g * Hkv + h) << lps) + (pu[i] & ((1 << lps) - 1));
+    }
   }
 };
 

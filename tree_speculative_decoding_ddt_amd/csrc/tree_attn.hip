@@ -216,14 +216,25 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     // scratch reload waits for every outstanding copy (they share vmcnt)
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    // paged: the pool rows of this wave's RPW key rows (wave-uniform scalar lookups)
+    size_t prow[RPW];
+    if constexpr (PAGED) {
+      static_assert(RPW == 4, "the paged lookup batches four rows per wave");
+      if (pre) {
+        int keys[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) keys[k] = r0 + min(wave + NW * k, rows - 1);
+        pg.rows_uniform4(s, kvh, Hkv, keys, prow);
+      }
+    }
     if (ln < LPR) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int row = wave + NW * k;
-        const int key = r0 + min(row, rows - 1);  // wave-uniform: a paged lookup is one scalar load
+        const int key = r0 + min(row, rows - 1);
         size_t e = (size_t)key * D;
         if constexpr (PAGED)
-          if (pre) e = pg.row_uniform(s, kvh, Hkv, key) * D;
+          if (pre) e = prow[k] * D;
         e += (ln ^ ((row >> 3) & 1)) * 8;
         const uint32_t m = kb + (uint32_t)(row * RS);
         dma16(Kg + e, m);
