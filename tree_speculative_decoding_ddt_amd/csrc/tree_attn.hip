@@ -38,12 +38,6 @@ constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, 
 #ifndef DDT_ATTN_PVROLL
 #define DDT_ATTN_PVROLL 1  // transposing V reads issued two blocks ahead of their products
 #endif
-#ifndef DDT_ATTN_PRIO
-#define DDT_ATTN_PRIO 1  // raise the wave priority during the MFMA phases (the other wave of the SIMD runs its softmax)
-#endif
-#ifndef DDT_ATTN_SOFTMAX_FIRST
-#define DDT_ATTN_SOFTMAX_FIRST 1  // softmax of S(it) before P.V of tile it-1 (S dies earlier)
-#endif
 constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
 
 // ------------------------------------------------------------------ scalar path
@@ -146,11 +140,13 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // s_waitcnt with vmcnt = n (0..63) and the other counters left unconstrained.
 #define DDT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// Block = 4 waves sharing one ring of K/V tiles in LDS; a wave owns NT 16-row tiles of
-// the flattened (tree row, q head) rows of one kv head.  The ring holds tile it-1
-// (its V still feeds P.V), tile it, and tiles it+1, it+2 whose copies are in flight.
-// Iteration it: S(it) = K(it) Q^T, then O += V(it-1)^T P(it-1)^T issued together with
-// the softmax of S(it), so the exp/max/sum work overlaps the matrix-core products.
+// Block = NW waves (two per SIMD) sharing one ring of K/V tiles in LDS; a wave owns NT
+// 16-row tiles of the flattened (tree row, q head) rows of one kv head.  The 4-stage
+// ring holds tile it, whose S = K Q^T, softmax and O += V^T P^T all run in iteration it,
+// and tiles it+1..it+3 whose copies are in flight (three tiles ahead keep more bytes
+// in flight than deferring tile it's P.V to the next iteration and prefetching two).
+// The two waves of a SIMD overlap one's softmax with the other's matrix-core products;
+// a wave raises its priority for its product phases.
 template <int D, int NT, int NW, int PK, int PV, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
@@ -262,13 +258,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   }
   __builtin_amdgcn_s_waitcnt(0);  // Q and masks in registers before the copy counting starts
 
-  // tile it must have landed (tile it+1 may stay in flight); the barrier also means
-  // every wave is done with iteration it-1, whose stage is refilled next
+  // tile it must have landed (tiles it+1, it+2 may stay in flight: 2*RPW copies each,
+  // completed in issue order); the barrier also means every wave is done with tile
+  // it-1, whose stage is refilled with tile it+3
   auto sync_tile = [&](int it) {
-    if (it + 1 < n_all) DDT_WAIT_VMCNT(2 * RPW);
+    if (it + 2 < n_all) DDT_WAIT_VMCNT(4 * RPW);
+    else if (it + 1 < n_all) DDT_WAIT_VMCNT(2 * RPW);
     else DDT_WAIT_VMCNT(0);
     barrier_nofence();
-    if (it + 2 < n_all) issue(it + 2);
+    if (it + 3 < n_all) issue(it + 3);
   };
 
   // per-lane LDS read bases inside a stage (K: key row 16h + l16, chunk 4*st + q4; V:
@@ -287,7 +285,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   float m[NT];    // softmax reference of the row (log2 units), fixed for a pass
   float l[NT];    // this lane's share of the row sum (8 of the row's keys per tile)
   float mxs[NT];  // largest raw score this lane has seen (sets the reference of a redo)
-  bf16x8 Pp[NT];  // P of the previous tile, B operand of its P.V product
+  bf16x8 Pp[NT];  // P of the current tile, B operand of its P.V product
 
   // S^T blocks: Sacc[j][h] lane (l16, q4) element e = key 16h + 4*q4 + e of row l16.
   // The 2*DS operand reads are issued PK ahead of the products that use them (the
@@ -426,6 +424,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   for (int pass = 0; n_all > 0; ++pass) {
     issue(0);  // every wave enters a pass with no copy in flight
     if (n_all > 1) issue(1);
+    if (n_all > 2) issue(2);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       l[j] = 0.f;
@@ -453,47 +452,30 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         }
       }
       softmax(Sacc, masked, tree, kb, kend, Pp);
+      pv_phase(0);
     }
     int it = 1;
     for (; it < n_full; ++it) {
       sync_tile(it);
       f32x4 Sacc[NT][2];
-#if DDT_ATTN_PRIO
       __builtin_amdgcn_s_setprio(1);
-#endif
       s_phase(it % NST, Sacc);
-#if DDT_ATTN_PRIO
       __builtin_amdgcn_s_setprio(0);
-#endif
-#if DDT_ATTN_SOFTMAX_FIRST
-      bf16x8 Pn[NT];  // softmax first: S dies before the P.V product, P(it) waits in Pn
-      softmax(Sacc, false, false, 0, 0, Pn);
-#if DDT_ATTN_PRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-      pv_phase((it - 1) % NST);
-#if DDT_ATTN_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-#pragma unroll
-      for (int j = 0; j < NT; ++j) Pp[j] = Pn[j];
-#else
-      pv_phase((it - 1) % NST);
       softmax(Sacc, false, false, 0, 0, Pp);
-#endif
+      __builtin_amdgcn_s_setprio(1);
+      pv_phase(it % NST);
+      __builtin_amdgcn_s_setprio(0);
     }
-    for (; it < n_all; ++it) {
+    for (; it < n_all; ++it) {  // the prefix tail and the tree tiles, under the mask
       sync_tile(it);
       const bool tree = it >= n_pre;
       const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
       const int kend = tree ? Tn : k_end;
       f32x4 Sacc[NT][2];
       s_phase(it % NST, Sacc);
-      pv_phase((it - 1) % NST);
       softmax(Sacc, true, tree, kb, kend, Pp);
+      pv_phase(it % NST);
     }
-    barrier_nofence();
-    pv_phase((n_all - 1) % NST);
     // one block-wide vote per pass: redo with references at the true row maxima
     if (__any(over)) redo_vote = pass + 1;
     __syncthreads();
