@@ -14,6 +14,7 @@ Output: one JSON line (metric, value = steps/s, per-kernel breakdown, roofline o
 the dominant kernel, tree-attention KV bandwidth, CPU-oracle baseline).
 
     python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu] [--variants]
+    python bench.py --kernel-configs      (per-config kernel figures, one JSON line each)
 """
 
 import argparse
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--n", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--kernel-configs", action="store_true",
+                    help="instead of the step line: per-config kernel figures (tree build, tree attention at "
+                         "8K/32K/128K, the full step at 16K), one JSON line each")
     ap.add_argument("--variants", action="store_true",
                     help="also time the step with GDN replay, RoPE in attention, paged KV and the sampled walk "
                          "(after the main measurement; reported under 'variants')")
@@ -121,6 +125,105 @@ def cpu_baseline(cfg, prefix):
                           cfg.n_gdn, t_step, cores))}
 
 
+def kernel_configs(a):
+    """Per-config kernel figures (tree build, tree attention at 8K/32K/128K, the full step at
+    its 16K prefix): median of 50 calls after 10 warm-up calls, each timed call preceded by a
+    512 MB write so that no input is served from the 256 MB last-level cache.  Prints one JSON
+    line per measurement; the CPU oracle time of one sequence is given beside it."""
+    import numpy as np
+    import torch
+
+    from tree_speculative_decoding_ddt_amd import ddt, synth
+    from tree_speculative_decoding_ddt_amd.step import HybridConfig, HybridVerifyStep
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(a.seed)
+    L, V, Hq, Hkv, D = 15, 151936, 24, 4, 256
+
+    def cold(fn, reps=50, warm=10):
+        for _ in range(warm):
+            fn()
+        ev = []
+        for _ in range(reps):
+            flush.fill_(1)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            ev.append((s, e))
+        torch.cuda.synchronize(dev)
+        return float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e-3  # seconds
+
+    def drafter(n):
+        z = 3.0 * torch.randn(n, L, V, generator=gen, device=dev)
+        hit = torch.rand(n, L, generator=gen, device=dev) < 0.6
+        where = torch.randint(0, V, (n, L), generator=gen, device=dev)
+        zz = z.view(-1, V)
+        rows = torch.nonzero(hit.view(-1)).flatten()
+        zz[rows, where.view(-1)[rows]] = z.amax(dim=-1).view(-1)[rows] + 8.0
+        return z.bfloat16()
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    # [1] tree build: n in {1, 16}, B in {32, 64}
+    for n in (1, 16):
+        z = drafter(n)
+        root = torch.zeros(n, dtype=torch.int32, device=dev)
+        for B in (32, 64):
+            ws = torch.empty(ddt.build_tree_workspace(n, L, V, B), dtype=torch.uint8, device=dev)
+            out = ddt.build_tree(z, B, root, ws=ws)
+            t = cold(lambda: ddt.build_tree(z, B, root, ws=ws, out=out))
+            nb = n * L * V * 2 + n * (B + 1) * 24
+            emit({"config": "tree build", "n": n, "B": B, "L": L, "V": V, "us": round(t * 1e6, 1),
+                  "GBps": round(nb / t / 1e9, 1), "hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBPS, 4)})
+    # [2] tree attention (n in {1, 8}, P in {8192, 32768}) and [3] long context (n 1, P 131072, lopsided tree)
+    cases = [(1, 8192, "random"), (8, 8192, "random"), (1, 32768, "random"), (8, 32768, "random"),
+             (1, 131072, "lopsided")]
+    for n, P, kind in cases:
+        T = 65
+        if kind == "random":
+            tree = ddt.build_tree(drafter(n), 64, torch.zeros(n, dtype=torch.int32, device=dev))
+            anc = tree["anc"]
+        else:
+            parent, _ = synth.lopsided_parents()
+            m = [0] * T
+            for i in range(1, T):
+                m[i] = m[int(parent[i])] | (1 << (i - 1))
+            anc = torch.tensor(np.array(m, dtype=np.uint64).view(np.int64), device=dev).view(1, T).repeat(n, 1)
+        rn = lambda *sh: torch.randn(*sh, generator=gen, device=dev).bfloat16()
+        q, kc, vc, kt, vt = rn(n, T, Hq, D), rn(n, Hkv, P, D), rn(n, Hkv, P, D), rn(n, Hkv, T, D), rn(n, Hkv, T, D)
+        pl = torch.full((n,), P, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(ddt.tree_attn_workspace(n, T - 1, Hq, Hkv, D, P, torch.bfloat16), 16),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        t = cold(lambda: ddt.tree_attn(q, kc, vc, pl, kt, vt, anc, ws=ws, out=o))
+        kv = n * Hkv * (P + T) * D * 2 * 2
+        fl = 4.0 * n * T * Hq * D * (P + T)
+        emit({"config": "tree attention" if P < 131072 else "long-context attention", "n": n, "P": P,
+              "tree": kind, "us": round(t * 1e6, 1), "kv_GBps": round(kv / t / 1e9, 1),
+              "kv_hbm_frac": round(kv / t / 1e9 / HBM_PEAK_GBPS, 4), "TFLOPps": round(fl / t / 1e12, 1),
+              "mfma_frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)})
+        del q, kc, vc, kt, vt, ws, o
+        torch.cuda.empty_cache()
+    # [4] the full hybrid step at its own prefix, 16384
+    cfg = HybridConfig(n=8, prefix=16384, extra_cap=(a.steps + a.warmup + 4) * 16 + 64)
+    step = HybridVerifyStep(cfg, dev)
+    step.fill_random(seed=a.seed)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / a.steps
+    emit({"config": "full hybrid verify step", "n": 8, "P": 16384, "steps_per_s": round(1.0 / dt, 3),
+          "ms_per_step": round(dt * 1e3, 3)})
+
+
 def load_traffic(name):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -138,6 +241,10 @@ def main():
               "(requested --gpus %d)" % a.gpus, file=sys.stderr)
         return 2
     import torch
+
+    if a.kernel_configs:
+        kernel_configs(a)
+        return 0
 
     if a.copy_probe:
         x = torch.empty(a.copy_probe << 20, dtype=torch.uint8, device="cuda:0")

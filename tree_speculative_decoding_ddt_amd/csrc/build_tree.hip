@@ -8,10 +8,10 @@
 // logits are not branch-conditioned, so a path's score is the sum of its log-probs.
 //
 // Kernels
-//  1. topk_partial  grid (n*L rows, S chunks).  One HBM pass: each block holds its
-//     chunk (<= 16384 logits) in registers as order-preserving integer keys, computes
-//     the chunk's (max, sum exp) and selects its exact top-K by (value desc, id asc):
-//     a lower bound from the K-th largest per-thread maximum filters the chunk, an
+//  1. topk_partial  grid (n*L rows, S chunks).  One HBM pass (16-byte loads): each block
+//     holds its chunk (<= 16384 logits) in registers as order-preserving integer keys,
+//     computes the chunk's (max, sum exp) and selects its exact top-K by (value desc, id asc):
+//     a lower bound from the per-thread maxima (per wave, by ballots) filters the chunk, an
 //     LDS radix select over the filtered keys finds the K-th value, and a second
 //     radix select over chunk offsets resolves ties at that value.
 //  2. topk_merge    grid (n*L).  Bitonic-sorts the S*K chunk candidates as 64-bit
@@ -70,7 +70,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
   }
 }
 
-template <typename T, int KBITS>
+template <typename T, int KBITS, bool VECLOAD>
 __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __restrict__ logits, int V, int chunk,
                                                                     int K, float* __restrict__ cval,
                                                                     int32_t* __restrict__ cid,
@@ -83,32 +83,66 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   const T* p = logits + (size_t)row * V + beg;
 
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t tmaxs[kTopkThreads];
+  __shared__ uint32_t tmaxs[kTopkThreads / 64];
   __shared__ uint32_t sel[3];
-  __shared__ uint32_t tau_s;
   __shared__ float2 red[kTopkThreads / 64];
   __shared__ int out_cnt;
 
-  // 1. load the chunk as keys; online (max, sum exp)
+  // chunk offset of register j: element-wise, or VEC consecutive elements per 16-byte load
+  constexpr int VEC = 16 / (int)sizeof(T);
+  auto elem = [&](int j) -> int {
+    if constexpr (VECLOAD) return VEC * (tid + kTopkThreads * (j / VEC)) + (j % VEC);
+    else return tid + kTopkThreads * j;
+  };
+
+  // 1. load the chunk as keys (exact: KBITS is the width of T), per-thread max key
   uint32_t key[kEmax];
-  float m = -INFINITY, sum = 0.f;
   uint32_t tmax = 0;
+  if constexpr (VECLOAD) {
+    // the chunk start and the row are 16-byte aligned (V and the chunk length are multiples of VEC)
 #pragma unroll
-  for (int j = 0; j < kEmax; ++j) {
-    const int e = tid + kTopkThreads * j;
-    uint32_t k = 0;
-    if (e < cnt) {
-      const float v = Elem<T>::load(p, e);
-      k = float_key(v) >> (32 - KBITS);
-      if (v > m) {
-        sum = sum * __expf(m - v) + 1.f;
-        m = v;
-      } else if (v != -INFINITY) {
-        sum += __expf(v - m);
+    for (int jv = 0; jv < kEmax / VEC; ++jv) {
+      const int e0 = VEC * (tid + kTopkThreads * jv);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (e0 + VEC <= cnt) w = *reinterpret_cast<const uint4*>(p + e0);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const int e = e0 + i;
+        float v;
+        if constexpr (sizeof(T) == 2) v = bf16_to_f32(static_cast<uint16_t>(i & 1 ? u[i >> 1] >> 16 : u[i >> 1] & 0xffffu));
+        else v = __uint_as_float(u[i]);
+        if (e0 + VEC > cnt && e < cnt) v = Elem<T>::load(p, e);  // ragged end of the chunk
+        const uint32_t k = e < cnt ? float_key(v) >> (32 - KBITS) : 0u;
+        key[jv * VEC + i] = k;
+        tmax = k > tmax ? k : tmax;
       }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kEmax; ++j) {
+      const int e = elem(j);
+      const uint32_t k = e < cnt ? float_key(Elem<T>::load(p, e)) >> (32 - KBITS) : 0u;
+      key[j] = k;
       tmax = k > tmax ? k : tmax;
     }
-    key[j] = k;
+  }
+  // the value of a key: the dropped low bits of a 16-bit key are zeros for a positive
+  // value and ones for a negative one (the key of a negative value is its complement)
+  auto kval = [](uint32_t k) {
+    uint32_t kf = k << (32 - KBITS);
+    if (KBITS < 32 && !(kf & 0x80000000u)) kf |= (1u << (32 - KBITS)) - 1u;
+    return key_float(kf);
+  };
+  // this thread's (max, sum exp): the max from the largest key, then one exp per element
+  float m = -INFINITY, sum = 0.f;
+  if (tmax != 0) {
+    m = kval(tmax);
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kEmax; ++j)
+        if (elem(j) < cnt) sum += __expf(kval(key[j]) - m);
+    }
   }
   // (max, sum) over the block
 #pragma unroll
@@ -119,7 +153,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
     m = mm;
   }
   if (lane == 0) red[wave] = make_float2(m, sum);
-  tmaxs[tid] = tmax;
   __syncthreads();
   if (tid == 0) {
     float mm = red[0].x, ss = red[0].y;
@@ -132,17 +165,24 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
     stat[(size_t)row * S + c] = make_float2(mm, ss);
   }
 
-  // 2. lower bound: the keff-th largest per-thread maximum
+  // 2. lower bound: each wave finds the c-th largest of its 64 per-thread maxima
+  // (c = ceil(keff / waves)) bit by bit with ballots; the smallest of the waves' values
+  // is a bound that at least keff thread maxima, hence at least keff keys, reach
   {
-    uint32_t rank = 0;
-    for (int u = 0; u < kTopkThreads; ++u) {
-      const uint32_t o = tmaxs[u];
-      rank += (o > tmax) || (o == tmax && u < tid);
+    constexpr int NWV = kTopkThreads / 64;
+    const uint32_t c = (uint32_t)((keff + NWV - 1) / NWV);
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = KBITS - 1; b >= 0; --b) {
+      const uint32_t cand = t | (1u << b);
+      if ((uint32_t)__popcll(__ballot(tmax >= cand)) >= c) t = cand;
     }
-    if ((int)rank == keff - 1) tau_s = tmax;
+    if (lane == 0) tmaxs[wave] = t;
   }
   __syncthreads();
-  const uint32_t tau = tau_s;
+  uint32_t tau = tmaxs[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / 64; ++w) tau = tmaxs[w] < tau ? tmaxs[w] : tau;
 
   // 3. radix select of the keff-th largest key among keys >= tau
   uint32_t prefix = 0, pmask = 0, need = keff, count_eq = 0;
@@ -153,7 +193,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
 #pragma unroll
     for (int j = 0; j < kEmax; ++j) {
       const uint32_t k = key[j];
-      if (tid + kTopkThreads * j < cnt && k >= tau && (k & pmask) == prefix)
+      if (elem(j) < cnt && k >= tau && (k & pmask) == prefix)
         atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -177,7 +217,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kEmax; ++j) {
-        const uint32_t e = tid + kTopkThreads * j;
+        const uint32_t e = elem(j);
         if ((int)e < cnt && key[j] == kth && (e & msk2) == pre2) atomicAdd(&hist[(e >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -196,7 +236,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   const size_t base = ((size_t)row * S + c) * K;
 #pragma unroll
   for (int j = 0; j < kEmax; ++j) {
-    const uint32_t e = tid + kTopkThreads * j;
+    const uint32_t e = elem(j);
     const uint32_t k = key[j];
     if ((int)e < cnt && (k > kth || (k == kth && e <= off_th))) {
       const int pos = atomicAdd(&out_cnt, 1);
@@ -280,7 +320,11 @@ __device__ __forceinline__ uint64_t slot_key(const Slot& s) {
   return (static_cast<uint64_t>(float_key(s.score)) << 32) | lo;
 }
 
-// One wavefront per sequence.  T = B+1 <= 65, frontier <= B+1 <= 65 entries.
+// One wavefront per sequence.  T = B+1 <= 65, frontier <= B+1 <= 65 entries.  Every
+// step of a pop is lane-local, a DPP move or a scalar read of one lane (readlane): the
+// wave-wide max of the frontier keys, the winner's fields, and the parent's score and
+// mask (node i's are kept by lane i mod 64, slot i / 64).  The wave needs no barrier: it
+// reads LDS only for the per-depth candidates, which are fixed before the walk.
 __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restrict__ top_id,
                                                          const float* __restrict__ top_lp, int L, int K,
                                                          int T, const int32_t* __restrict__ root_token,
@@ -291,8 +335,6 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   extern __shared__ uint8_t smem[];
   float* lp = reinterpret_cast<float*>(smem);                  // [L][K]
   int32_t* ids = reinterpret_cast<int32_t*>(lp + L * K);       // [L][K]
-  __shared__ float nscore[128];
-  __shared__ uint64_t nanc[128];
   for (int i = lane; i < L * K; i += 64) {
     lp[i] = top_lp[(size_t)s * L * K + i];
     ids[i] = top_id[(size_t)s * L * K + i];
@@ -305,40 +347,59 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
     score[ob + i] = (i == 0) ? 0.f : -INFINITY;
     anc[ob + i] = 0;
   }
-  if (lane == 0) {
-    nscore[0] = 0.f;
-    nanc[0] = 0;
-  }
   __syncthreads();
+
+  // built nodes: score and ancestor mask of node i held by lane i & 63, slot i >> 6
+  float nsc0 = 0.f, nsc1 = 0.f;
+  uint64_t nan0 = 0ull, nan1 = 0ull;
+  auto node_score = [&](int i) {
+    const float v = (i >> 6) ? nsc1 : nsc0;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i & 63));
+  };
+  auto node_anc = [&](int i) { return readlane_u64((i >> 6) ? nan1 : nan0, i & 63); };
 
   Slot s0, s1;  // this lane's frontier slots: index lane and 64 + lane
   s0.valid = s1.valid = false;
   int nslots = 0;
+  // (fields assigned one by one: a reference chosen at run time would put both slots in
+  // scratch memory)
   auto put = [&](int idx, float sc, int tk, int pr, int dp, int rk) {
     if ((idx & 63) == lane) {
-      Slot& d = (idx >> 6) ? s1 : s0;
-      d.score = sc; d.tok = tk; d.par = pr; d.dep = dp; d.rank = rk; d.valid = true;
+      if (idx >> 6) {
+        s1.score = sc; s1.tok = tk; s1.par = pr; s1.dep = dp; s1.rank = rk; s1.valid = true;
+      } else {
+        s0.score = sc; s0.tok = tk; s0.par = pr; s0.dep = dp; s0.rank = rk; s0.valid = true;
+      }
     }
   };
   if (T > 1 && L >= 1 && ids[0] >= 0) put(nslots++, 0.f + lp[0], ids[0], 0, 1, 0);
 
   for (int i = 1; i < T; ++i) {
     const uint64_t k0 = slot_key(s0), k1 = slot_key(s1);
-    const uint64_t best = wave_max_u64(k0 > k1 ? k0 : k1);
+    const uint64_t best = wave_max_u64_uniform(k0 > k1 ? k0 : k1);
     if (best == 0) break;
     const uint64_t b0 = __ballot(k0 == best && k0 != 0), b1 = __ballot(k1 == best && k1 != 0);
     const int j = b0 ? 0 : 1;
-    const int owner = (int)__ffsll((unsigned long long)(b0 ? b0 : b1)) - 1;
+    const int owner = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)(b0 ? b0 : b1)) - 1);
     const int idx = 64 * j + owner;
-    const Slot w = j ? s1 : s0;
-    const float sc = __shfl(w.score, owner, 64);
-    const int tk = __shfl(w.tok, owner, 64), pr = __shfl(w.par, owner, 64);
-    const int dp = __shfl(w.dep, owner, 64), rk = __shfl(w.rank, owner, 64);
-    const uint64_t a = nanc[pr] | (1ull << (i - 1));
+    const float wsc = j ? s1.score : s0.score;
+    const int wtk = j ? s1.tok : s0.tok, wpr = j ? s1.par : s0.par, wdp = j ? s1.dep : s0.dep;
+    const int wrk = j ? s1.rank : s0.rank;
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsc), owner));
+    const int tk = __builtin_amdgcn_readlane(wtk, owner), pr = __builtin_amdgcn_readlane(wpr, owner);
+    const int dp = __builtin_amdgcn_readlane(wdp, owner), rk = __builtin_amdgcn_readlane(wrk, owner);
+    const uint64_t a = node_anc(pr) | (1ull << (i - 1));
     if (lane == 0) {
       tok[ob + i] = tk; parent[ob + i] = pr; depth[ob + i] = dp; score[ob + i] = sc; anc[ob + i] = a;
-      nscore[i] = sc;
-      nanc[i] = a;
+    }
+    if (lane == (i & 63)) {
+      if (i >> 6) {
+        nsc1 = sc;
+        nan1 = a;
+      } else {
+        nsc0 = sc;
+        nan0 = a;
+      }
     }
     // the popped slot takes the next-ranked sibling, or empties
     if (lane == owner) {
@@ -347,10 +408,9 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
     }
     const int r2 = rk + 1;
     if (r2 < K && ids[(dp - 1) * K + r2] >= 0)
-      put(idx, nscore[pr] + lp[(dp - 1) * K + r2], ids[(dp - 1) * K + r2], pr, dp, r2);
+      put(idx, node_score(pr) + lp[(dp - 1) * K + r2], ids[(dp - 1) * K + r2], pr, dp, r2);
     // the best child goes to a fresh slot
     if (dp < L && ids[dp * K] >= 0) put(nslots++, sc + lp[dp * K], ids[dp * K], i, dp + 1, 0);
-    __syncthreads();
   }
 }
 
@@ -362,6 +422,10 @@ BuildPlan plan_build_tree(int n, int L, int V, int B, int K) {
   const int smax_len = V / 2048 > 1 ? V / 2048 : 1;
   if (want > S) S = want < smax_len ? want : (smax_len > S ? smax_len : S);
   if (S * K > kSortMax) S = kSortMax / K;
+  // the merge sorts S*K candidates; above 1024 its cost outgrows what more chunks save
+  // in the scan, so stay at 1024 when the chunk size allows
+  const int smin = cdiv(V, kChunkMax);
+  if (S * K > 1024 && smin * K <= 1024) S = 1024 / K > smin ? 1024 / K : smin;
   p.chunk = (cdiv(V, S) + 7) / 8 * 8;
   p.S = cdiv(V, p.chunk);
   int sn = 1;
@@ -389,12 +453,19 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
   int32_t* tid = reinterpret_cast<int32_t*>(w + plan.off_tid);
   float* tlp = reinterpret_cast<float*>(w + plan.off_tlp);
   const dim3 g1(n * L, plan.S);
-  if (dt == DDT_BF16)
-    hipLaunchKernelGGL((topk_partial_kernel<uint16_t, 16>), g1, dim3(kTopkThreads), 0, st,
-                       static_cast<const uint16_t*>(logits), V, plan.chunk, plan.K, cval, cid, stat);
-  else
-    hipLaunchKernelGGL((topk_partial_kernel<float, 32>), g1, dim3(kTopkThreads), 0, st,
-                       static_cast<const float*>(logits), V, plan.chunk, plan.K, cval, cid, stat);
+  const int vec = dt == DDT_BF16 ? 8 : 4;
+  const bool vload = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 && V % vec == 0 && plan.chunk % vec == 0;
+#define DDT_TOPK(TY, KB, VL)                                                                                     \
+  hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL>), g1, dim3(kTopkThreads), 0, st, static_cast<const TY*>(logits), \
+                     V, plan.chunk, plan.K, cval, cid, stat)
+  if (dt == DDT_BF16) {
+    if (vload) DDT_TOPK(uint16_t, 16, true);
+    else DDT_TOPK(uint16_t, 16, false);
+  } else {
+    if (vload) DDT_TOPK(float, 32, true);
+    else DDT_TOPK(float, 32, false);
+  }
+#undef DDT_TOPK
   hipLaunchKernelGGL(topk_merge_kernel, dim3(n * L), dim3(256), 0, st, cval, cid, stat, plan.S, plan.K,
                      plan.sortN, tid, tlp);
   const size_t smem = (size_t)L * plan.K * (sizeof(float) + sizeof(int32_t));

@@ -88,6 +88,31 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Wave-uniform maximum of a 64-bit value over all 64 lanes: DPP row rotations inside each
+// 16-lane row, then the four row maxima read as scalars (no LDS round trip).
+#define DDT_DPP_U32(x, ctrl) static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), (ctrl), 0xf, 0xf, false))
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_uniform(uint64_t v) {
+#define DDT_MAX_STEP(ctrl)                                                                              \
+  {                                                                                                     \
+    const uint64_t w = (static_cast<uint64_t>(DDT_DPP_U32(static_cast<uint32_t>(v >> 32), ctrl)) << 32) | \
+                       DDT_DPP_U32(static_cast<uint32_t>(v), ctrl);                                      \
+    v = w > v ? w : v;                                                                                  \
+  }
+  DDT_MAX_STEP(0x128)  // row_ror:8
+  DDT_MAX_STEP(0x124)  // row_ror:4
+  DDT_MAX_STEP(0x122)  // row_ror:2
+  DDT_MAX_STEP(0x121)  // row_ror:1
+#undef DDT_MAX_STEP
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16), c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace ddt
