@@ -104,6 +104,14 @@ def test_bf16_full_size_sampled(n, P):
     run_case(40 + n + P, n, 64, 15, 24, 4, 256, P + 64, [P] * n, "bf16", rows=lambda p: sample_rows(p)[:6])
 
 
+def test_bf16_bench_launch_configuration_sampled():
+    # the launch the step benchmark times: 8 sequences at a prefix that has grown past
+    # 32768 in a cache of 33104 rows (four splits of 8288 keys, the last one ragged)
+    say("tree_attn bf16 n=8 P=32790 Pmax=33104 (sampled rows)")
+    run_case(91, 8, 64, 15, 24, 4, 256, 33104, [32790 + s for s in range(8)], "bf16",
+             rows=lambda p: sample_rows(p)[:4])
+
+
 def test_bf16_long_context_lopsided():
     say("tree_attn bf16 P=131072 lopsided tree (sampled rows)")
     rows = [0, 2, 15, 16, 64]
