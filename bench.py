@@ -129,7 +129,8 @@ def kernel_configs(a):
     """Per-config kernel figures (tree build, tree attention at 8K/32K/128K, the full step at
     its 16K prefix): median of 50 calls after 10 warm-up calls, each timed call preceded by a
     512 MB write so that no input is served from the 256 MB last-level cache.  Prints one JSON
-    line per measurement; the CPU oracle time of one sequence is given beside it."""
+    line per measurement; for n = 1 the CPU oracle's time on the same shapes is given beside
+    it (one sequence, float64 NumPy on the host cores; skipped with --no-cpu)."""
     import numpy as np
     import torch
 
@@ -168,6 +169,27 @@ def kernel_configs(a):
     def emit(rec):
         print(json.dumps(rec), flush=True)
 
+    def cpu_baseline_seconds(kind, **k):
+        """The CPU oracle on one sequence of the config (the same workload shapes)."""
+        if a.no_cpu:
+            return None
+        from oracle import attention as oattn
+        from oracle import tree as otree
+        rng = np.random.default_rng(1)
+        z = synth.quantize(synth.draft_logits(rng, 1, L, V, 3.0, plant_p=0.6), "bf16")[1][0]
+        if kind == "build":
+            t0 = time.perf_counter()
+            otree.build_tree(z, k["B"], 0)
+            return time.perf_counter() - t0
+        P = k["P"]
+        tree = otree.build_tree(z, 64, 0)
+        anc = tree["anc"] if k["tree"] == "random" else k["anc"]
+        x = synth.attention_inputs(rng, 1, 65, Hq, Hkv, D, P)
+        x = {kk: synth.quantize(v, "bf16")[1][0] for kk, v in x.items()}
+        t0 = time.perf_counter()
+        oattn.tree_attention(x["q"], x["k_cache"], x["v_cache"], P, x["k_tree"], x["v_tree"], anc)
+        return time.perf_counter() - t0
+
     # [1] tree build: n in {1, 16}, B in {32, 64}
     for n in (1, 16):
         z = drafter(n)
@@ -177,8 +199,10 @@ def kernel_configs(a):
             out = ddt.build_tree(z, B, root, ws=ws)
             t = cold(lambda: ddt.build_tree(z, B, root, ws=ws, out=out))
             nb = n * L * V * 2 + n * (B + 1) * 24
+            oc = cpu_baseline_seconds("build", B=B) if n == 1 else None
             emit({"config": "tree build", "n": n, "B": B, "L": L, "V": V, "us": round(t * 1e6, 1),
-                  "GBps": round(nb / t / 1e9, 1), "hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBPS, 4)})
+                  "GBps": round(nb / t / 1e9, 1), "hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBPS, 4),
+                  "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3)})
     # [2] tree attention (n in {1, 8}, P in {8192, 32768}) and [3] long context (n 1, P 131072, lopsided tree)
     cases = [(1, 8192, "random"), (8, 8192, "random"), (1, 32768, "random"), (8, 32768, "random"),
              (1, 131072, "lopsided")]
@@ -193,6 +217,7 @@ def kernel_configs(a):
             for i in range(1, T):
                 m[i] = m[int(parent[i])] | (1 << (i - 1))
             anc = torch.tensor(np.array(m, dtype=np.uint64).view(np.int64), device=dev).view(1, T).repeat(n, 1)
+        anc_np = None if kind == "random" else np.array(m, dtype=np.uint64)
         rn = lambda *sh: torch.randn(*sh, generator=gen, device=dev).bfloat16()
         q, kc, vc, kt, vt = rn(n, T, Hq, D), rn(n, Hkv, P, D), rn(n, Hkv, P, D), rn(n, Hkv, T, D), rn(n, Hkv, T, D)
         pl = torch.full((n,), P, dtype=torch.int32, device=dev)
@@ -202,11 +227,14 @@ def kernel_configs(a):
         t = cold(lambda: ddt.tree_attn(q, kc, vc, pl, kt, vt, anc, ws=ws, out=o))
         kv = n * Hkv * (P + T) * D * 2 * 2
         fl = 4.0 * n * T * Hq * D * (P + T)
+        del q, kc, vc, kt, vt, ws, o
+        torch.cuda.empty_cache()
+        oc = cpu_baseline_seconds("attn", P=P, tree=kind, anc=anc_np) if n == 1 else None
         emit({"config": "tree attention" if P < 131072 else "long-context attention", "n": n, "P": P,
               "tree": kind, "us": round(t * 1e6, 1), "kv_GBps": round(kv / t / 1e9, 1),
               "kv_hbm_frac": round(kv / t / 1e9 / HBM_PEAK_GBPS, 4), "TFLOPps": round(fl / t / 1e12, 1),
-              "mfma_frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)})
-        del q, kc, vc, kt, vt, ws, o
+              "mfma_frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+              "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3)})
         torch.cuda.empty_cache()
     # [4] the full hybrid step at its own prefix, 16384
     cfg = HybridConfig(n=8, prefix=16384, extra_cap=(a.steps + a.warmup + 4) * 16 + 64)
