@@ -35,9 +35,6 @@ constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
 constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
 constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, O) partials of a
                                      // split cost about as much traffic as 400 keys of K/V
-#ifndef DDT_ATTN_PVROLL
-#define DDT_ATTN_PVROLL 1  // transposing V reads issued two blocks ahead of their products
-#endif
 constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
 
 // ------------------------------------------------------------------ scalar path
@@ -147,7 +144,7 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // in flight than deferring tile it's P.V to the next iteration and prefetching two).
 // The two waves of a SIMD overlap one's softmax with the other's matrix-core products;
 // a wave raises its priority for its product phases.
-template <int D, int NT, int NW, int PK, int PV, bool PAGED>
+template <int D, int NT, int NW, int PK, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
                                                            const uint16_t* __restrict__ v_cache,
@@ -313,10 +310,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     }
   };
   // O^T += V^T P^T: A = V^T (d = 16b + l16; keys 4*q4 + 0..3, then 16 + 4*q4 + 0..3),
-  // two transposing reads per block issued PV blocks ahead of their products
+  // two transposing reads per block, issued two blocks ahead of their products
   auto pv_phase = [&](int stage) {
     const uint8_t* Vs = lds + stage * 2 * TILE;
-#if DDT_ATTN_PVROLL
     // rolling prefetch: the transposing reads of block b+2 are issued before the
     // products of block b (a sched_barrier after each block keeps that order)
     s16x4 lo[3], hi[3];
@@ -337,27 +333,6 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pp[j], O[j][b], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-#else
-    bf16x8 Vop[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[0] + 32 * b));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + vbase[1] + 32 * b));
-      Vop[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vop[b], Pp[j], O[j][b], 0, 0, 0);
-    if constexpr (PV > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV, 1);
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NT, 1);
-        if (b + PV < DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-    }
-#endif
   };
   // ancestor mask of this lane's row in tile j (tree tiles only: read when needed)
   auto anc_row = [&](int j) -> uint64_t {
@@ -567,9 +542,6 @@ __global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __rest
 #ifndef DDT_ATTN_PK
 #define DDT_ATTN_PK 4  // K operand reads pinned ahead of their products (0: scheduler's order)
 #endif
-#ifndef DDT_ATTN_PV
-#define DDT_ATTN_PV 0  // V operand blocks pinned ahead of their products (0: scheduler's order)
-#endif
 constexpr int attn_nt(int D) { return D == 256 ? DDT_ATTN_NT256 : DDT_ATTN_NT128; }
 constexpr int attn_nw(int D) { return D == 256 ? DDT_ATTN_NW256 : DDT_ATTN_NW128; }
 
@@ -641,7 +613,7 @@ hipError_t launch_tree_attn(const void* q, const void* k_cache, const void* v_ca
   const auto* vt = static_cast<const uint16_t*>(v_tree);
   auto* o16 = static_cast<uint16_t*>(out);
 #define DDT_MFMA(DD, PG)                                                                                     \
-  hipLaunchKernelGGL((attn_mfma_kernel<DD, attn_nt(DD), attn_nw(DD), DDT_ATTN_PK, DDT_ATTN_PV, PG>), grid,      \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, attn_nt(DD), attn_nw(DD), DDT_ATTN_PK, PG>), grid,      \
                      dim3(64 * attn_nw(DD)), 0, st, qq, kc, vc, prefix_len, kt, vt, anc, T, Hq, Hkv, Pmax, sl2, \
                      plan.nwg, plan.nsplit, plan.split_len, plan.units, pg, part_lse, part_o, o16)
   if (D == 256) {
