@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -58,9 +59,17 @@ def parse():
     return ap.parse_args()
 
 
+def code_hash(text):
+    """Hash of a kernel source's code: comments and white space are left out, so that an
+    edit of a comment keeps the counter figures taken on the same code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def src_hash(name):
     path = os.path.join(ROOT, "tree_speculative_decoding_ddt_amd", "csrc", KERNEL_SOURCES[name])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return code_hash(open(path).read())
 
 
 def algorithmic(cfg, prefix_now):

@@ -13,9 +13,10 @@
 //                   each lane then holds 8 scores of ONE query row,
 //     online softmax in the log2 domain (fp32),
 //     O^T += V^T P^T  A = V^T from LDS, B = P straight from the score registers.
-//   Keys are the MFMA contraction index of the second product, so their order is
-//   free: V is written transposed into LDS with keys permuted so that the 8 keys a
-//   lane holds are the 8 contiguous bf16 the A operand reads (one ds_read_b128).
+//   Keys are the contraction index of the second product and V sits in LDS key-major
+//   as copied, so each A operand (8 keys of one column d) comes from two transposing
+//   reads (ds_read_b64_tr_b16), keys 4*q4..+3 and 16+4*q4..+3: the same key order in
+//   which S^T leaves a lane's 8 scores, so P feeds the B operand straight from them.
 //   The prefix is split across blocks (split-K); one extra split handles the T tree
 //   keys under the ancestor mask.  Each split writes (lse, O/l) per row and a combine
 //   kernel merges them with log-sum-exp weights.
