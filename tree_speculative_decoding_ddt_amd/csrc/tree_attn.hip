@@ -8,10 +8,11 @@
 // bf16, D in {128, 256}: matrix-core path.
 //   Rows of one kv head are the G = Hq/Hkv query heads of all T tree rows, flattened
 //   r = t*G + h_local and cut into 16-row tiles; a wave owns up to NT tiles, a block
-//   (4 waves) shares one 32-key K/V tile in LDS.  Per 32 keys:
+//   (NW = 8 waves) shares each 32-key K/V tile in LDS.  Per 32 keys:
 //     S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q from VGPRs;
 //                   each lane then holds 8 scores of ONE query row,
-//     online softmax in the log2 domain (fp32),
+//     softmax in the log2 domain (fp32) against a reference fixed for the pass
+//                   (a pass is redone once if a score overshoots it),
 //     O^T += V^T P^T  A = V^T from LDS, B = P straight from the score registers.
 //   Keys are the contraction index of the second product and V sits in LDS key-major
 //   as copied, so each A operand (8 keys of one column d) comes from two transposing
@@ -226,13 +227,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       for (int k = 0; k < RPW; ++k) {
         const int row = wave + NW * k;
         const int key = r0 + min(row, rows - 1);
-        size_t e = (size_t)key * D;
+        size_t e = (size_t)key * D;  // wave-uniform row start
         if constexpr (PAGED)
           if (pre) e = prow[k] * D;
-        e += (ln ^ ((row >> 3) & 1)) * 8;
+        const uint32_t voff = (uint32_t)(ln ^ ((row >> 3) & 1)) << 4;  // this lane's 16-byte chunk
         const uint32_t m = kb + (uint32_t)(row * RS);
-        dma16(Kg + e, m);
-        dma16(Vg + e, m + TILE);
+        dma16(reinterpret_cast<const uint8_t*>(Kg + e) + voff, m);
+        dma16(reinterpret_cast<const uint8_t*>(Vg + e) + voff, m + TILE);
       }
     }
   };
@@ -282,7 +283,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   f32x4 O[NT][DB];
   float m[NT];    // softmax reference of the row (log2 units), fixed for a pass
   float l[NT];    // this lane's share of the row sum (8 of the row's keys per tile)
-  float mxs[NT];  // largest raw score this lane has seen (sets the reference of a redo)
+  float mxs[NT];  // largest exponent argument (score in log2 units - m) of the pass (sets a redo's m)
   bf16x8 Pp[NT];  // P of the current tile, B operand of its P.V product
 
   // S^T blocks: Sacc[j][h] lane (l16, q4) element e = key 16h + 4*q4 + e of row l16.
@@ -356,23 +357,28 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         sv[4 * h + e] = x;
       }
   };
-  // P = 2^(score*scale*log2e - m) against the fixed reference; `over` marks a score more
-  // than kOver above it (P could overflow: the pass is redone with a larger reference)
+  // P = 2^(score*scale*log2e - m) against the fixed reference; `over` marks an exponent
+  // above kOver (P could overflow: the pass is redone with a larger reference)
   bool over = false;
   auto softmax = [&](const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend, bf16x8 (&Pout)[NT]) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       float sv[8];
       scores(Sacc, j, masked, tree, kb, kend, sv);
-      float mx = sv[0];
+      // the exponent arguments: results of arithmetic, so their maximum needs no NaN
+      // canonicalisation of the raw matrix-core outputs
+      float a[8];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      for (int e = 0; e < 8; ++e) a[e] = fmaf(sv[e], sl2, -m[j]);
+      float mx = a[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, a[e]);
       mxs[j] = fmaxf(mxs[j], mx);
-      over = over || (mx * sl2 > m[j] + kOver);
+      over |= mx > kOver;
       float r = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -m[j]));
+        const float p = __builtin_amdgcn_exp2f(a[e]);
         r += p;
         Pout[j][e] = static_cast<__bf16>(p);
       }
@@ -404,6 +410,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       l[j] = 0.f;
+      mxs[j] = -INFINITY;
 #pragma unroll
       for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -460,7 +467,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     if (!redo) break;
     over = false;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) m[j] = fmaxf(m[j], row_max(mxs[j]) * sl2);
+    for (int j = 0; j < NT; ++j) m[j] += fmaxf(row_max(mxs[j]), 0.f);
   }
   // every wave reaches this point with no copy in flight (the last sync waited for all)
 
