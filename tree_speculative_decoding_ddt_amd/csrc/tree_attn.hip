@@ -35,8 +35,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
 constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
-constexpr int kAttnMinSplit = 1024;  // fewest prefix keys per split: the (lse, O) partials of a
-                                     // split cost about as much traffic as 400 keys of K/V
+constexpr int kAttnMinSplit = 512;  // fewest prefix keys per split: a split's (lse, O) partials
+                                    // cost about the traffic of 400 keys of K/V, but with few
+                                    // sequences more splits fill more of the 256 CUs
 constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
 
 // ------------------------------------------------------------------ scalar path
