@@ -101,7 +101,7 @@ def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None):
         gd_dev.append((Ssc, S, csc, cst))
         gd_np.append(dict(S_scratch=down(Ssc), S=down(S), conv_scratch=down(csc), conv_state=down(cst)))
     pl = up_int(prefix)
-    ddt.commit(acc["acc_rows"], acc["acc_len"], pl, kv_dev, gd_dev, B=B)
+    ddt.commit(acc["acc_rows"], acc["acc_len"], pl, kv_dev, gd_dev, B=B, Pmax=Pmax)
     torch.cuda.synchronize()
     for s in range(n):
         kv_s = [{k: v[s] for k, v in lay.items()} for lay in kv_np]
@@ -125,3 +125,12 @@ def test_commit_bit_exact(dtype):
 def test_commit_many_layers_and_guards():
     # more layers than one launch carries; sequence 1 overflows Pmax; sequence 2 had a failed walk
     commit_case(2, 3, 18, 20, "bf16", np.array([5, 47, 7]), 48, acc_override=np.array([0, 0, -1]))
+
+
+def test_commit_without_kv_layers():
+    # GDN layers only: the prefix capacity must be stated, else the call refuses
+    commit_case(3, 4, 0, 2, "f32", np.array([61, 15, 60, 50]), 68)
+    commit_case(4, 2, 0, 0, "bf16", np.array([3, 9]), 10)
+    z = up_int(np.zeros((1, 2), dtype=np.int64))
+    with pytest.raises(ValueError, match="Pmax"):
+        ddt.commit(z, up_int(np.zeros(1, dtype=np.int64)), up_int(np.zeros(1, dtype=np.int64)), (), (), B=1)

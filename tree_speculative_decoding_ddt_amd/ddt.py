@@ -325,22 +325,26 @@ def tree_accept_sampled(target_logits, gumbel, temperature, tok, parent, L, ws=N
     return out
 
 
-def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None, block_table=None):
+def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None, block_table=None, Pmax=None,
+           page_size=None):
     """In-place commit.  kv_layers: sequence of (k_tree, v_tree, k_cache, v_cache);
     gdn_layers: sequence of (S_scratch, S, conv_scratch, conv_state).
     With block_table [n][max_blocks] int32, k_cache / v_cache are page pools
-    [num_pages][Hkv][page_size][D] (ddt_commit_paged)."""
+    [num_pages][Hkv][page_size][D] (ddt_commit_paged).
+    The prefix capacity that guards overflow comes from the KV caches (Pmax rows, or
+    max_blocks * page_size); with no KV layer it must be given (Pmax, or page_size with
+    a block table)."""
     _gpu(acc_rows, acc_len, prefix_len)
     n, Lp1 = acc_rows.shape
     dev = acc_rows.device
     kv = (KVLayer * max(1, len(kv_layers)))()
-    Hkv = D = Pmax = 1
+    Hkv = D = 1
     kv_dt = DDT_BF16
     T = None
     for i, (kt, vt, kc, vc) in enumerate(kv_layers):
         _gpu(kt, vt, kc, vc)
         kv[i] = KVLayer(kt.data_ptr(), vt.data_ptr(), kc.data_ptr(), vc.data_ptr())
-        Hkv, D, Pmax, kv_dt, T = kc.shape[1], kc.shape[3], kc.shape[2], _dt(kc), kt.shape[2]
+        Hkv, D, kv_dt, T = kc.shape[1], kc.shape[3], _dt(kc), kt.shape[2]
     gd = (GDNLayer * max(1, len(gdn_layers)))()
     H = dk = dv = C = 1
     W = 2
@@ -356,13 +360,25 @@ def commit(acc_rows, acc_len, prefix_len, kv_layers=(), gdn_layers=(), B=None, b
         B = T - 1
     if block_table is not None:
         _gpu(block_table)
-        ps = kv_layers[0][2].shape[2] if len(kv_layers) else 1
-        num_pages = kv_layers[0][2].shape[0] if len(kv_layers) else 1
+        if len(kv_layers):
+            ps, num_pages = kv_layers[0][2].shape[2], kv_layers[0][2].shape[0]
+            if page_size is not None and page_size != ps:
+                raise ValueError("commit: page_size %d does not match the page pool's %d" % (page_size, ps))
+        elif page_size is None:
+            raise ValueError("commit: with no KV layer, give page_size (the capacity is max_blocks * page_size)")
+        else:
+            ps, num_pages = page_size, 1
         _check("ddt_commit_paged", lib().ddt_commit_paged(
             _ptr(acc_rows), _ptr(acc_len), _ptr(prefix_len), kv, len(kv_layers), Hkv, D, _ptr(block_table),
             block_table.shape[1], ps, num_pages, kv_dt, gd, len(gdn_layers), H, dk, dv, C, W, act_dt, n, B,
             Lp1 - 1, _stream(dev)))
         return
+    if len(kv_layers):
+        if Pmax is not None and Pmax != kv_layers[0][2].shape[2]:
+            raise ValueError("commit: Pmax %d does not match the cache's %d rows" % (Pmax, kv_layers[0][2].shape[2]))
+        Pmax = kv_layers[0][2].shape[2]
+    elif Pmax is None:
+        raise ValueError("commit: with no KV layer, give Pmax (the prefix capacity that guards overflow)")
     _check("ddt_commit", lib().ddt_commit(
         _ptr(acc_rows), _ptr(acc_len), _ptr(prefix_len), kv, len(kv_layers), Hkv, D, Pmax, kv_dt,
         gd, len(gdn_layers), H, dk, dv, C, W, act_dt, n, B, Lp1 - 1, _stream(dev)))
