@@ -17,6 +17,10 @@ from tests import test_gpu_accept_commit as TC
 from tests import test_gpu_attention as TA
 from tests import test_gpu_build_tree as TB
 from tests import test_gpu_gdn as TG
+from tests import test_gpu_paged as TP
+from tests import test_gpu_replay as TR
+from tests import test_gpu_rope as TRo
+from tests import test_gpu_sampled as TS
 from tests.gpu_util import say
 from tree_speculative_decoding_ddt_amd import synth
 
@@ -37,7 +41,7 @@ def attention_shape(seed):
     return dict(n=n, B=B, L=L, Hq=G * Hkv, Hkv=Hkv, D=D, Pmax=Pmax, prefix=prefix, dtype=dtype)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(30))
 def test_attention_sweep(seed):
     c = attention_shape(seed)
     say("sweep tree_attn seed", seed, c)
@@ -51,19 +55,20 @@ def gdn_shape(seed):
                 dk=int(r.choice([32, 64, 128])), W=int(r.integers(2, 9)), dtype="f32" if seed % 2 else "bf16")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(20))
 def test_gdn_sweep(seed):
     c = gdn_shape(seed)
     say("sweep gdn_tree_step seed", seed, c)
     TG.run_case(4000 + seed, c["n"], c["B"], c["L"], c["H"], c["dk"], c["W"], c["dtype"])
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(15))
 def test_build_tree_sweep(seed):
     r = np.random.default_rng(5000 + seed)
-    n, B, L, V = int(r.integers(1, 5)), int(r.integers(1, 65)), int(r.integers(1, 16)), int(r.integers(64, 6000))
+    n, B, L, V = int(r.integers(1, 5)), int(r.integers(1, 65)), int(r.integers(1, 16)), int(r.integers(300, 6000))
     dtype = "f32" if seed % 3 == 0 else "bf16"
-    # K < B only on continuous fp32 draws (bf16 rows tie often at the K-th value)
+    # K < B only on continuous fp32 draws (bf16 rows tie often at the K-th value); vocabularies
+    # of a few dozen bf16 tokens make near-tied path sums unavoidable (the gap guard refuses them)
     K = int(r.integers(1, B + 1)) if dtype == "f32" and seed % 2 else 0
     say("sweep build_tree seed", seed, dict(n=n, B=B, L=L, V=V, K=K, dtype=dtype))
 
@@ -75,7 +80,7 @@ def test_build_tree_sweep(seed):
     TB.run_and_compare(z, dtype, B, r.integers(0, V, size=n), K=K)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(15))
 def test_accept_sweep(seed):
     r = np.random.default_rng(7000 + seed)
     n, L, V, B = int(r.integers(1, 6)), int(r.integers(1, 16)), int(r.integers(50, 20000)), int(r.integers(1, 65))
@@ -85,7 +90,7 @@ def test_accept_sweep(seed):
     TC.run_accept(t, y, L, dtype)
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(12))
 def test_commit_sweep(seed):
     r = np.random.default_rng(9000 + seed)
     n, Pmax = int(r.integers(1, 5)), int(r.integers(8, 80))
@@ -94,3 +99,43 @@ def test_commit_sweep(seed):
              dtype="f32" if seed % 2 else "bf16")
     say("sweep commit seed", seed, c)
     TC.commit_case(9100 + seed, n, c["n_kv"], c["n_gdn"], c["dtype"], prefix, Pmax)
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_paged_attention_sweep(seed):
+    c = attention_shape(100 + seed)
+    r = np.random.default_rng(11000 + seed)
+    ps = int(r.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    maxb = (c["Pmax"] + ps - 1) // ps
+    say("sweep tree_attn_paged seed", seed, dict(c, page_size=ps, max_blocks=maxb))
+    TP.run_case(12000 + seed, c["n"], c["B"], c["L"], c["Hq"], c["Hkv"], c["D"], ps, maxb, c["prefix"], c["dtype"])
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_rope_attention_sweep(seed):
+    c = attention_shape(200 + seed)
+    r = np.random.default_rng(13000 + seed)
+    rot = 16 * int(r.integers(1, c["D"] // 16 + 1))
+    theta = float(r.choice([10000.0, 500000.0]))
+    say("sweep tree_attn_rope seed", seed, dict(c, rot_dim=rot, theta=theta))
+    TRo.run_case(14000 + seed, c["n"], c["B"], c["L"], c["Hq"], c["Hkv"], c["D"], c["Pmax"], c["prefix"], c["dtype"],
+                 rot, theta)
+
+
+@pytest.mark.parametrize("seed", range(15))
+def test_replay_sweep(seed):
+    c = gdn_shape(100 + seed)
+    n_layers = int(np.random.default_rng(15000 + seed).integers(1, 21))  # past 16: two launches
+    say("sweep gdn_replay seed", seed, dict(c, n_layers=n_layers))
+    TR.run_case(16000 + seed, c["n"], c["B"], c["L"], c["H"], c["dk"], c["W"], c["dtype"], n_layers=n_layers)
+
+
+@pytest.mark.parametrize("seed", range(15))
+def test_sampled_walk_sweep(seed):
+    r = np.random.default_rng(17000 + seed)
+    n, L, V, B = int(r.integers(1, 6)), int(r.integers(1, 16)), int(r.integers(50, 20000)), int(r.integers(1, 65))
+    temps = [float(t) for t in r.choice([0.0, -1.0, 0.3, 0.7, 1.0, 1.7, 4.0], size=n)]
+    dtype = "f32" if seed % 2 else "bf16"
+    say("sweep tree_accept_sampled seed", seed, dict(n=n, L=L, V=V, B=B, temps=temps, dtype=dtype))
+    t, y, g = TS.make_case(18000 + seed, n, L, V, B, 4.0)
+    TS.run(t, y, g, temps, L, dtype)
