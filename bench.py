@@ -138,8 +138,10 @@ def kernel_configs(a):
     """Per-config kernel figures (tree build, tree attention at 8K/32K/128K, the full step at
     its 16K prefix): median of 50 calls after 10 warm-up calls, each timed call preceded by a
     512 MB write so that no input is served from the 256 MB last-level cache.  Prints one JSON
-    line per measurement; for n = 1 the CPU oracle's time on the same shapes is given beside
-    it (one sequence, float64 NumPy on the host cores; skipped with --no-cpu)."""
+    line per measurement, fractions against the nominal HBM peak and against the box's own
+    device-copy rate; for n = 1 the CPU oracle's time on the same shapes is given beside it
+    (one sequence, float64 NumPy on every host core and, except at 131072, on one BLAS
+    thread; skipped with --no-cpu)."""
     import numpy as np
     import torch
 
@@ -178,10 +180,36 @@ def kernel_configs(a):
     def emit(rec):
         print(json.dumps(rec), flush=True)
 
-    def cpu_baseline_seconds(kind, **k):
-        """The CPU oracle on one sequence of the config (the same workload shapes)."""
+    # the host and the box's own copy rate (a STREAM-style 1 GiB device-to-device copy,
+    # bytes read + written), beside the nominal HBM peak
+    model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")), "?")
+    emit({"config": "host", "cpu_model": model, "cpu_threads": len(os.sched_getaffinity(0))})
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    for _ in range(3):
+        dst.copy_(src)
+    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cs.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ce.record()
+    torch.cuda.synchronize(dev)
+    copy_gbps = 2 * src.numel() * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    emit({"config": "device copy", "bytes_per_copy": 2 << 30, "GBps": round(copy_gbps, 1),
+          "frac_of_nominal": round(copy_gbps / HBM_PEAK_GBPS, 4)})
+
+    def cpu_baseline_seconds(kind, threads=None, **k):
+        """The CPU oracle on one sequence of the config (the same workload shapes); threads
+        limits the BLAS pool (None: every host core)."""
         if a.no_cpu:
             return None
+        if threads is not None:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=threads):
+                return cpu_baseline_seconds(kind, None, **k)
         from oracle import attention as oattn
         from oracle import tree as otree
         rng = np.random.default_rng(1)
@@ -209,9 +237,12 @@ def kernel_configs(a):
             t = cold(lambda: ddt.build_tree(z, B, root, ws=ws, out=out))
             nb = n * L * V * 2 + n * (B + 1) * 24
             oc = cpu_baseline_seconds("build", B=B) if n == 1 else None
+            o1 = cpu_baseline_seconds("build", threads=1, B=B) if n == 1 else None
             emit({"config": "tree build", "n": n, "B": B, "L": L, "V": V, "us": round(t * 1e6, 1),
                   "GBps": round(nb / t / 1e9, 1), "hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBPS, 4),
-                  "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3)})
+                  "copy_frac": round(nb / t / 1e9 / copy_gbps, 4),
+                  "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3),
+                  "cpu_oracle_s_per_seq_1thread": None if o1 is None else round(o1, 3)})
     # [2] tree attention (n in {1, 8}, P in {8192, 32768}) and [3] long context (n 1, P 131072, lopsided tree)
     cases = [(1, 8192, "random"), (8, 8192, "random"), (1, 32768, "random"), (8, 32768, "random"),
              (1, 131072, "lopsided")]
@@ -239,11 +270,13 @@ def kernel_configs(a):
         del q, kc, vc, kt, vt, ws, o
         torch.cuda.empty_cache()
         oc = cpu_baseline_seconds("attn", P=P, tree=kind, anc=anc_np) if n == 1 else None
+        o1 = cpu_baseline_seconds("attn", threads=1, P=P, tree=kind, anc=anc_np) if n == 1 and P < 131072 else None
         emit({"config": "tree attention" if P < 131072 else "long-context attention", "n": n, "P": P,
               "tree": kind, "us": round(t * 1e6, 1), "kv_GBps": round(kv / t / 1e9, 1),
-              "kv_hbm_frac": round(kv / t / 1e9 / HBM_PEAK_GBPS, 4), "TFLOPps": round(fl / t / 1e12, 1),
-              "mfma_frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4),
-              "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3)})
+              "kv_hbm_frac": round(kv / t / 1e9 / HBM_PEAK_GBPS, 4), "kv_copy_frac": round(kv / t / 1e9 / copy_gbps, 4),
+              "TFLOPps": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+              "cpu_oracle_s_per_seq": None if oc is None else round(oc, 3),
+              "cpu_oracle_s_per_seq_1thread": None if o1 is None else round(o1, 3)})
         torch.cuda.empty_cache()
     # [4] the full hybrid step at its own prefix, 16384
     cfg = HybridConfig(n=8, prefix=16384, extra_cap=(a.steps + a.warmup + 4) * 16 + 64)
