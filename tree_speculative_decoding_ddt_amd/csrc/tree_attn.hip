@@ -7,8 +7,9 @@
 //
 // bf16, D in {128, 256}: matrix-core path.
 //   Rows of one kv head are the G = Hq/Hkv query heads of all T tree rows, flattened
-//   r = t*G + h_local and cut into 16-row tiles; a wave owns up to NT tiles, a block
-//   (NW = 8 waves) shares each 32-key K/V tile in LDS.  Per 32 keys:
+//   r = t*G + h_local and cut into 16-row tiles; a wave owns up to NT tiles (and runs
+//   the products of only those that hold rows), a block (NW = 8 waves) shares each
+//   32-key K/V tile in LDS.  Per 32 keys:
 //     S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q from VGPRs;
 //                   each lane then holds 8 scores of ONE query row,
 //     softmax in the log2 domain (fp32) against a reference fixed for the pass
@@ -139,6 +140,18 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and the other counters left unconstrained.
 #define DDT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+template <int N> struct IntC { static constexpr int value = N; };
+// f(IntC<min(n, N)>) for a wave-uniform count n >= 0
+template <int N, typename F>
+__device__ __forceinline__ void dispatch_count(int n, F& f) {
+  if constexpr (N == 0) {
+    f(IntC<0>{});
+  } else {
+    if (n >= N) f(IntC<N>{});
+    else dispatch_count<N - 1>(n, f);
+  }
+}
 
 // Block = NW waves (two per SIMD) sharing one ring of K/V tiles in LDS; a wave owns NT
 // 16-row tiles of the flattened (tree row, q head) rows of one kv head.  The 4-stage
@@ -290,31 +303,36 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   // S^T blocks: Sacc[j][h] lane (l16, q4) element e = key 16h + 4*q4 + e of row l16.
   // The 2*DS operand reads are issued PK ahead of the products that use them (the
   // sched_group_barrier sequence pins that order for the machine scheduler).
-  auto s_phase = [&](int stage, f32x4 (&Sacc)[NT][2]) {
+  auto s_phase = [&](auto NAc, int stage, f32x4 (&Sacc)[NT][2]) {
+    constexpr int NA = decltype(NAc)::value;
+    if constexpr (NA > 0) {
     const uint8_t* Ks = lds + stage * 2 * TILE;
     constexpr int NOP = 2 * DS;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) Sacc[j][0] = Sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NA; ++j) Sacc[j][0] = Sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 Kop[NOP];
 #pragma unroll
     for (int i = 0; i < NOP; ++i) Kop[i] = *reinterpret_cast<const bf16x8*>(Ks + kbase[i & 1] + 64 * (i >> 1));
 #pragma unroll
     for (int i = 0; i < NOP; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NA; ++j)
         Sacc[j][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kop[i], Qf[j][i >> 1], Sacc[j][i & 1], 0, 0, 0);
     if constexpr (PK > 0) {  // PK = 0: leave the order to the scheduler
       __builtin_amdgcn_sched_group_barrier(0x100, PK, 0);  // DS reads
 #pragma unroll
       for (int i = 0; i < NOP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, NA, 0);  // MFMA
         if (i + PK < NOP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+    }
     }
   };
   // O^T += V^T P^T: A = V^T (d = 16b + l16; keys 4*q4 + 0..3, then 16 + 4*q4 + 0..3),
   // two transposing reads per block, issued two blocks ahead of their products
-  auto pv_phase = [&](int stage) {
+  auto pv_phase = [&](auto NAc, int stage) {
+    constexpr int NA = decltype(NAc)::value;
+    if constexpr (NA > 0) {
     const uint8_t* Vs = lds + stage * 2 * TILE;
     // rolling prefetch: the transposing reads of block b+2 are issued before the
     // products of block b (a sched_barrier after each block keeps that order)
@@ -333,8 +351,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       const bf16x8 A =
           __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[b % 3], hi[b % 3], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int j = 0; j < NT; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pp[j], O[j][b], 0, 0, 0);
+      for (int j = 0; j < NA; ++j) O[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pp[j], O[j][b], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
   };
   // ancestor mask of this lane's row in tile j (tree tiles only: read when needed)
@@ -361,9 +380,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   // P = 2^(score*scale*log2e - m) against the fixed reference; `over` marks an exponent
   // above kOver (P could overflow: the pass is redone with a larger reference)
   bool over = false;
-  auto softmax = [&](const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend, bf16x8 (&Pout)[NT]) {
+  auto softmax = [&](auto NAc, const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend,
+                     bf16x8 (&Pout)[NT]) {
+    constexpr int NA = decltype(NAc)::value;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int j = 0; j < NA; ++j) {
       float sv[8];
       scores(Sacc, j, masked, tree, kb, kend, sv);
       // the exponent arguments: results of arithmetic, so their maximum needs no NaN
@@ -404,72 +425,84 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 #pragma unroll
     for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int pass = 0; n_all > 0; ++pass) {
-    issue(0);  // every wave enters a pass with no copy in flight
-    if (n_all > 1) issue(1);
-    if (n_all > 2) issue(2);
+  // The passes over this split's key tiles, for a wave that owns NA valid 16-row tiles
+  // (its first NA; the rest lie past the last row): tiles past the rows skip their
+  // operand reads and products, but the wave still copies its share of every K/V tile
+  // and meets every barrier.
+  auto passes = [&](auto NAc) {
+    constexpr int NA = decltype(NAc)::value;
+    for (int pass = 0; n_all > 0; ++pass) {
+      issue(0);  // every wave enters a pass with no copy in flight
+      if (n_all > 1) issue(1);
+      if (n_all > 2) issue(2);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      l[j] = 0.f;
-      mxs[j] = -INFINITY;
+      for (int j = 0; j < NT; ++j) {
+        l[j] = 0.f;
+        mxs[j] = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // tile 0: S, then (first pass) the reference from its exact row max
-    {
-      sync_tile(0);
-      const bool tree = 0 >= n_pre;
-      const int kb = tree ? 0 : k_beg;
-      const int kend = tree ? Tn : k_end;
-      const bool masked = tree || kb + NK > kend;
-      f32x4 Sacc[NT][2];
-      s_phase(0, Sacc);
-      if (pass == 0) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          float sv[8];
-          scores(Sacc, j, masked, tree, kb, kend, sv);
-          float mx = sv[0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-          m[j] = row_max(mx) * sl2;  // every row sees at least one key of its first tile
-        }
+        for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      softmax(Sacc, masked, tree, kb, kend, Pp);
-      pv_phase(0);
-    }
-    int it = 1;
-    for (; it < n_full; ++it) {
-      sync_tile(it);
-      f32x4 Sacc[NT][2];
-      __builtin_amdgcn_s_setprio(1);
-      s_phase(it % NST, Sacc);
-      __builtin_amdgcn_s_setprio(0);
-      softmax(Sacc, false, false, 0, 0, Pp);
-      __builtin_amdgcn_s_setprio(1);
-      pv_phase(it % NST);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    for (; it < n_all; ++it) {  // the prefix tail and the tree tiles, under the mask
-      sync_tile(it);
-      const bool tree = it >= n_pre;
-      const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
-      const int kend = tree ? Tn : k_end;
-      f32x4 Sacc[NT][2];
-      s_phase(it % NST, Sacc);
-      softmax(Sacc, true, tree, kb, kend, Pp);
-      pv_phase(it % NST);
-    }
-    // one block-wide vote per pass: redo with references at the true row maxima
-    if (__any(over)) redo_vote = pass + 1;
-    __syncthreads();
-    const bool redo = redo_vote == pass + 1;
-    __syncthreads();
-    if (!redo) break;
-    over = false;
+      // tile 0: S, then (first pass) the reference from its exact row max
+      {
+        sync_tile(0);
+        const bool tree = 0 >= n_pre;
+        const int kb = tree ? 0 : k_beg;
+        const int kend = tree ? Tn : k_end;
+        const bool masked = tree || kb + NK > kend;
+        f32x4 Sacc[NT][2];
+        s_phase(NAc, 0, Sacc);
+        if (pass == 0) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) m[j] += fmaxf(row_max(mxs[j]), 0.f);
-  }
+          for (int j = 0; j < NA; ++j) {
+            float sv[8];
+            scores(Sacc, j, masked, tree, kb, kend, sv);
+            float mx = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+            m[j] = row_max(mx) * sl2;  // every row sees at least one key of its first tile
+          }
+        }
+        softmax(NAc, Sacc, masked, tree, kb, kend, Pp);
+        pv_phase(NAc, 0);
+      }
+      int it = 1;
+      for (; it < n_full; ++it) {
+        sync_tile(it);
+        f32x4 Sacc[NT][2];
+        __builtin_amdgcn_s_setprio(1);
+        s_phase(NAc, it % NST, Sacc);
+        __builtin_amdgcn_s_setprio(0);
+        softmax(NAc, Sacc, false, false, 0, 0, Pp);
+        __builtin_amdgcn_s_setprio(1);
+        pv_phase(NAc, it % NST);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      for (; it < n_all; ++it) {  // the prefix tail and the tree tiles, under the mask
+        sync_tile(it);
+        const bool tree = it >= n_pre;
+        const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
+        const int kend = tree ? Tn : k_end;
+        f32x4 Sacc[NT][2];
+        s_phase(NAc, it % NST, Sacc);
+        softmax(NAc, Sacc, true, tree, kb, kend, Pp);
+        pv_phase(NAc, it % NST);
+      }
+      // one block-wide vote per pass: redo with references at the true row maxima
+      if (__any(over)) redo_vote = pass + 1;
+      __syncthreads();
+      const bool redo = redo_vote == pass + 1;
+      __syncthreads();
+      if (!redo) break;
+      over = false;
+#pragma unroll
+      for (int j = 0; j < NA; ++j) m[j] += fmaxf(row_max(mxs[j]), 0.f);
+    }
+  };
+  int na = 0;  // wave-uniform: the valid tiles are a prefix of tile[]
+#pragma unroll
+  for (int j = 0; j < NT; ++j) na += tile[j] < ntiles;
+  dispatch_count<NT>(na, passes);
+
   // every wave reaches this point with no copy in flight (the last sync waited for all)
 
   // results: with one split the normalised output directly, else (lse, O/l) partials
