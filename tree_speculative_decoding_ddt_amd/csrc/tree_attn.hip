@@ -253,11 +253,17 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   };
 
   // this wave's tiles and Q fragments (B operand of S^T: row l16, d = 32*st + 8*q4 .. +7)
+  // Two row groups and an odd tile count: group 0 holds one tile more.  The slot of
+  // group 1 that would hold the tile past the last one recomputes group 0's last tile
+  // instead (its result is dropped), so both groups carry the same load per key tile and
+  // keep pace: the K/V tiles they share are then read from HBM once and hit in L2.
+  const int tdup = (nwg == 2 && (ntiles & 1)) ? ntiles - 1 : -1;
   int tile[NT];
   bf16x8 Qf[NT][DS];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     tile[j] = grp + nwg * (wave + NW * j);
+    if (tdup >= 0 && tile[j] == ntiles) tile[j] = tdup;
     const int r = tile[j] * 16 + l16;
     const bool ok = tile[j] < ntiles && r < R;
     const int trow = ok ? r / G : 0;
@@ -512,7 +518,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const int r = tile[j] * 16 + l16;
-    if (tile[j] >= ntiles || r >= R) continue;
+    if (tile[j] >= ntiles || r >= R || (grp == 1 && tile[j] == tdup)) continue;
     const float lse = lt > 0.f ? m[j] + log2f(lt) : -INFINITY;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (nsplit == 1) {
