@@ -84,6 +84,24 @@ def test_exact_bf16_ties_by_token_id():
     run_and_compare(zz, "bf16", 48, np.array([0, 1]))
 
 
+def test_many_ties_at_the_top_take_the_radix_path():
+    # more than 512 keys of a chunk at or above the chunk's bound: flat rows (every
+    # logit equal) and rows with 2000 tokens tied at the top value, bf16 at the full
+    # vocabulary and fp32 at a small one; ties go to the lowest token ids
+    say("build_tree flat and heavily tied rows")
+    rng = np.random.default_rng(31)
+    flat = np.zeros((1, 2, 151936), dtype=np.float32)
+    run_and_compare(flat, "bf16", 64, np.array([3]))
+    tied = rng.standard_normal((2, 3, 151936)).astype(np.float32)
+    for s in range(2):
+        for d in range(3):
+            tied[s, d, rng.choice(151936, size=2000, replace=False)] = 5.0
+    run_and_compare(tied, "bf16", 64, np.array([0, 1]))
+    tied32 = rng.standard_normal((1, 2, 3000)).astype(np.float32)
+    tied32[0, :, rng.choice(3000, size=1200, replace=False)] = 4.0
+    run_and_compare(tied32, "f32", 48, np.array([2]))
+
+
 @pytest.mark.parametrize("V", [1000, 5003, 16385])
 def test_ragged_vocab_fp32(V):
     # vocab sizes that are not a multiple of the chunk or of 8

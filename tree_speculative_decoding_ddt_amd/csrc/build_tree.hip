@@ -11,12 +11,14 @@
 //  1. topk_partial  grid (n*L rows, S chunks).  One HBM pass (16-byte loads): each block
 //     holds its chunk (<= 16384 logits) in registers as order-preserving integer keys,
 //     computes the chunk's (max, sum exp) and selects its exact top-K by (value desc, id asc):
-//     a lower bound from the per-thread maxima (per wave, by ballots) filters the chunk, an
-//     LDS radix select over the filtered keys finds the K-th value, and a second
-//     radix select over chunk offsets resolves ties at that value.
-//  2. topk_merge    grid (n*L).  Bitonic-sorts the S*K chunk candidates as 64-bit
-//     (value, -id) keys, keeps the best K, combines the chunk (max, sum) pairs into
-//     the row's log-sum-exp and writes lp = z - lse in fp32.
+//     a lower bound from the per-thread maxima (per wave, by ballots) filters the chunk;
+//     the keys that pass (typically about a hundred) are compacted into LDS as unique
+//     64-bit (key, -offset) words and ranked by counting.  When more than 512 pass (many
+//     ties near the top), an LDS radix select over the filtered keys finds the K-th value
+//     and a second radix select over chunk offsets resolves ties at that value.
+//  2. topk_merge    grid (n*L), one thread per compare-exchange.  Bitonic-sorts the S*K
+//     chunk candidates as 64-bit (value, -id) keys, keeps the best K, combines the chunk
+//     (max, sum) pairs into the row's log-sum-exp and writes lp = z - lse in fp32.
 //  3. heap_expand   grid (n), one wavefront.  The frontier (<= B+1 entries) lives in
 //     registers, two slots per lane; each pop is a wave-wide max over 64-bit keys
 //     (score desc, token asc, parent row asc) -- exact integer comparisons, so the
@@ -32,6 +34,7 @@ constexpr int kTopkThreads = 256;
 constexpr int kEmax = 64;                              // keys per thread
 constexpr int kChunkMax = kTopkThreads * kEmax;        // 16384 logits per block
 constexpr int kSortMax = 2048;                         // merge capacity (S*K)
+constexpr int kCand = 2 * kTopkThreads;                // compacted keys of the usual case
 
 // --- block-wide digit search over a 256-bin LDS histogram (wave 0 only).
 // Finds the bin where the running count (from the top bin down when `desc`, else from
@@ -71,7 +74,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
 }
 
 template <typename T, int KBITS, bool VECLOAD>
-__global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __restrict__ logits, int V, int chunk,
+__global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(3))) topk_partial_kernel(const T* __restrict__ logits, int V, int chunk,
                                                                     int K, float* __restrict__ cval,
                                                                     int32_t* __restrict__ cid,
                                                                     float2* __restrict__ stat) {
@@ -87,6 +90,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   __shared__ uint32_t sel[3];
   __shared__ float2 red[kTopkThreads / 64];
   __shared__ int out_cnt;
+  __shared__ uint32_t wpass[kTopkThreads / 64];
+  __shared__ uint64_t cand[kCand];
 
   // chunk offset of register j: element-wise, or VEC consecutive elements per 16-byte load
   constexpr int VEC = 16 / (int)sizeof(T);
@@ -183,6 +188,57 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   uint32_t tau = tmaxs[0];
 #pragma unroll
   for (int w = 1; w < kTopkThreads / 64; ++w) tau = tmaxs[w] < tau ? tmaxs[w] : tau;
+  const size_t base = ((size_t)row * S + c) * K;
+
+  // 3a. usual case: the keys at or above tau (at least keff of them, typically about a
+  // hundred per chunk) fit in LDS.  They are compacted there as unique 64-bit words
+  // (key, complement of the chunk offset) and each is ranked by counting the words above
+  // it: rank < keff are the chunk's top keff by (value desc, id asc), emitted in order.
+  uint32_t npass = 0;
+#pragma unroll
+  for (int j = 0; j < kEmax; ++j) npass += (elem(j) < cnt && key[j] >= tau) ? 1u : 0u;
+  uint32_t incl = npass;  // inclusive prefix over the wave's lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wpass[wave] = incl;
+  __syncthreads();
+  uint32_t total = 0, off = incl - npass;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    const uint32_t x = wpass[w];
+    total += x;
+    off += w < wave ? x : 0u;
+  }
+  if (total <= (uint32_t)kCand) {  // block-uniform
+#pragma unroll
+    for (int j = 0; j < kEmax; ++j) {
+      const int e = elem(j);
+      if (e < cnt && key[j] >= tau) cand[off++] = (static_cast<uint64_t>(key[j]) << 32) | (0xffffffffu - (uint32_t)e);
+    }
+    __syncthreads();
+    const uint64_t w0 = tid < (int)total ? cand[tid] : 0ull;
+    const uint64_t w1 = tid + kTopkThreads < (int)total ? cand[tid + kTopkThreads] : 0ull;
+    uint32_t r0 = 0, r1 = 0;
+    for (uint32_t i = 0; i < total; ++i) {
+      const uint64_t x = cand[i];
+      r0 += x > w0 ? 1u : 0u;
+      r1 += x > w1 ? 1u : 0u;
+    }
+    if (tid < (int)total && r0 < (uint32_t)keff) {
+      cval[base + r0] = kval(static_cast<uint32_t>(w0 >> 32));
+      cid[base + r0] = beg + (int)(0xffffffffu - (uint32_t)w0);
+    }
+    if (tid + kTopkThreads < (int)total && r1 < (uint32_t)keff) {
+      cval[base + r1] = kval(static_cast<uint32_t>(w1 >> 32));
+      cid[base + r1] = beg + (int)(0xffffffffu - (uint32_t)w1);
+    }
+    if (tid >= keff && tid < K) cid[base + tid] = -1;
+    return;
+  }
+  // 3b. otherwise (many keys tied near the top, e.g. a flat row): radix select below
 
   // 3. radix select of the keff-th largest key among keys >= tau
   uint32_t prefix = 0, pmask = 0, need = keff, count_eq = 0;
@@ -233,7 +289,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   // 5. emit exactly keff candidates (unordered); pad to K with id -1
   if (tid == 0) out_cnt = 0;
   __syncthreads();
-  const size_t base = ((size_t)row * S + c) * K;
 #pragma unroll
   for (int j = 0; j < kEmax; ++j) {
     const uint32_t e = elem(j);
@@ -249,7 +304,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __r
   if (tid >= keff && tid < K) cid[base + tid] = -1;
 }
 
-__global__ void __launch_bounds__(256) topk_merge_kernel(const float* __restrict__ cval,
+__global__ void __launch_bounds__(1024) topk_merge_kernel(const float* __restrict__ cval,
                                                          const int32_t* __restrict__ cid,
                                                          const float2* __restrict__ stat, int S, int K,
                                                          int sortN, int32_t* __restrict__ top_id,
@@ -278,18 +333,17 @@ __global__ void __launch_bounds__(256) topk_merge_kernel(const float* __restrict
     lse_s = M + __logf(tot);
   }
   __syncthreads();
-  // bitonic sort, descending
+  // bitonic sort, descending: in each stage, pair p compares i (bit j of i clear) with i + j
   for (int k = 2; k <= sortN; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < sortN; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = sk[i], b = sk[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            sk[i] = b;
-            sk[ixj] = a;
-          }
+      for (int pr = tid; pr < sortN / 2; pr += blockDim.x) {
+        const int i = (pr / j) * 2 * j + (pr % j);
+        const int ixj = i + j;
+        const uint64_t a = sk[i], b = sk[ixj];
+        const bool desc = (i & k) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          sk[i] = b;
+          sk[ixj] = a;
         }
       }
       __syncthreads();
@@ -466,8 +520,9 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
     else DDT_TOPK(float, 32, false);
   }
 #undef DDT_TOPK
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(n * L), dim3(256), 0, st, cval, cid, stat, plan.S, plan.K,
-                     plan.sortN, tid, tlp);
+  // one thread per compare-exchange of a sorting stage (sortN / 2 <= 1024)
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(n * L), dim3(plan.sortN / 2 < 64 ? 64 : plan.sortN / 2), 0, st, cval,
+                     cid, stat, plan.S, plan.K, plan.sortN, tid, tlp);
   const size_t smem = (size_t)L * plan.K * (sizeof(float) + sizeof(int32_t));
   hipLaunchKernelGGL(heap_expand_kernel, dim3(n), dim3(64), smem, st, tid, tlp, L, plan.K, B + 1, root_token,
                      tok, parent, depth, score, anc);
