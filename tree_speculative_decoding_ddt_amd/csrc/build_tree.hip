@@ -20,7 +20,7 @@
 //     chunk candidates as 64-bit (value, -id) keys, keeps the best K, combines the chunk
 //     (max, sum) pairs into the row's log-sum-exp and writes lp = z - lse in fp32.
 //  3. heap_expand   grid (n), one wavefront.  The frontier (<= B+1 entries) lives in
-//     registers, two slots per lane; each pop is a wave-wide max over 64-bit keys
+//     registers, one slot per lane; each pop is a wave-wide max over 64-bit keys
 //     (score desc, token asc, parent row asc) -- exact integer comparisons, so the
 //     pop order is deterministic.
 #include <math.h>
@@ -362,9 +362,12 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const float* __restric
   }
 }
 
+// One frontier entry: a candidate node (score, token, parent row, depth, rank among the
+// depth's top-K) and its next-ranked sibling's (log-prob, token), fetched when the entry
+// is made so that a pop reads no LDS on its critical path.
 struct Slot {
-  float score;
-  int tok, par, dep, rank;
+  float score, nlp;
+  int tok, par, dep, rank, ntok;
   bool valid;
 };
 
@@ -374,11 +377,13 @@ __device__ __forceinline__ uint64_t slot_key(const Slot& s) {
   return (static_cast<uint64_t>(float_key(s.score)) << 32) | lo;
 }
 
-// One wavefront per sequence.  T = B+1 <= 65, frontier <= B+1 <= 65 entries.  Every
-// step of a pop is lane-local, a DPP move or a scalar read of one lane (readlane): the
-// wave-wide max of the frontier keys, the winner's fields, and the parent's score and
-// mask (node i's are kept by lane i mod 64, slot i / 64).  The wave needs no barrier: it
-// reads LDS only for the per-depth candidates, which are fixed before the walk.
+// One wavefront per sequence, T = B+1 <= 65.  The frontier has one slot per lane: the
+// seed takes slot 0, pop i puts the popped node's sibling in the popped slot and its best
+// child in slot i at most (a fresh slot per pop), and the child of the last pop is never
+// popped, so 64 slots suffice.  Every step of a pop is lane-local, a DPP move or a scalar
+// read of one lane (readlane): the wave-wide max of the frontier keys, the winner's
+// fields, the parent's score and mask (node i's are kept by lane i), and the best child of
+// depth d (lane d).  The wave needs no barrier.
 __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restrict__ top_id,
                                                          const float* __restrict__ top_lp, int L, int K,
                                                          int T, const int32_t* __restrict__ root_token,
@@ -403,68 +408,64 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   }
   __syncthreads();
 
-  // built nodes: score and ancestor mask of node i held by lane i & 63, slot i >> 6
-  float nsc0 = 0.f, nsc1 = 0.f;
-  uint64_t nan0 = 0ull, nan1 = 0ull;
-  auto node_score = [&](int i) {
-    const float v = (i >> 6) ? nsc1 : nsc0;
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i & 63));
-  };
-  auto node_anc = [&](int i) { return readlane_u64((i >> 6) ? nan1 : nan0, i & 63); };
+  // best candidate of depth d + 1 (rank 0) in lane d
+  const float blp = lane < L ? lp[lane * K] : -INFINITY;
+  const int btok = lane < L ? ids[lane * K] : -1;
+  // built nodes: score and ancestor mask of node i held by lane i (i <= 63 are read)
+  float nsc = 0.f;
+  uint64_t nan = 0ull;
 
-  Slot s0, s1;  // this lane's frontier slots: index lane and 64 + lane
-  s0.valid = s1.valid = false;
+  Slot sl;
+  sl.valid = false;
+  sl.score = sl.nlp = 0.f;
+  sl.tok = sl.par = sl.dep = sl.rank = sl.ntok = 0;
   int nslots = 0;
-  // (fields assigned one by one: a reference chosen at run time would put both slots in
+  // (fields assigned one by one: a reference chosen at run time would put the slot in
   // scratch memory)
   auto put = [&](int idx, float sc, int tk, int pr, int dp, int rk) {
-    if ((idx & 63) == lane) {
-      if (idx >> 6) {
-        s1.score = sc; s1.tok = tk; s1.par = pr; s1.dep = dp; s1.rank = rk; s1.valid = true;
-      } else {
-        s0.score = sc; s0.tok = tk; s0.par = pr; s0.dep = dp; s0.rank = rk; s0.valid = true;
-      }
+    if (idx == lane) {
+      sl.score = sc; sl.tok = tk; sl.par = pr; sl.dep = dp; sl.rank = rk; sl.valid = true;
+      const int nx = (dp - 1) * K + rk + 1;
+      sl.ntok = rk + 1 < K ? ids[nx] : -1;
+      sl.nlp = rk + 1 < K ? lp[nx] : -INFINITY;
     }
   };
-  if (T > 1 && L >= 1 && ids[0] >= 0) put(nslots++, 0.f + lp[0], ids[0], 0, 1, 0);
+  const int tok0 = __builtin_amdgcn_readlane(btok, 0);
+  if (T > 1 && L >= 1 && tok0 >= 0)
+    put(nslots++, 0.f + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), 0)), tok0,
+        0, 1, 0);
 
   for (int i = 1; i < T; ++i) {
-    const uint64_t k0 = slot_key(s0), k1 = slot_key(s1);
-    const uint64_t best = wave_max_u64_uniform(k0 > k1 ? k0 : k1);
+    const uint64_t k = slot_key(sl);
+    const uint64_t best = wave_max_u64_uniform(k);
     if (best == 0) break;
-    const uint64_t b0 = __ballot(k0 == best && k0 != 0), b1 = __ballot(k1 == best && k1 != 0);
-    const int j = b0 ? 0 : 1;
-    const int owner = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)(b0 ? b0 : b1)) - 1);
-    const int idx = 64 * j + owner;
-    const float wsc = j ? s1.score : s0.score;
-    const int wtk = j ? s1.tok : s0.tok, wpr = j ? s1.par : s0.par, wdp = j ? s1.dep : s0.dep;
-    const int wrk = j ? s1.rank : s0.rank;
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsc), owner));
-    const int tk = __builtin_amdgcn_readlane(wtk, owner), pr = __builtin_amdgcn_readlane(wpr, owner);
-    const int dp = __builtin_amdgcn_readlane(wdp, owner), rk = __builtin_amdgcn_readlane(wrk, owner);
-    const uint64_t a = node_anc(pr) | (1ull << (i - 1));
+    const int owner = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)__ballot(k == best && k != 0)) - 1);
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl.score), owner));
+    const int tk = __builtin_amdgcn_readlane(sl.tok, owner), pr = __builtin_amdgcn_readlane(sl.par, owner);
+    const int dp = __builtin_amdgcn_readlane(sl.dep, owner), rk = __builtin_amdgcn_readlane(sl.rank, owner);
+    const int ntk = __builtin_amdgcn_readlane(sl.ntok, owner);
+    const float nlp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl.nlp), owner));
+    const uint64_t a = readlane_u64(nan, pr) | (1ull << (i - 1));
     if (lane == 0) {
       tok[ob + i] = tk; parent[ob + i] = pr; depth[ob + i] = dp; score[ob + i] = sc; anc[ob + i] = a;
     }
-    if (lane == (i & 63)) {
-      if (i >> 6) {
-        nsc1 = sc;
-        nan1 = a;
-      } else {
-        nsc0 = sc;
-        nan0 = a;
-      }
+    if (lane == i) {  // node 64 (never a parent) is not kept
+      nsc = sc;
+      nan = a;
     }
     // the popped slot takes the next-ranked sibling, or empties
-    if (lane == owner) {
-      if (j) s1.valid = false;
-      else s0.valid = false;
+    if (lane == owner) sl.valid = false;
+    if (ntk >= 0) {
+      const float psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nsc), pr));
+      put(owner, psc + nlp, ntk, pr, dp, rk + 1);
     }
-    const int r2 = rk + 1;
-    if (r2 < K && ids[(dp - 1) * K + r2] >= 0)
-      put(idx, node_score(pr) + lp[(dp - 1) * K + r2], ids[(dp - 1) * K + r2], pr, dp, r2);
-    // the best child goes to a fresh slot
-    if (dp < L && ids[dp * K] >= 0) put(nslots++, sc + lp[dp * K], ids[dp * K], i, dp + 1, 0);
+    // the best child goes to a fresh slot (none after the last pop)
+    if (i + 1 < T && dp < L) {
+      const int ctk = __builtin_amdgcn_readlane(btok, dp);
+      if (ctk >= 0)
+        put(nslots++, sc + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), dp)), ctk,
+            i, dp + 1, 0);
+    }
   }
 }
 
