@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--n", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="take value from the eager rounds (no HIP graph capture; for profiler runs)")
     ap.add_argument("--kernel-configs", action="store_true",
                     help="instead of the step line: per-config kernel figures (tree build, tree attention at "
                          "8K/32K/128K, the full step at 16K), one JSON line each")
@@ -402,19 +404,22 @@ def main():
     # The same round captured once in a HIP graph and replayed (every length is read on
     # the device, so a replay continues from the state the previous round left): the
     # launch gaps of the eager rounds drop out, the work is identical.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(a.warmup):
-        graph.replay()
-    torch.cuda.synchronize(dev)
-    tg = time.perf_counter()
-    for _ in range(a.steps):
-        graph.replay()
-    torch.cuda.synchronize(dev)
-    dtg = time.perf_counter() - tg
-    p2 = int(step.prefix_len.float().mean().item())
-    del graph
+    if a.no_graph:
+        dtg, p2 = dt, p1
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        tg = time.perf_counter()
+        for _ in range(a.steps):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        dtg = time.perf_counter() - tg
+        p2 = int(step.prefix_len.float().mean().item())
+        del graph
 
     alg = algorithmic(cfg, (p0 + p1) // 2)
     kernels = {}
@@ -500,11 +505,12 @@ def main():
                                % a.prefix,
                    "global_batch": cfg.n, "seq_len": a.prefix, "parallelism": "single GPU"},
         "roofline": roof, "tree_attn": attn, "kernels": kernels,
-        "timing": "value: K replays of one round captured in a HIP graph; kernels: HIP events per call "
-                  "over K eager rounds run before it (the same work, launched one call at a time)",
+        "timing": ("value and kernels: HIP events per call over K eager rounds (--no-graph)" if a.no_graph else
+                   "value: K replays of one round captured in a HIP graph; kernels: HIP events per call "
+                   "over K eager rounds run before it (the same work, launched one call at a time)"),
         "eager": {"steps_per_s": round(a.steps / dt, 3), "ms_per_step": round(dt / a.steps * 1e3, 3),
                   "prefix_during_timing": [p0, p1]},
-        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p1, p2],
+        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p0, p1] if a.no_graph else [p1, p2],
         "cpu_baseline": cpu, "variants": variant,
     }
     print(json.dumps(line), flush=True)

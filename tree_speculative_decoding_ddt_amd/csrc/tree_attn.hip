@@ -208,11 +208,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   const uint16_t* Kt = k_tree + hoff * Tn * D;
   const uint16_t* Vt = v_tree + hoff * Tn * D;
 
-  // LDS layout of a tile: key row r at r*RS, RS = row bytes + 32, so rows start 32 bytes
-  // apart modulo the 256 bytes the banks span; the 16-byte chunk c of row r is stored at
-  // chunk c ^ ((r >> 3) & 1).  Then the 16 keys of a K operand read (16 bytes each) and
-  // the 8 rows x 32 bytes of two transposing V reads both fall on distinct banks, and
-  // every read address is a per-lane base plus an immediate offset.
+  // LDS layout of a tile: key row r at r*RS, RS = row bytes + 32, so consecutive rows
+  // start 32 bytes apart modulo the 256 bytes the banks span, chunks in row order.  The
+  // K operand reads (16 bytes per lane) and the transposing V reads then run without bank
+  // conflicts (the hardware counter reads zero; an XOR swizzle of the chunks by row,
+  // tried first, caused conflicts on a third of the LDS-active cycles), and every read
+  // address is a per-lane base plus an immediate offset.
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto issue = [&](int it) {
     const uint32_t kb = lds0 + (uint32_t)((it % NST) * 2 * TILE);
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         size_t e = (size_t)key * D;  // wave-uniform row start
         if constexpr (PAGED)
           if (pre) e = prow[k] * D;
-        const uint32_t voff = (uint32_t)(ln ^ ((row >> 3) & 1)) << 4;  // this lane's 16-byte chunk
+        const uint32_t voff = (uint32_t)ln << 4;  // this lane's 16-byte chunk
         const uint32_t m = kb + (uint32_t)(row * RS);
         dma16(reinterpret_cast<const uint8_t*>(Kg + e) + voff, m);
         dma16(reinterpret_cast<const uint8_t*>(Vg + e) + voff, m + TILE);
@@ -295,9 +296,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int key = 16 * h + l16;
-    kbase[h] = key * RS + ((q4 ^ ((key >> 3) & 1)) << 4);
+    kbase[h] = key * RS + (q4 << 4);
     const int vkey = 16 * h + 4 * q4 + (l16 >> 2);
-    vbase[h] = TILE + vkey * RS + ((((l16 & 3) >> 1) ^ ((vkey >> 3) & 1)) << 4) + (l16 & 1) * 8;
+    vbase[h] = TILE + vkey * RS + (((l16 & 3) >> 1) << 4) + (l16 & 1) * 8;
   }
 
   f32x4 O[NT][DB];
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __rest
 #define DDT_ATTN_NW128 8
 #endif
 #ifndef DDT_ATTN_PK
-#define DDT_ATTN_PK 4  // K operand reads pinned ahead of their products (0: scheduler's order)
+#define DDT_ATTN_PK 3  // K operand reads pinned ahead of their products (0: scheduler's order)
 #endif
 constexpr int attn_nt(int D) { return D == 256 ? DDT_ATTN_NT256 : DDT_ATTN_NT128; }
 constexpr int attn_nw(int D) { return D == 256 ? DDT_ATTN_NW256 : DDT_ATTN_NW128; }
