@@ -40,6 +40,7 @@ constexpr int kAttnMinSplit = 512;  // fewest prefix keys per split: a split's (
                                     // cost about the traffic of 400 keys of K/V, but with few
                                     // sequences more splits fill more of the 256 CUs
 constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
+constexpr int kPageTab = 1024;   // block-table entries a paged split stages in LDS
 
 // ------------------------------------------------------------------ scalar path
 template <typename T, int D, bool PAGED>
@@ -215,6 +216,20 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   // tried first, caused conflicts on a third of the LDS-active cycles), and every read
   // address is a per-lane base plus an immediate offset.
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  // paged: the block-table entries of this split's pages, staged in LDS once (clamped into
+  // the pool) when they fit, so that a prefix row's page is an in-order LDS read instead of
+  // a scalar load that may miss the scalar cache; wider splits keep the scalar lookups
+  __shared__ int32_t pgtab[PAGED ? kPageTab : 1];
+  const int pfirst = PAGED ? k_beg >> pg.lps : 0;
+  const int pcount = PAGED && k_end > k_beg ? ((k_end - 1) >> pg.lps) - pfirst + 1 : 0;
+  const bool use_tab = PAGED && pcount <= kPageTab;
+  if constexpr (PAGED) {
+    if (use_tab)
+      for (int i = threadIdx.x; i < pcount; i += NW * 64) {
+        const int g = pg.bt[(size_t)s * pg.maxb + pfirst + i];
+        pgtab[i] = g < 0 ? 0 : (g >= pg.npages ? pg.npages - 1 : g);
+      }
+  }
   auto issue = [&](int it) {
     const uint32_t kb = lds0 + (uint32_t)((it % NST) * 2 * TILE);
     const bool pre = it < n_pre;
@@ -234,7 +249,14 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         int keys[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) keys[k] = r0 + min(wave + NW * k, rows - 1);
-        pg.rows_uniform4(s, kvh, Hkv, keys, prow);
+        if (use_tab) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            prow[k] = (((size_t)pgtab[(keys[k] >> pg.lps) - pfirst] * Hkv + kvh) << pg.lps) +
+                      (keys[k] & ((1 << pg.lps) - 1));
+        } else {
+          pg.rows_uniform4(s, kvh, Hkv, keys, prow);
+        }
       }
     }
     if (ln < LPR) {
@@ -277,6 +299,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // Q and masks in registers before the copy counting starts
+  if constexpr (PAGED) __syncthreads();  // the staged page table before the first copy
 
   // tile it must have landed (tiles it+1, it+2 may stay in flight: 2*RPW copies each,
   // completed in issue order); the barrier also means every wave is done with tile
