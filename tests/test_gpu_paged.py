@@ -86,6 +86,15 @@ def test_bf16_full_size_sampled():
     run_case(4, 8, 64, 15, 24, 4, 256, 16, 520, [8192] * 8, "bf16", rows=rows_by_depth)
 
 
+def test_bf16_wide_splits_look_pages_up_one_by_one():
+    # pages of one position and 8 sequences of up to 6000: a split spans about 1500
+    # pages, more than a block stages in LDS, so prefix rows find their pages by scalar
+    # loads; shorter prefixes leave later splits empty
+    say("paged bf16 page size 1, splits wider than the staged table (sampled rows)")
+    run_case(6, 8, 64, 15, 24, 4, 256, 1, 6000, [6000, 5000, 3001, 1500, 1024, 1025, 4000, 2500], "bf16",
+             rows=rows_by_depth)
+
+
 def test_empty_prefix():
     say("paged empty prefix")
     run_case(5, 2, 8, 4, 24, 4, 256, 16, 4, [0, 0], "bf16")
