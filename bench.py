@@ -203,10 +203,20 @@ def kernel_configs(a):
     ce.record()
     torch.cuda.synchronize(dev)
     copy_gbps = 2 * src.numel() * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
+    # write-only stream (a device fill of the same 1 GiB): the rate a call that mostly
+    # writes, like the GDN tree step with stored node states, compares against
+    cs.record()
+    for _ in range(10):
+        dst.fill_(7)
+    ce.record()
+    torch.cuda.synchronize(dev)
+    fill_gbps = dst.numel() * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
     emit({"config": "device copy", "bytes_per_copy": 2 << 30, "GBps": round(copy_gbps, 1),
           "frac_of_nominal": round(copy_gbps / HBM_PEAK_GBPS, 4)})
+    emit({"config": "device fill", "bytes_per_fill": 1 << 30, "GBps": round(fill_gbps, 1),
+          "frac_of_nominal": round(fill_gbps / HBM_PEAK_GBPS, 4)})
 
     def cpu_baseline_seconds(kind, threads=None, **k):
         """The CPU oracle on one sequence of the config (the same workload shapes); threads
