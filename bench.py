@@ -414,12 +414,18 @@ def main():
     # The same round captured once in a HIP graph and replayed (every length is read on
     # the device, so a replay continues from the state the previous round left): the
     # launch gaps of the eager rounds drop out, the work is identical.
-    if a.no_graph:
-        dtg, p2 = dt, p1
-    else:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
+    graph_ok = not a.no_graph
+    if graph_ok:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+        except RuntimeError as exc:  # capture refused: report the eager rounds instead
+            print("bench: HIP graph capture failed (%s); value from the eager rounds" % exc, file=sys.stderr,
+                  flush=True)
+            graph_ok = False
+            torch.cuda.synchronize(dev)
+    if graph_ok:
         for _ in range(a.warmup):
             graph.replay()
         torch.cuda.synchronize(dev)
@@ -430,6 +436,8 @@ def main():
         dtg = time.perf_counter() - tg
         p2 = int(step.prefix_len.float().mean().item())
         del graph
+    else:
+        dtg, p2 = dt, p1
 
     alg = algorithmic(cfg, (p0 + p1) // 2)
     kernels = {}
@@ -515,12 +523,12 @@ def main():
                                % a.prefix,
                    "global_batch": cfg.n, "seq_len": a.prefix, "parallelism": "single GPU"},
         "roofline": roof, "tree_attn": attn, "kernels": kernels,
-        "timing": ("value and kernels: HIP events per call over K eager rounds (--no-graph)" if a.no_graph else
+        "timing": ("value and kernels: HIP events per call over K eager rounds" if not graph_ok else
                    "value: K replays of one round captured in a HIP graph; kernels: HIP events per call "
                    "over K eager rounds run before it (the same work, launched one call at a time)"),
         "eager": {"steps_per_s": round(a.steps / dt, 3), "ms_per_step": round(dt / a.steps * 1e3, 3),
                   "prefix_during_timing": [p0, p1]},
-        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p0, p1] if a.no_graph else [p1, p2],
+        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p1, p2] if graph_ok else [p0, p1],
         "cpu_baseline": cpu, "variants": variant,
     }
     print(json.dumps(line), flush=True)
