@@ -456,9 +456,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // The passes over this split's key tiles, for a wave that owns NA valid 16-row tiles
-  // (its first NA; the rest lie past the last row): tiles past the rows skip their
-  // operand reads and products, but the wave still copies its share of every K/V tile
-  // and meets every barrier.
+  // (its first NA; the rest lie past the last row): tiles past the rows run no products
+  // (the K/V operand reads, shared by a wave's tiles, are skipped only when NA = 0), but
+  // the wave still copies its share of every K/V tile and meets every barrier.
   auto passes = [&](auto NAc) {
     constexpr int NA = decltype(NAc)::value;
     for (int pass = 0; n_all > 0; ++pass) {
