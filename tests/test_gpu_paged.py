@@ -75,6 +75,13 @@ def test_bf16_d256_page_sizes(ps):
     run_case(10 + ps, 2, 64, 15, 24, 4, 256, ps, 2048 // ps, [1000, 1777], "bf16")
 
 
+def test_bf16_d256_one_split_direct_output():
+    # capacity 512: one split writes the output directly; 24 q heads x 65 rows are 25 row
+    # tiles over two blocks, the second recomputing the first's last tile
+    say("paged bf16 D256 capacity 512 (one split)")
+    run_case(7, 2, 64, 15, 24, 4, 256, 16, 32, [512, 300], "bf16")
+
+
 def test_bf16_d128_small_pages():
     say("paged bf16 D128 page size 16")
     run_case(3, 2, 40, 10, 16, 2, 128, 16, 64, [1023, 5], "bf16")

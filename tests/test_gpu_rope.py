@@ -83,6 +83,12 @@ def test_bf16_partial_rotation_full_compare():
     run_case(3, 2, 64, 15, 24, 4, 256, 1200, [1000, 1136], "bf16", 64, 1e7)
 
 
+def test_bf16_one_split_direct_output():
+    # capacity 500: one split writes the output directly (25 row tiles over two blocks)
+    say("rope bf16 D256 capacity 500 (one split)")
+    run_case(6, 2, 64, 15, 24, 4, 256, 500, [500, 123], "bf16", 256, 1e4)
+
+
 def test_bf16_d128_chain():
     say("rope bf16 D128 chain")
     run_case(4, 2, 31, 31, 8, 2, 128, 700, [600, 7], "bf16", 128, 1e6, kind="chain")
