@@ -123,6 +123,18 @@ def test_small_K_and_small_trees():
     run_and_compare(z3, "f32", 1, np.array([0]))               # B = 1
 
 
+def test_deepest_drafter_depth():
+    # L = 63, the largest depth: dominant peaks at every depth make the best prefixes a
+    # 63-deep chain plus siblings; without peaks the tree stays shallow
+    say("build_tree L=63")
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((2, 63, 300)).astype(np.float32)
+    for s in range(2):
+        z[s, np.arange(63), rng.integers(0, 300, 63)] += 40.0
+    run_and_compare(z, "f32", 64, np.array([1, 2]))
+    run_and_compare(rng.standard_normal((1, 63, 300)).astype(np.float32), "f32", 64, np.array([3]))
+
+
 def test_invariants_full_size_batch():
     say("build_tree invariants n=16 B=64 V=151936")
     rng = np.random.default_rng(21)
