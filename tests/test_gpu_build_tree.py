@@ -100,6 +100,11 @@ def test_many_ties_at_the_top_take_the_radix_path():
     tied32 = rng.standard_normal((1, 2, 3000)).astype(np.float32)
     tied32[0, :, rng.choice(3000, size=1200, replace=False)] = 4.0
     run_and_compare(tied32, "f32", 48, np.array([2]))
+    # one flat stretch (at least one whole chunk at 3.5, radix path) beside chunks whose
+    # few larger values take the compacted path: the best 64 mix both kinds
+    mixed = rng.standard_normal((2, 3, 151936)).astype(np.float32)
+    mixed[:, :, :20000] = 3.5
+    run_and_compare(mixed, "bf16", 64, np.array([4, 5]))
 
 
 @pytest.mark.parametrize("V", [1000, 5003, 16385])
