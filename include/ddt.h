@@ -196,8 +196,8 @@ int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, cons
  *   S [n][H][dv][dk] (f32, committed, read only), S_scratch [n][T][H][dv][dk] (f32, written)
  *   o [n][T][H][dv] (act_dt, written)
  *   parent [n][T] int32: parent[i] < i, or < 0 for a row that reads the committed state
- *   L: upper bound on the tree depth (row depth by parent chain), L <= 31; rows deeper
- *      than L are not processed
+ *   L: the tree's depth bound, 0 <= L <= 63 (validated only: every row is processed,
+ *      whatever its depth by parent chain)
  *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q in fp32,
  *       and the tree's depth-first order)
  * S_scratch and conv_scratch may both be NULL: then no node state is stored (o is still
@@ -253,7 +253,8 @@ int ddt_tree_accept_sampled(const void* target_logits, int dt, const float* gumb
  * the accepted path is copied into the contiguous KV and recurrent buffers, through
  * an explicit commit keyed by node ids.  [arch]: the KV cache keeps only the
  * accepted path's entries.
- * For every sequence s with a = acc_len[s] >= 0 and P = prefix_len[s], P + a + 1 <= Pmax:
+ * For every sequence s with a = acc_len[s] in [0, L], P = prefix_len[s], P + a + 1 <= Pmax
+ * and every accepted row acc_rows[s][0..a] a tree row in [0, T):
  *   every attention layer:  k_cache/v_cache[s][:][P+j] = k_tree/v_tree[s][:][acc_rows[s][j]], j = 0..a
  *   every GDN layer:        S[s] = S_scratch[s][r], conv_state[s] = conv_scratch[s][r],
  *                           r = acc_rows[s][a] (the deepest accepted row)

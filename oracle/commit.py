@@ -12,7 +12,8 @@ positions P..P+a; the recurrent and conv state of the deepest accepted row
 (the root when a = 0) replace the committed state; prefix_len grows by a+1.
 A sequence whose prefix would exceed the cache capacity Pmax is left
 untouched and reported with acc_len = -1, as is a sequence whose acc_len is
-already negative.
+already negative or one of whose accepted rows is not a tree row (malformed
+input, reading R23: nothing is written for it).
 """
 
 import numpy as np
@@ -23,8 +24,8 @@ def _copy64(a):
     return np.array(a, dtype=np.float64, copy=True)
 
 
-def commit(acc_rows, acc_len, prefix_len, kv_layers, gdn_layers, Pmax):
-    """One sequence.
+def commit(acc_rows, acc_len, prefix_len, kv_layers, gdn_layers, Pmax, T=None):
+    """One sequence.  T (tree rows) defaults to the rows of the layers' scratch.
 
     kv_layers:  list of dicts with k_tree, v_tree [Hkv][T][D], k_cache, v_cache [Hkv][Pmax][D]
     gdn_layers: list of dicts with S_scratch [T][H][dv][dk], S [H][dv][dk],
@@ -36,9 +37,14 @@ def commit(acc_rows, acc_len, prefix_len, kv_layers, gdn_layers, Pmax):
     P = int(prefix_len)
     kv_out = [{k: _copy64(v) for k, v in lay.items()} for lay in kv_layers]
     gdn_out = [{k: _copy64(v) for k, v in lay.items()} for lay in gdn_layers]
+    if T is None:
+        T = (kv_layers[0]["k_tree"].shape[1] if kv_layers else
+             gdn_layers[0]["S_scratch"].shape[0] if gdn_layers else None)
     if a < 0 or P + a + 1 > Pmax:
         return P, -1, kv_out, gdn_out
     rows = [int(r) for r in acc_rows[: a + 1]]
+    if len(rows) < a + 1 or (T is not None and any(r < 0 or r >= T for r in rows)):
+        return P, -1, kv_out, gdn_out
     for lay in kv_out:
         for j, r in enumerate(rows):
             lay["k_cache"][:, P + j, :] = lay["k_tree"][:, r, :]

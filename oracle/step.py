@@ -89,5 +89,8 @@ def verify_step(draft_logits, root_token, B, attn_layers, gdn_layers, target_log
             "gdn_o": [g[0] for g in gdn_out], "S_scratch": [g[1] for g in gdn_out],
             "conv_scratch": [g[2] for g in gdn_out],
             "acc_rows": acc_rows, "acc_len_walk": acc_len, "bonus": bonus,
+            # the next round's root: the bonus token where the round was committed; a
+            # sequence that was not (acc_len -1) keeps its root and repeats the round
+            "next_root": np.where(new_acc >= 0, bonus, np.asarray(root_token)),
             "acc_len": new_acc, "prefix_len": new_prefix,
             "kv_after": kv_after, "gdn_after": gdn_after}

@@ -112,8 +112,3 @@ def ancestor_masks(parent):
             anc[i] = anc[parent[i]] | (1 << (i - 1))
     return np.array(anc, dtype=np.uint64)
 
-
-def positions(depth, prefix_len):
-    """Position ids of the flattened tree: nodes at one depth share a position."""
-    depth = np.asarray(depth)
-    return np.where(depth >= 0, prefix_len + depth, -1)

@@ -1,6 +1,8 @@
 """Helpers shared by the GPU parity tests: upload seeded inputs in a storage dtype,
 read results back, and compare against the oracle with the stated tolerances."""
 
+import os
+
 import numpy as np
 import torch
 
@@ -37,15 +39,33 @@ def down(t):
     return t.numpy().astype(np.float64) if t.is_floating_point() else t.numpy()
 
 
+# (test id, what, dtype, max abs err, max rel err, worst err / allowed) of every compare
+MARGINS = []
+
+
 def assert_close(got, ref, dtype, what=""):
+    """Elementwise |got - ref| <= atol + rtol * |ref|; the max-abs and max-rel errors and
+    the worst fraction of the allowed error are logged for every compare (also when it
+    passes), so the margin to the tolerance is visible."""
     atol, rtol = TOL[dtype]
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     err = np.abs(got - ref)
-    bad = err > atol + rtol * np.abs(ref)
+    allowed = atol + rtol * np.abs(ref)
+    if err.size:
+        max_abs = float(err.max())
+        max_rel = float((err / np.maximum(np.abs(ref), 1e-30)).max())
+        frac = float((err / allowed).max())
+    else:
+        max_abs = max_rel = frac = 0.0
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    MARGINS.append((test, what, dtype, max_abs, max_rel, frac))
+    say("  compare %-28s %s: max abs %.3g, max rel %.3g, worst %.3f of the allowed error"
+        % (what or "-", dtype, max_abs, max_rel, frac))
+    bad = err > allowed
     if bad.any():
-        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        i = np.unravel_index(np.argmax(err - allowed), err.shape)
         raise AssertionError("%s: %d/%d elements out of tolerance (%s); worst at %s: got %r ref %r; "
                              "max abs err %.3g" % (what, bad.sum(), bad.size, dtype, i, got[i], ref[i], err.max()))
 

@@ -133,7 +133,8 @@ def test_gdn_validation():
     assert status("ddt_gdn_tree_step", *args(dk=48, dv=48, C=96)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_gdn_tree_step", *args(dv=64)) == ddt.DDT_ERR_UNSUPPORTED
     assert status("ddt_gdn_tree_step", *args(W=9)) == ddt.DDT_ERR_UNSUPPORTED
-    assert status("ddt_gdn_tree_step", *args(L=32)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step", *args(L=64)) == ddt.DDT_ERR_ARG      # depth bound above 63
+    assert status("ddt_gdn_tree_step", *args(L=-1)) == ddt.DDT_ERR_ARG
     assert status("ddt_gdn_tree_step", *args(wsb=64)) == ddt.DDT_ERR_WORKSPACE
     assert ddt.gdn_tree_step_workspace(8, 64, 32, 128) > ddt.gdn_tree_step_workspace(1, 64, 32, 128) > 0
     assert status("ddt_gdn_tree_step", *args(dt=2)) == ddt.DDT_ERR_UNSUPPORTED

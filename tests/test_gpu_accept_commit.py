@@ -67,7 +67,7 @@ def test_accept_malformed_trees():
     assert down(out["acc_len"]).tolist() == [-1, -1]
 
 
-def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None):
+def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None, bad_row=None):
     rng = np.random.default_rng(seed)
     L, B, Hkv, D, H, dk, W = 5, 12, 2, 64, 2, 32, 4
     T, C = B + 1, 2 * H * dk
@@ -85,6 +85,9 @@ def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None):
         alen_np[s] = len(path) - 1
     if acc_override is not None:
         alen_np = np.where(acc_override < 0, -1, alen_np)
+    if bad_row is not None:  # (sequence, value): its last accepted row is not a tree row
+        alen_np[bad_row[0]] = max(alen_np[bad_row[0]], 1)
+        rows_np[bad_row[0], alen_np[bad_row[0]]] = bad_row[1]
     acc = {"acc_rows": up_int(rows_np), "acc_len": up_int(alen_np)}
     kv_np, kv_dev = [], []
     for _ in range(n_kv):
@@ -106,7 +109,7 @@ def commit_case(seed, n, n_kv, n_gdn, dtype, prefix, Pmax, acc_override=None):
     for s in range(n):
         kv_s = [{k: v[s] for k, v in lay.items()} for lay in kv_np]
         gd_s = [{k: v[s] for k, v in lay.items()} for lay in gd_np]
-        P2, a2, kv2, gd2 = ocommit.commit(rows_np[s], alen_np[s], prefix[s], kv_s, gd_s, Pmax)
+        P2, a2, kv2, gd2 = ocommit.commit(rows_np[s], alen_np[s], prefix[s], kv_s, gd_s, Pmax, T=T)
         assert down(pl)[s] == P2 and down(acc["acc_len"])[s] == a2
         for j, (_, _, kc, vc) in enumerate(kv_dev):
             np.testing.assert_array_equal(down(kc)[s], kv2[j]["k_cache"])
@@ -134,3 +137,11 @@ def test_commit_without_kv_layers():
     z = up_int(np.zeros((1, 2), dtype=np.int64))
     with pytest.raises(ValueError, match="Pmax"):
         ddt.commit(z, up_int(np.zeros(1, dtype=np.int64)), up_int(np.zeros(1, dtype=np.int64)), (), (), B=1)
+
+
+@pytest.mark.parametrize("bad", [13, 1 << 20, -2])
+def test_commit_refuses_rows_outside_the_tree(bad):
+    # sequence 1's accepted path names a row outside [0, T): nothing of it is written,
+    # its prefix stays and acc_len becomes -1; the other sequences commit as usual
+    say("commit bad row", bad)
+    commit_case(5, 3, 2, 2, "bf16", np.array([4, 9, 20]), 48, bad_row=(1, bad))

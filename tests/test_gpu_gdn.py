@@ -24,6 +24,17 @@ def run_case(seed, n, B, L, H, dk, W, dtype, kind="random", check_heads=None):
         parents = np.stack([np.arange(-1, B)] * n)  # row i's parent is row i-1: depth i
     elif kind == "star":
         parents = np.stack([np.r_[-1, np.zeros(B, dtype=np.int64)]] * n)  # every node a child of the root
+    elif kind == "deep":
+        # each row hangs off one of the 2 rows before it: depths around 40 at B 64, with
+        # branch points all the way down
+        parents = np.full((n, B + 1), -1, dtype=np.int64)
+        for s in range(n):
+            dep = [0]
+            for i in range(1, B + 1):
+                cands = [j for j in range(max(0, i - 2), i) if dep[j] < L]
+                p = int(cands[rng.integers(0, len(cands))])
+                parents[s, i] = p
+                dep.append(dep[p] + 1)
     elif kind == "unused":
         parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
         parents[:, B - 3:] = -1  # rows left unused by the build read the committed state
@@ -80,11 +91,15 @@ def test_full_batch_sampled_heads():
     run_case(33, 8, 64, 15, 32, 128, 4, "bf16", check_heads=[0, 17, 31])
 
 
-def test_deep_chain_uses_the_long_stack():
-    # depth 31 (> 15): the walk keeps 32 stack levels of 4 columns per thread
-    say("gdn chain depth 31")
-    run_case(40, 2, 31, 31, 2, 128, 4, "bf16", kind="chain")
-    run_case(41, 1, 40, 31, 1, 64, 3, "f32")  # random tree, depth bound 31
+def test_deep_chain_and_deep_trees():
+    # every row is processed whatever its depth: a 64-deep chain (all 65 rows, depth bound
+    # 63), 63-deep chains, and random trees about 40 deep with many branch points
+    say("gdn chain depth 64 / 63, deep random trees")
+    run_case(40, 2, 64, 63, 2, 128, 4, "bf16", kind="chain")
+    run_case(44, 1, 63, 63, 1, 64, 3, "f32", kind="chain")
+    out = run_case(45, 3, 64, 63, 2, 128, 4, "bf16", kind="deep")
+    run_case(46, 2, 64, 40, 1, 32, 4, "f32", kind="deep")
+    run_case(41, 1, 40, 31, 1, 64, 3, "f32")  # random tree
 
 
 def test_star_and_root_only():

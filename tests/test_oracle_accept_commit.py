@@ -134,3 +134,8 @@ def test_commit_capacity_guard():
     assert not kv2[0]["k_cache"].any() and not gd2[0]["S"].any()
     P, a, kv2, gd2 = ocommit.commit(np.array([0, 1, 2]), -1, 0, kv, gd, Pmax=6)  # malformed walk
     assert (P, a) == (0, -1)
+    P, a, kv2, gd2 = ocommit.commit(np.array([0, 3, 1]), 2, 0, kv, gd, Pmax=6)  # row 3 is not a tree row
+    assert (P, a) == (0, -1)
+    assert not kv2[0]["k_cache"].any() and not gd2[0]["S"].any()
+    P, a, kv2, gd2 = ocommit.commit(np.array([0, 2, -1]), 1, 0, kv, gd, Pmax=6)  # in range: committed
+    assert (P, a) == (2, 1) and kv2[0]["k_cache"][:, :2].all() and gd2[0]["S"].all()

@@ -13,6 +13,7 @@ import pytest
 import oracle.accept
 import oracle.attention
 import oracle.commit
+import oracle.gaps
 import oracle.gdn
 import oracle.paged
 import oracle.rope
@@ -20,6 +21,7 @@ import oracle.sampled
 import oracle.tree
 from tests import test_oracle_accept_commit as t_ac
 from tests import test_oracle_attention as t_attn
+from tests import test_oracle_gaps as t_gaps
 from tests import test_oracle_gdn as t_gdn
 from tests import test_oracle_paged as t_paged
 from tests import test_oracle_rope as t_rope
@@ -36,11 +38,12 @@ def mutated(module, name, old, new):
 
 
 def run_pins(pins):
-    """True if at least one pin fails."""
+    """True if at least one pin fails (a wrong answer, or an error the mistake causes;
+    every pin passes on the unmodified oracle)."""
     for pin in pins:
         try:
             pin()
-        except AssertionError:
+        except Exception:
             return True
     return False
 
@@ -69,6 +72,11 @@ SMP_PINS = [lambda: t_smp.test_draws_follow_the_tempered_softmax(0.5), t_smp.tes
             t_smp.test_power_of_two_rescaling_is_exact, t_smp.test_sampled_tokens_decide_the_path,
             t_smp.test_walk_emits_target_samples_along_a_chain]
 
+GAPS_PINS = [t_gaps.test_gap_below_eps_fails, t_gaps.test_gap_above_eps_passes,
+             t_gaps.test_exact_tie_of_identical_values_passes, t_gaps.test_exact_tie_of_different_values_fails,
+             t_gaps.test_near_tie_only_matters_up_to_b_plus_one, lambda: t_gaps.test_guard_equals_brute_force(1),
+             lambda: t_gaps.test_guard_equals_brute_force(2), t_gaps.test_ancestor_masks_match_the_parent_chain]
+
 CASES = [
     (oracle.tree, "build_tree", "int(ids[0, 0]), 0, 1, 0", "int(ids[0, 0]), 0, 1, 1", TREE_PINS),
     (oracle.tree, "build_tree", "score[p] + vals[d - 1, r + 1]", "score[p] + vals[d - 1, r]", TREE_PINS),
@@ -94,6 +102,9 @@ CASES = [
     (oracle.commit, "commit", 'lay["k_cache"][:, P + j, :] = lay["k_tree"][:, r, :]',
      'lay["k_cache"][:, P + j + 1, :] = lay["k_tree"][:, r, :]', ACC_PINS),
     (oracle.commit, "commit", "last = rows[-1]", "last = rows[0]", ACC_PINS),
+    (oracle.commit, "commit", "any(r < 0 or r >= T for r in rows)", "any(r < 0 for r in rows)",
+     ACC_PINS + [t_ac.test_commit_capacity_guard]),
+    (oracle.commit, "commit", "P + a + 1 > Pmax", "P + a > Pmax", ACC_PINS + [t_ac.test_commit_capacity_guard]),
     (oracle.rope, "rope", "hi * c + lo * s", "hi * c - lo * s", ROPE_PINS),
     (oracle.rope, "rope", "lo * c - hi * s", "lo * c + hi * s", ROPE_PINS),
     (oracle.rope, "rope", "lo, hi = x[..., :half], x[..., half:rot_dim]",
@@ -108,6 +119,14 @@ CASES = [
     (oracle.sampled, "sample_token", "key + np.asarray(g_row", "key - np.asarray(g_row", SMP_PINS),
     (oracle.sampled, "sample_token", "if temperature <= 0:", "if temperature < 0:", SMP_PINS),
     (oracle.sampled, "tree_accept_sampled", "gumbel[i], temperature)", "gumbel[0], temperature)", SMP_PINS),
+    (oracle.gaps, "gaps_ok", "for i in range(1, B + 1):", "for i in range(1, B):", GAPS_PINS),
+    (oracle.gaps, "gaps_ok", "if path_values(z, t, i) != path_values(z, t, i + 1):", "if True:", GAPS_PINS),
+    (oracle.gaps, "gaps_ok", "if path_values(z, t, i) != path_values(z, t, i + 1):", "if False:", GAPS_PINS),
+    (oracle.gaps, "gaps_ok", '"score"][i + 1] > eps', '"score"][i + 1] > 0', GAPS_PINS),
+    (oracle.gaps, "gaps_ok", '"score"][i + 1] > eps', '"score"][i + 1] > 10 * eps', GAPS_PINS),
+    (oracle.gaps, "path_values", "z[tree[\"depth\"][i] - 1, tree[\"tok\"][i]]", "z[tree[\"depth\"][i], tree[\"tok\"][i]]", GAPS_PINS),
+    (oracle.tree, "ancestor_masks", "anc[parent[i]] | (1 << (i - 1))", "anc[parent[i]] | (1 << i)", GAPS_PINS),
+    (oracle.tree, "ancestor_masks", "anc[parent[i]] | (1 << (i - 1))", "(1 << (i - 1))", GAPS_PINS),
     # the mistake the pages warn of: positions by flattened row order instead of depth
     (oracle.rope, "tree_positions", "prefix_len[:, None] + depth", "prefix_len[:, None] + np.arange(depth.shape[1])",
      ROPE_PINS),

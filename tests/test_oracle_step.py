@@ -90,3 +90,15 @@ def test_tiny_step_with_rope_commits_keys_rotated_at_their_cache_position(seed):
                 sc = kk @ qr[h] / 8.0
                 p = np.exp(sc - sc.max())
                 np.testing.assert_allclose((p / p.sum()) @ vv, r["attn_out"][0][s][row, h], rtol=1e-10, atol=1e-12)
+
+
+def test_uncommitted_sequence_keeps_its_root():
+    # sequence 1's cache is full: its round is not committed, so it keeps root 5 for the
+    # next round; sequence 0 commits and continues from its bonus token
+    d = tiny_inputs(0)
+    P = np.array([d["P"][0], d["Pmax"] - 1])
+    r = ostep.verify_step(d["z"], np.array([3, 5]), d["B"], [d["at"]], [dict(d["gi"])], d["y"],
+                          P, d["Pmax"], H=1, dk=32)
+    assert r["acc_len"][0] >= 0 and r["acc_len"][1] == -1
+    assert r["next_root"].tolist() == [r["bonus"][0], 5]
+    assert r["prefix_len"].tolist() == [P[0] + r["acc_len"][0] + 1, P[1]]

@@ -153,8 +153,3 @@ def test_small_tree_leaves_unused_rows():
     assert np.isneginf(t["score"][7:]).all() and (t["anc"][7:] == 0).all()
     assert sorted(row_paths(t)[1:]) == sorted([(0,), (1,), (0, 0), (0, 1), (1, 0), (1, 1)])
 
-
-def test_positions_share_depth():
-    t = otree.build_tree(np.log([[4.0, 2, 1, 1], [7.0, 1, 1, 1]]), 6, root_token=0)
-    pos = otree.positions(t["depth"], 100)
-    assert pos.tolist() == [100 + d for d in t["depth"].tolist()]

@@ -248,7 +248,7 @@ int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, cons
 static int gdn_args(int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt) {
   DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && L >= 0 && H >= 1, DDT_ERR_ARG,
             "ddt_gdn_tree_step: need n>=1, 0<=B<=64, L>=0, H>=1 (got n=%d B=%d L=%d H=%d)", n, B, L, H);
-  DDT_CHECK(L <= 31, DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: depth bound L=%d exceeds 31", L);
+  DDT_CHECK(L <= 63, DDT_ERR_ARG, "ddt_gdn_tree_step: depth bound L=%d exceeds 63", L);
   DDT_CHECK(dt_ok(act_dt), DDT_ERR_UNSUPPORTED, "ddt_gdn_tree_step: dtype %d", act_dt);
   DDT_CHECK(dk == dv && (dk == 32 || dk == 64 || dk == 128), DDT_ERR_UNSUPPORTED,
             "ddt_gdn_tree_step: dk=%d dv=%d not built (dk == dv in {32, 64, 128})", dk, dv);
@@ -278,7 +278,7 @@ int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state
                 aligned16(conv_scratch),
             DDT_ERR_ARG, "ddt_gdn_tree_step: workspace, state and activation buffers must be 16-byte aligned");
   return hip_status(ddt::launch_gdn_tree_step(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o,
-                                              parent, n, B + 1, L, H, dk, C, W, act_dt, ws,
+                                              parent, n, B + 1, H, dk, C, W, act_dt, ws,
                                               static_cast<hipStream_t>(stream)),
                     "ddt_gdn_tree_step");
 }

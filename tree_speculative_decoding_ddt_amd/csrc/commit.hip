@@ -7,9 +7,10 @@
 // DDTree" (the KV cache keeps only the accepted path).
 //
 // All copies move 16-byte words; every length is read on the device.  A sequence
-// whose walk failed (acc_len < 0) or whose prefix would overflow Pmax is skipped by
-// every copy kernel and finally reported with acc_len = -1; prefix_len is advanced
-// by the last kernel only, after all copies have read it.
+// whose walk failed (acc_len < 0), whose accepted rows are not tree rows, or whose
+// prefix would overflow Pmax is skipped by every copy kernel and finally reported
+// with acc_len = -1; prefix_len is advanced by the last kernel only, after all copies
+// have read it.
 #include "common.h"
 #include "launch.h"
 
@@ -30,14 +31,20 @@ struct GDNTable {
   uint8_t* conv_state[kLayersPerLaunch];
 };
 
-// Pmax is the capacity (max_blocks * page_size for a paged cache).  A paged cache also
-// needs a valid page for every destination position P .. P+a.
-__device__ __forceinline__ bool commit_ok(const int32_t* acc_len, const int32_t* prefix_len,
-                                          int s, int Pmax, int Lp1, int& a, int& P,
-                                          const PagedKV& pg = PagedKV{nullptr, 0, 0, 0}) {
+// Pmax is the capacity (max_blocks * page_size for a paged cache).  Every accepted row
+// acc_rows[s][0..a] must be a tree row in [0, T); a paged cache also needs a valid page
+// for every destination position P .. P+a.  A sequence that fails any check is not
+// written by any copy kernel, and the last kernel reports it with acc_len = -1.
+__device__ __forceinline__ bool commit_ok(const int32_t* acc_rows, const int32_t* acc_len,
+                                          const int32_t* prefix_len, int s, int T, int Pmax, int Lp1,
+                                          int& a, int& P, const PagedKV& pg = PagedKV{nullptr, 0, 0, 0}) {
   a = acc_len[s];
   P = prefix_len[s];
   if (!(a >= 0 && a < Lp1 && P >= 0 && P + a + 1 <= Pmax)) return false;
+  for (int j = 0; j <= a; ++j) {
+    const int r = acc_rows[(size_t)s * Lp1 + j];
+    if (r < 0 || r >= T) return false;
+  }
   if (pg.bt != nullptr)
     for (int b = P >> pg.lps; b <= (P + a) >> pg.lps; ++b) {
       const int id = pg.bt[(size_t)s * pg.maxb + b];
@@ -54,7 +61,7 @@ __global__ void __launch_bounds__(256) commit_kv_kernel(KVTable tab, const int32
                                                         int T, int Pmax, int row_vecs, int Lp1, PagedKV pg) {
   const int s = blockIdx.x, layer = blockIdx.y;
   int a, P;
-  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) return;
+  if (!commit_ok(acc_rows, acc_len, prefix_len, s, T, Pmax, Lp1, a, P, pg)) return;
   const uint4* kt = reinterpret_cast<const uint4*>(tab.k_tree[layer]);
   const uint4* vt = reinterpret_cast<const uint4*>(tab.v_tree[layer]);
   uint4* kc = reinterpret_cast<uint4*>(tab.k_cache[layer]);
@@ -82,7 +89,7 @@ __global__ void __launch_bounds__(256) commit_gdn_kernel(GDNTable tab, const int
                                                          int Lp1, PagedKV pg) {
   const int s = blockIdx.x, layer = blockIdx.y;
   int a, P;
-  if (!commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) return;
+  if (!commit_ok(acc_rows, acc_len, prefix_len, s, T, Pmax, Lp1, a, P, pg)) return;
   const int r = acc_rows[s * Lp1 + a];
   if (r < 0 || r >= T) return;
   const uint4* Ss = reinterpret_cast<const uint4*>(tab.S_scratch[layer]) + ((size_t)s * T + r) * state_vecs;
@@ -99,12 +106,12 @@ __global__ void __launch_bounds__(256) commit_gdn_kernel(GDNTable tab, const int
   }
 }
 
-__global__ void commit_finalize_kernel(int32_t* acc_len, int32_t* prefix_len, int n, int Pmax, int Lp1,
-                                       PagedKV pg) {
+__global__ void commit_finalize_kernel(const int32_t* __restrict__ acc_rows, int32_t* acc_len, int32_t* prefix_len,
+                                       int n, int T, int Pmax, int Lp1, PagedKV pg) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n) return;
   int a, P;
-  if (commit_ok(acc_len, prefix_len, s, Pmax, Lp1, a, P, pg)) prefix_len[s] = P + a + 1;
+  if (commit_ok(acc_rows, acc_len, prefix_len, s, T, Pmax, Lp1, a, P, pg)) prefix_len[s] = P + a + 1;
   else acc_len[s] = -1;
 }
 
@@ -140,7 +147,8 @@ hipError_t launch_commit(const int32_t* acc_rows, int32_t* acc_len, int32_t* pre
     hipLaunchKernelGGL(commit_gdn_kernel, dim3(n, cnt, chunks), dim3(256), 0, st, tab, acc_rows,
                        acc_len, prefix_len, T, Pmax, state_vecs, conv_vecs, Lp1, pg);
   }
-  hipLaunchKernelGGL(commit_finalize_kernel, dim3(cdiv(n, 64)), dim3(64), 0, st, acc_len, prefix_len, n, Pmax, Lp1, pg);
+  hipLaunchKernelGGL(commit_finalize_kernel, dim3(cdiv(n, 64)), dim3(64), 0, st, acc_rows, acc_len, prefix_len, n, T, Pmax,
+                     Lp1, pg);
   return hipGetLastError();
 }
 

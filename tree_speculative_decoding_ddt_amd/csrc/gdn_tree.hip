@@ -18,11 +18,12 @@
 //  gdn_state  grid (n*H, dv/R): a block owns R rows of one head's [dv][dk] state, a
 //             thread CPT columns of one row (groups of 4, so that a wave's 16-byte
 //             stores cover whole row segments).  The block loads every node's
-//             q, k, k.q, v, g, beta into LDS, orders the nodes depth-first (in parallel:
-//             subtree sizes and sibling offsets), then walks them with no barrier:
-//             the parent's state is the newest one at depth d-1, held in a register
-//             stack indexed by the (wave-uniform) depth.  Each node's state is written
-//             once to S_scratch; nothing is re-read from memory.
+//             q, k, k.q, v, g, beta into LDS, reads the depth-first order the conv
+//             kernel computed (largest subtree last), then walks the nodes with no
+//             barrier: the parent's state is the node just visited or a branch point
+//             held in a register stack of 8 slots (enough for any tree of up to 128
+//             rows, whatever its depth).  Each node's state is written once to
+//             S_scratch; nothing is re-read from memory.
 #include <math.h>
 
 #include "common.h"
@@ -34,12 +35,23 @@ constexpr int kGdnMaxT = 128;
 constexpr int kGdnMaxW = 8;
 
 // Depth-first (pre-)order of one sequence's tree, computed in parallel over nodes by a
-// block of >= Tn threads: subtree sizes, then each node's offset among its earlier
-// siblings, then its position.  A row whose parent is not an earlier row starts a tree
-// of its own (it reads the committed state).  Word k = node | depth << 16 | save << 24,
-// where save marks a node with two or more children (a later child takes its state
-// from the stack; a first child takes it from the node just before it).
-__device__ void dfs_order(const int* par, int Tn, int* sz, int* nch, int* esib, int32_t* out) {
+// block of >= Tn threads.  A row whose parent is not an earlier row starts a tree of its
+// own (it reads the committed state).  Children are visited in increasing order of
+// (subtree size, row), so the largest subtree comes last.  The walk keeps the state of
+// a node with two or more children in a register stack slot while its earlier children
+// are walked; a child that is not its parent's last one is "light" and its subtree holds
+// fewer than half of its parent's nodes, so a node has at most log2(Tn) light edges
+// above it and the slot index lvl (the count of those edges) stays below 8 for Tn <= 128
+// whatever the depth.  Word k of the order describes the k-th node visited:
+//   bits 0-7   node (row)
+//   bits 8-9   source of the parent state: 0 committed, 1 the node just visited (a first
+//              child), 2 stack slot `rslot` (a later child)
+//   bits 12-14 rslot = lvl(parent)
+//   bits 16-18 sslot = lvl(node), bit 20: save the node's state there (two or more children)
+// While a later child of p is still to come, every node visited in between lies under a
+// light child of p and has lvl > lvl(p), so slot lvl(p) still holds p's state when that
+// child reads it.
+__device__ void dfs_order(const int* par, int Tn, int* sz, int* nch, int* esib, int* lvl, int32_t* out) {
   const int tid = threadIdx.x;
   for (int u = tid; u < Tn; u += blockDim.x) sz[u] = nch[u] = 0;
   __syncthreads();
@@ -56,27 +68,48 @@ __device__ void dfs_order(const int* par, int Tn, int* sz, int* nch, int* esib, 
     }
   }
   __syncthreads();
+  // esib: nodes of the siblings visited before this one; light: a sibling comes after it
+  int light = 0;
   if (tid < Tn) {
     const int p = par[tid];
     const int vp = (p >= 0 && p < tid) ? p : -1;
+    const int my = sz[tid];
     int e = 0;
-    for (int j = 0; j < tid; ++j) {
+    for (int j = 0; j < Tn; ++j) {
+      if (j == tid) continue;
       const int pj = par[j];
       const int vpj = (pj >= 0 && pj < j) ? pj : -1;
-      if (vpj == vp) e += sz[j];
+      if (vpj != vp) continue;
+      const bool before = sz[j] < my || (sz[j] == my && j < tid);
+      if (before) e += sz[j];
+      else light = 1;
     }
     esib[tid] = e;
+    if (vp < 0) light = 0;  // the roots' order needs no stack: each reads the committed state
+    lvl[tid] = light;       // this node's own edge; the chain sum follows
   }
   __syncthreads();
+  int pos = 0, lv = 0;
   if (tid < Tn) {
-    int pos = d_me, a = tid;
+    pos = d_me;
+    int a = tid;
     while (true) {
       pos += esib[a];
+      lv += lvl[a];
       const int p = par[a];
       if (!(p >= 0 && p < a)) break;
       a = p;
     }
-    out[pos] = tid | (d_me << 16) | ((nch[tid] >= 2) << 24);
+  }
+  __syncthreads();
+  if (tid < Tn) lvl[tid] = lv;
+  __syncthreads();
+  if (tid < Tn) {
+    const int p = par[tid];
+    const bool rooted = !(p >= 0 && p < tid);
+    const int src = rooted ? 0 : (esib[tid] == 0 ? 1 : 2);
+    const int rslot = rooted ? 0 : lvl[p];
+    out[pos] = tid | (src << 8) | (rslot << 12) | (lv << 16) | ((nch[tid] >= 2) << 20);
   }
 }
 
@@ -159,8 +192,8 @@ __global__ void __launch_bounds__(256) gdn_conv_kernel(const A* __restrict__ x, 
   }
   __syncthreads();
   if (u == 0 && blockIdx.y == 0) {  // one block per sequence also orders its tree for the walk
-    __shared__ int sz[kGdnMaxT], nch[kGdnMaxT], esib[kGdnMaxT];
-    dfs_order(par_s, Tn, sz, nch, esib, order + (size_t)s * Tn);
+    __shared__ int sz[kGdnMaxT], nch[kGdnMaxT], esib[kGdnMaxT], lvl[kGdnMaxT];
+    dfs_order(par_s, Tn, sz, nch, esib, lvl, order + (size_t)s * Tn);
   }
   const int hp = blockIdx.y * HG + tid / LPH;
   if (hp >= H) return;
@@ -251,38 +284,24 @@ template <int N> struct VecT;
 template <> struct VecT<4> { typedef fv4 type; };
 template <> struct VecT<8> { typedef fv8 type; };
 
-// A stack of LMAX states (one CPT-wide vector per thread) kept in registers: one
-// named member per depth and a switch on the wave-uniform depth, so no level is
-// ever addressed through memory.
-#define DDT_L16(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15)
-#define DDT_L32(X) DDT_L16(X) X(16) X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24) X(25) X(26) X(27) X(28) \
-  X(29) X(30) X(31)
-#define DDT_DECL(i) V v##i;
-#define DDT_GET(i) case i: return v##i;
-#define DDT_PUT(i) case i: v##i = x; break;
-
-template <int LMAX, typename V> struct RegStack;
-template <typename V> struct RegStack<16, V> {
-  DDT_L16(DDT_DECL)
-  __device__ __forceinline__ V get(int d) const {
-    switch (d) { DDT_L16(DDT_GET) default: return v0; }
+// The stack of saved states (one CPT-wide vector per thread per slot) kept in registers:
+// one named member per slot and a switch on the wave-uniform slot index, so no slot is
+// ever addressed through memory.  8 slots cover every tree of up to 128 rows.
+template <typename V> struct RegStack {
+  V v0, v1, v2, v3, v4, v5, v6, v7;
+  __device__ __forceinline__ V get(int i) const {
+    switch (i) {
+      case 0: return v0; case 1: return v1; case 2: return v2; case 3: return v3;
+      case 4: return v4; case 5: return v5; case 6: return v6; default: return v7;
+    }
   }
-  __device__ __forceinline__ void put(int d, V x) {
-    switch (d) { DDT_L16(DDT_PUT) default: break; }
+  __device__ __forceinline__ void put(int i, V x) {
+    switch (i) {
+      case 0: v0 = x; break; case 1: v1 = x; break; case 2: v2 = x; break; case 3: v3 = x; break;
+      case 4: v4 = x; break; case 5: v5 = x; break; case 6: v6 = x; break; default: v7 = x; break;
+    }
   }
 };
-template <typename V> struct RegStack<32, V> {
-  DDT_L32(DDT_DECL)
-  __device__ __forceinline__ V get(int d) const {
-    switch (d) { DDT_L32(DDT_GET) default: return v0; }
-  }
-  __device__ __forceinline__ void put(int d, V x) {
-    switch (d) { DDT_L32(DDT_PUT) default: break; }
-  }
-};
-#undef DDT_DECL
-#undef DDT_GET
-#undef DDT_PUT
 
 // A thread's N columns of a row are N/4 groups of 4, the groups GS floats apart: with
 // GS = DK/(N/4), each 16-byte store instruction of a wave covers whole row segments.
@@ -307,12 +326,12 @@ __device__ __forceinline__ void store_vec_nt(float* p, V x) {
   }
 }
 
-template <typename A, int DK, int CPT, int LMAX>
+template <typename A, int DK, int CPT>
 __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict__ qk, const float* __restrict__ kq,
                                                         const A* __restrict__ v, const float* __restrict__ beta,
                                                         const float* __restrict__ g, const float* __restrict__ S,
                                                         float* __restrict__ S_scratch, A* __restrict__ o,
-                                                        const int32_t* __restrict__ order_g, int Tn, int L, int H) {
+                                                        const int32_t* __restrict__ order_g, int Tn, int H) {
   typedef typename VecT<CPT>::type V;
   constexpr int DV = DK;
   constexpr int LPR = DK / CPT;          // lanes per state row
@@ -353,20 +372,19 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
 
   // ---- walk (the next node's word is read while the current one is processed).  In
   // depth-first order a node's parent is either the node just processed (its state is
-  // still in registers) or an earlier node with two or more children (kept on the stack).
-  RegStack<LMAX, V> stk;
+  // still in registers) or an earlier node with two or more children (kept in the stack
+  // slot the order names); every row is processed, whatever its depth.
+  RegStack<V> stk;
   V sprev = sc;
-  int dprev = -1;
   int nxt = order[0];
   for (int k = 0; k < Tn; ++k) {
     const int cur = __builtin_amdgcn_readfirstlane(nxt);
     if (k + 1 < Tn) nxt = order[k + 1];
-    const int u = cur & 0xffff, d = (cur >> 16) & 0xff;
-    const bool save = (cur >> 24) & 1;
-    if (d > L) continue;  // deeper than the stated bound: not processed
+    const int u = cur & 0xff, src = (cur >> 8) & 3, rslot = (cur >> 12) & 7, sslot = (cur >> 16) & 7;
+    const bool save = (cur >> 20) & 1;
     const V qv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + c0]);
     const V kv = load_vec<V, CPT, GS>(&qk_s[u * 2 * DK + DK + c0]);
-    const V sp = d == 0 ? sc : (d == dprev + 1 ? sprev : stk.get(d - 1));
+    const V sp = src == 0 ? sc : (src == 1 ? sprev : stk.get(rslot));
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
@@ -378,9 +396,8 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
     const float gi = gb[u][0], bi = gb[u][1], kqi = gb[u][2], vi = vv[u][rl];
     const float delta = bi * (vi - gi * a);
     const V sn = gi * sp + delta * kv;
-    if (save) stk.put(d, sn);
+    if (save) stk.put(sslot, sn);
     sprev = sn;
-    dprev = d;
     const size_t ti = ((size_t)s * Tn + u) * H + h;
     if (S_scratch != nullptr) store_vec_nt<V, CPT, GS>(&S_scratch[(ti * DV + r) * DK + c0], sn);
     if (c0 == 0) Elem<A>::store(o, ti * DV + r, gi * b + delta * kqi);
@@ -397,10 +414,9 @@ size_t gdn_workspace(int n, int T, int H, int dk) {
 template <typename A, int DK>
 static void launch_gdn(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
                        const float* beta, const float* g, const float* S, float* S_scratch, void* o,
-                       const int32_t* parent, int n, int T, int L, int H, int C, int W, void* ws, hipStream_t st) {
-  constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread, depth bound < 16
-  constexpr int R = 256 / (DK / CPT);
-  constexpr int R4 = 256 / (DK / 4);      // 4 columns per thread, depth bound < 32
+                       const int32_t* parent, int n, int T, int H, int C, int W, void* ws, hipStream_t st) {
+  constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread
+  constexpr int R = 256 / (DK / CPT);     // state rows per block
   const size_t qk_b = ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256;
   const size_t kq_b = ((size_t)n * T * H * sizeof(float) + 255) / 256 * 256;
   float* qk = static_cast<float*>(ws);
@@ -417,29 +433,20 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   // the dynamic LDS limit is raised once per kernel, to the largest size any call uses
   // (a host-side attribute, not a stream operation: calls stay capturable in a graph)
   constexpr int kMaxSmem = 65 * 2 * DK * (int)sizeof(float);  // T <= 65 (B <= 64)
-  if (L < 16) {
-    auto kern = gdn_state_kernel<A, DK, CPT, 16>;
-    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxSmem) == hipSuccess;
-    (void)attr;
-    hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
-                       S_scratch, static_cast<A*>(o), ord, T, L, H);
-  } else {
-    auto kern = gdn_state_kernel<A, DK, 4, 32>;
-    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxSmem) == hipSuccess;
-    (void)attr;
-    hipLaunchKernelGGL(kern, dim3(n * H, DK / R4), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
-                       S_scratch, static_cast<A*>(o), ord, T, L, H);
-  }
+  auto kern = gdn_state_kernel<A, DK, CPT>;
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxSmem) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
+                     S_scratch, static_cast<A*>(o), ord, T, H);
 }
 
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
                                 const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
-                                void* o, const int32_t* parent, int n, int T, int L, int H, int dk, int C, int W,
+                                void* o, const int32_t* parent, int n, int T, int H, int dk, int C, int W,
                                 int act_dt, void* ws, hipStream_t st) {
 #define DDT_GDN(TY, DKV) \
-  launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, L, H, C, W, ws, st)
+  launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H, C, W, ws, st)
   if (act_dt == DDT_BF16) {
     if (dk == 32) DDT_GDN(uint16_t, 32);
     else if (dk == 64) DDT_GDN(uint16_t, 64);

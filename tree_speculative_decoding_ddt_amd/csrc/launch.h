@@ -88,7 +88,7 @@ size_t gdn_workspace(int n, int T, int H, int dk);
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,
                                 void* conv_scratch, const void* v, const float* beta,
                                 const float* g, const float* S, float* S_scratch, void* o,
-                                const int32_t* parent, int n, int T, int L, int H, int dk, int C,
+                                const int32_t* parent, int n, int T, int H, int dk, int C,
                                 int W, int act_dt, void* ws, hipStream_t st);
 
 // ---- GDN replay on commit

@@ -213,8 +213,10 @@ class HybridVerifyStep:
             ddt.commit(self.acc["acc_rows"], self.acc["acc_len"], self.prefix_len, kv,
                        [(g["out"]["S_scratch"], g["S"], g["out"]["conv_scratch"], g["conv_state"])
                         for g in self.gdn], B=self.cfg.B, block_table=self.block_table)
-        # the bonus token of this round is the root of the next one
-        self.root_token.copy_(self.acc["bonus"])
+        # the bonus token of this round is the root of the next one; a sequence that was
+        # not committed (acc_len -1: malformed walk, capacity or bad rows) keeps its root,
+        # so no token drops out of its sequence
+        self.root_token.copy_(torch.where(self.acc["acc_len"] >= 0, self.acc["bonus"], self.root_token))
 
     def __call__(self):
         self.build()
