@@ -101,6 +101,24 @@ int ddt_build_tree(const void* draft_logits, int dt, int n, int L, int V, int B,
                    const int32_t* root_token, int32_t* tok, int32_t* parent, int32_t* depth,
                    float* score, uint64_t* anc, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- tree build, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ddt_build_tree with the same arguments
+ * and results, minus the workspace.  Its scratch is a static device array of
+ * ddt_build_tree_noalloc_max_scratch() bytes (8 MiB) per device, held from the first call
+ * on a device until the process ends; the call allocates nothing and calls no allocating
+ * routine.  A size whose scratch (ddt_build_tree_workspace) exceeds it is rejected with
+ * DDT_ERR_WORKSPACE before any HIP call (n = 64 at L = 15, V = 151936, K = 64 fits).
+ * Every call on a device shares that device's array: calls that overlap on one device
+ * (different streams, or host threads) race and must be serialised by the caller.
+ * stream must belong to the current device.  The array needs no clearing: every call
+ * writes the scratch it reads.
+ */
+size_t ddt_build_tree_noalloc_max_scratch(void);
+int ddt_build_tree_noalloc(const void* draft_logits, int dt, int n, int L, int V, int B, int K,
+                           const int32_t* root_token, int32_t* tok, int32_t* parent, int32_t* depth,
+                           float* score, uint64_t* anc, void* stream);
+
 /* ---------------------------------------------------------------- tree attention
  * [notes] "Why hybrid attention makes it hard": each tree row attends to the
  * committed prefix plus its own ancestors and never to its siblings.  [arch]: one

@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -51,6 +51,22 @@ P = ctypes.c_void_p(256)  # a non-null placeholder: every call below fails valid
 
 def status(fn, *args):
     return getattr(ddt.lib(), fn)(*args)
+
+
+def test_build_tree_noalloc_validation():
+    # same checks as ddt_build_tree, plus the static scratch bound, all before any HIP call
+    L = ddt.lib()
+    assert L.ddt_build_tree_noalloc_max_scratch() == 8 << 20
+    args = lambda **k: [k.get("z", P), 1, k.get("n", 1), k.get("L", 15), k.get("V", 1000), k.get("B", 64),
+                        k.get("K", 0), P, P, P, P, P, P, None]
+    assert status("ddt_build_tree_noalloc", *args(z=None)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree_noalloc", *args(B=65)) == ddt.DDT_ERR_ARG
+    assert status("ddt_build_tree_noalloc", *args(L=64)) == ddt.DDT_ERR_ARG
+    assert ddt.build_tree_workspace(64, 15, 151936, 64) <= 8 << 20       # the stated fit
+    big = dict(n=256, L=15, V=151936)
+    assert ddt.build_tree_workspace(256, 15, 151936, 64) > 8 << 20
+    assert status("ddt_build_tree_noalloc", *args(**big)) == ddt.DDT_ERR_WORKSPACE
+    assert "static" in L.ddt_last_error().decode()
 
 
 def test_build_tree_validation():

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -93,6 +95,60 @@ int ddt_build_tree(const void* draft_logits, int dt, int n, int L, int V, int B,
   return hip_status(ddt::launch_build_tree(draft_logits, dt, n, L, V, B, plan, root_token, tok, parent, depth,
                                            score, anc, ws, static_cast<hipStream_t>(stream)),
                     "ddt_build_tree");
+}
+
+// ---------------------------------------------------------------- tree build, no workspace argument
+// For callers that cannot allocate (code under graph capture, tight serving loops): the
+// tree build's scratch lives in a file-scope device array.  Its host-side name is not a
+// device address; the address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that pointer is handed to kernels.
+namespace {
+constexpr size_t kBuildScratchBytes = size_t(8) << 20;  // 8 MiB per device
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kBuildScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "ddt_build_tree_noalloc: hipGetDevice");
+  DDT_CHECK(dev >= 0 && dev < kMaxDevices, DDT_ERR_ARG, "ddt_build_tree_noalloc: device %d above %d", dev,
+            kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "ddt_build_tree_noalloc: hipGetSymbolAddress");
+    DDT_CHECK(p != nullptr, DDT_ERR_HIP, "ddt_build_tree_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DDT_OK;
+}
+}  // namespace
+
+size_t ddt_build_tree_noalloc_max_scratch(void) { return kBuildScratchBytes; }
+
+int ddt_build_tree_noalloc(const void* draft_logits, int dt, int n, int L, int V, int B, int K,
+                           const int32_t* root_token, int32_t* tok, int32_t* parent, int32_t* depth, float* score,
+                           uint64_t* anc, void* stream) {
+  // the same host-side checks as ddt_build_tree, all before the first HIP call
+  DDT_NEED(draft_logits); DDT_NEED(root_token); DDT_NEED(tok); DDT_NEED(parent);
+  DDT_NEED(depth); DDT_NEED(score); DDT_NEED(anc);
+  DDT_CHECK(dt_ok(dt), DDT_ERR_UNSUPPORTED, "ddt_build_tree_noalloc: dtype %d", dt);
+  ddt::BuildPlan plan;
+  const int st = build_args(n, L, V, B, K, &plan);
+  if (st != DDT_OK) return st;
+  DDT_CHECK(plan.total <= kBuildScratchBytes, DDT_ERR_WORKSPACE,
+            "ddt_build_tree_noalloc: needs %zu bytes of scratch, above the static %zu (n=%d L=%d V=%d K=%d)",
+            plan.total, kBuildScratchBytes, n, L, V, K);
+  void* ws = nullptr;
+  const int sa = scratch_address(&ws);
+  if (sa != DDT_OK) return sa;
+  return hip_status(ddt::launch_build_tree(draft_logits, dt, n, L, V, B, plan, root_token, tok, parent, depth,
+                                           score, anc, ws, static_cast<hipStream_t>(stream)),
+                    "ddt_build_tree_noalloc");
 }
 
 // ---------------------------------------------------------------- tree attention

@@ -19,6 +19,7 @@ DDT_F32, DDT_BF16 = 0, 1
 
 EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_build_tree_workspace", "ddt_build_tree",
+           "ddt_build_tree_noalloc_max_scratch", "ddt_build_tree_noalloc",
            "ddt_tree_attn_workspace", "ddt_tree_attn",
            "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope", "ddt_tree_rope",
            "ddt_tree_attn_paged_workspace", "ddt_tree_attn_paged", "ddt_commit_paged",
@@ -71,6 +72,8 @@ def lib():
         "ddt_abi_version": (I, []),
         "ddt_build_tree_workspace": (Z, [I, I, I, I, I]),
         "ddt_build_tree": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]),
+        "ddt_build_tree_noalloc_max_scratch": (Z, []),
+        "ddt_build_tree_noalloc": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P]),
         "ddt_tree_attn_workspace": (Z, [I, I, I, I, I, I, I]),
         "ddt_tree_attn": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_tree_attn_rope_workspace": (Z, [I, I, I, I, I, I, I]),
@@ -188,6 +191,25 @@ def build_tree(draft_logits, B, root_token, K=0, ws=None, out=None):
         _ptr(draft_logits), _dt(draft_logits), n, L, V, B, K, _ptr(root_token), _ptr(out["tok"]),
         _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc"]),
         _ptr(w), w.numel() * w.element_size(), _stream(dev)))
+    return out
+
+
+def build_tree_noalloc(draft_logits, B, root_token, K=0, out=None):
+    """build_tree without a workspace: the library's static per-device scratch (for callers
+    that cannot allocate; calls on one device must not overlap)."""
+    _gpu(draft_logits, root_token)
+    n, L, V = draft_logits.shape
+    dev = draft_logits.device
+    T = B + 1
+    if out is None:
+        out = {"tok": torch.empty(n, T, dtype=torch.int32, device=dev),
+               "parent": torch.empty(n, T, dtype=torch.int32, device=dev),
+               "depth": torch.empty(n, T, dtype=torch.int32, device=dev),
+               "score": torch.empty(n, T, dtype=torch.float32, device=dev),
+               "anc": torch.empty(n, T, dtype=torch.int64, device=dev)}
+    _check("ddt_build_tree_noalloc", lib().ddt_build_tree_noalloc(
+        _ptr(draft_logits), _dt(draft_logits), n, L, V, B, K, _ptr(root_token), _ptr(out["tok"]),
+        _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc"]), _stream(dev)))
     return out
 
 
