@@ -31,7 +31,8 @@ def run_case(seed, n, B, L, H, dk, W, dtype, kind="random", check_heads=None):
         for s in range(n):
             dep = [0]
             for i in range(1, B + 1):
-                cands = [j for j in range(max(0, i - 2), i) if dep[j] < L]
+                cands = [j for j in range(max(0, i - 2), i) if dep[j] < L] or \
+                    [j for j in range(i) if dep[j] < L]
                 p = int(cands[rng.integers(0, len(cands))])
                 parents[s, i] = p
                 dep.append(dep[p] + 1)
