@@ -18,7 +18,7 @@ replayed W + K times: `value` is the K timed replays, the same work without the
 launch gaps between calls (every length is read on the device, so each replay is a
 new round that continues from the state the previous one left).
 
-    python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu] [--variants]
+    python bench.py [--steps K] [--warmup W] [--prefix P] [--no-cpu] [--no-variants] [--no-graph]
     python bench.py --kernel-configs      (per-config kernel figures, one JSON line each)
 """
 
@@ -58,9 +58,9 @@ def parse():
     ap.add_argument("--kernel-configs", action="store_true",
                     help="instead of the step line: per-config kernel figures (tree build, tree attention at "
                          "8K/32K/128K, the full step at 16K), one JSON line each")
-    ap.add_argument("--variants", action="store_true",
-                    help="also time the step with GDN replay, RoPE in attention, paged KV and the sampled walk "
-                         "(after the main measurement; reported under 'variants')")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the variants (GDN replay on commit, RoPE in attention, paged KV with the sampled "
+                         "walk) timed after the main measurement and reported under 'variants'")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -79,66 +79,119 @@ def src_hash(name):
     return code_hash(open(path).read())
 
 
-def algorithmic(cfg, prefix_now):
-    """Algorithmic HBM bytes (and flops) per launch of each call, for the current prefix."""
+def algorithmic(cfg, prefix_now, rows_per_round):
+    """Algorithmic HBM bytes (and flops) per launch of each call, for the current prefix.
+    rows_per_round: rows committed per round over all sequences (sum of acc_len + 1)."""
     n, T, V, L = cfg.n, cfg.T, cfg.V, cfg.L
     kv = n * cfg.Hkv * (prefix_now + T) * cfg.D * 2 * 2                  # K and V, bf16
     attn_io = 2 * n * T * cfg.Hq * cfg.D * 2                              # q in, out
     attn_flops = 4.0 * n * T * cfg.Hq * cfg.D * (prefix_now + T)           # QK^T + PV over all keys
     state = cfg.H * cfg.dk * cfg.dk * 4
-    gdn = (n * T * state                                                  # S_scratch written
-           + n * state                                                    # committed S read
-           + n * T * cfg.C * 2                                            # x read
-           + n * (cfg.W - 1) * cfg.C * 2                                  # committed conv state read
-           + n * T * (cfg.W - 1) * cfg.C * 2                              # conv scratch written
-           + 2 * n * T * cfg.H * cfg.dk * 2                               # v read, o written
-           + 2 * n * T * cfg.H * 4)                                       # beta, g
+    conv = (cfg.W - 1) * cfg.C * 2
+    inputs = (n * state                                                   # committed S read
+              + n * T * cfg.C * 2                                         # x read
+              + n * conv                                                  # committed conv state read
+              + 2 * n * T * cfg.H * cfg.dk * 2                            # v read, o written
+              + 2 * n * T * cfg.H * 4)                                    # beta, g
+    if cfg.replay:
+        gdn = inputs                                                      # no node state stored
+    else:
+        gdn = inputs + n * T * state + n * T * conv                       # S and conv scratch written
     build = n * L * V * 2 + n * T * 24
-    accept = n * T * V * 2
+    accept = n * T * V * (2 + 4 if cfg.sampled else 2)                    # (+ fp32 noise when sampled)
+    kv_rows = cfg.n_attn * rows_per_round * cfg.Hkv * cfg.D * 2 * 2 * 2   # k, v rows read + written
+    if cfg.replay:
+        # replay: committed S and conv rows read + written, the path rows' x, v, beta, g read
+        path = rows_per_round * (cfg.C * 2 + cfg.H * cfg.dk * 2 + cfg.H * 8)
+        commit = kv_rows + cfg.n_gdn * (2 * n * state + 2 * n * conv + path)
+    else:
+        commit = kv_rows + cfg.n_gdn * 2 * n * (state + conv)             # deepest row's S, conv: read + written
     return {"tree_attn": (kv + attn_io, attn_flops), "gdn_tree_step": (gdn, 0.0),
-            "build_tree": (build, 0.0), "tree_accept": (accept, 0.0)}
+            "build_tree": (build, 0.0), "tree_accept": (accept, 0.0), "commit": (int(commit), 0.0)}
 
 
-def cpu_baseline(cfg, prefix):
-    """Time the oracle on a bounded sample of the same workload; extrapolate to steps/s."""
+def cpu_baseline(step, a):
+    """The CPU oracle on sequence 0 of one round of the workload, all of it (tree build,
+    the 16 attention and 48 GDN layers, the walk, the commit), on the very inputs the GPU
+    reads at the start of that round (copied from the device before it; the copies and
+    the fp64 conversions are not timed).  The GPU then runs the same round and its
+    sequence-0 tree and walk are compared with the oracle's.  A step is n sequences, so
+    the oracle's steps/s is 1 / (n x its time for one sequence)."""
     import numpy as np
+    import torch
 
     from oracle import accept as oacc
     from oracle import attention as oattn
+    from oracle import commit as ocommit
     from oracle import gdn as ogdn
     from oracle import tree as otree
-    from tree_speculative_decoding_ddt_amd import synth
 
-    rng = np.random.default_rng(1)
-    z = synth.quantize(synth.draft_logits(rng, 1, cfg.L, cfg.V, 3.0, plant_p=0.6), "bf16")[1][0]
+    cfg, s = step.cfg, 0
+    torch.cuda.synchronize(step.dev)
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    P = int(step.prefix_len[s])
+    root = int(step.root_token[s])
+    z = f64(step.draft_logits[s])
+    y = f64(step.target_logits[s])
+    # snapshot in the storage dtype (host copies, converted to fp64 one layer at a time)
+    attn_in = [{k: lay[k][s].cpu() for k in ("q", "k_tree", "v_tree")} |
+               {"k_cache": lay["k_cache"][s, :, :P].cpu(), "v_cache": lay["v_cache"][s, :, :P].cpu()}
+               for lay in step.attn]
+    gdn_in = [{k: lay[k][s].cpu() for k in ("x", "v", "beta", "g", "S", "conv_state")} | {"conv_w": lay["conv_w"].cpu()}
+              for lay in step.gdn]
+    # the GPU's own round on those inputs
+    step()
+    torch.cuda.synchronize(step.dev)
+    gpu_tok, gpu_par = step.tree["tok"][s].cpu().numpy(), step.tree["parent"][s].cpu().numpy()
+    gpu_rows = step.acc["acc_rows"][s].cpu().numpy()
+
+    from threadpoolctl import threadpool_info
+    blas = [d.get("num_threads") for d in threadpool_info() if d.get("user_api") == "blas"]
+    t = {}
     t0 = time.perf_counter()
-    tree = otree.build_tree(z, cfg.B, 0)
-    t_build = time.perf_counter() - t0
-    at = synth.attention_inputs(rng, 1, cfg.T, cfg.Hq, cfg.Hkv, cfg.D, prefix)
-    at = {k: synth.quantize(v, "bf16")[1][0].astype(np.float64) for k, v in at.items()}
+    tree = otree.build_tree(z, cfg.B, root)
+    t["build"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oattn.tree_attention(at["q"], at["k_cache"], at["v_cache"], prefix, at["k_tree"], at["v_tree"], tree["anc"])
-    t_attn = time.perf_counter() - t0
-    del at
-    gi = synth.gdn_inputs(rng, 1, cfg.T, cfg.H, cfg.dk, cfg.dk, cfg.W)
-    t0 = time.perf_counter()
-    ogdn.gdn_tree_step(gi["x"][0], gi["conv_w"], gi["conv_state"][0], gi["v"][0], gi["beta"][0], gi["g"][0],
-                       gi["S"][0], tree["parent"], cfg.H, cfg.dk)
-    t_gdn = time.perf_counter() - t0
-    y = synth.quantize(synth.target_logits(rng, 1, cfg.T, cfg.V, 3.0, tree["depth"][None],
-                                           synth.draft_top1(z[None]), 0.7), "bf16")[1][0]
-    t0 = time.perf_counter()
-    oacc.tree_accept(y, tree["tok"], tree["parent"], cfg.L)
-    t_acc = time.perf_counter() - t0
-    per_seq = t_build + cfg.n_attn * t_attn + cfg.n_gdn * t_gdn + t_acc
-    t_step = cfg.n * per_seq
+    rows, acc, _ = oacc.tree_accept(y, tree["tok"], tree["parent"], cfg.L)
+    t["walk"] = time.perf_counter() - t0
+    path = [int(r) for r in rows[: acc + 1]]
+    t["attn"] = t["gdn"] = t["commit"] = 0.0
+    for lay in attn_in:
+        x = {k: v.float().numpy().astype(np.float64) for k, v in lay.items()}
+        t0 = time.perf_counter()
+        oattn.tree_attention(x["q"], x["k_cache"], x["v_cache"], P, x["k_tree"], x["v_tree"], tree["anc"])
+        t["attn"] += time.perf_counter() - t0
+        cap = np.zeros((cfg.Hkv, P + acc + 1, cfg.D))
+        kv = [dict(k_tree=x["k_tree"], v_tree=x["v_tree"], k_cache=np.concatenate([x["k_cache"], cap[:, P:]], 1),
+                   v_cache=np.concatenate([x["v_cache"], cap[:, P:]], 1))]
+        t0 = time.perf_counter()
+        ocommit.commit(rows, acc, P, kv, [], P + acc + 1)
+        t["commit"] += time.perf_counter() - t0
+        del x, kv
+    for lay in gdn_in:
+        x = {k: v.float().numpy().astype(np.float64) for k, v in lay.items()}
+        t0 = time.perf_counter()
+        o, S_scr, c_scr = ogdn.gdn_tree_step(x["x"], x["conv_w"], x["conv_state"], x["v"], x["beta"], x["g"], x["S"],
+                                             tree["parent"], cfg.H, cfg.dk)
+        t["gdn"] += time.perf_counter() - t0
+        gd = [dict(S_scratch=S_scr, S=x["S"], conv_scratch=c_scr, conv_state=x["conv_state"])]
+        t0 = time.perf_counter()
+        ocommit.commit(rows, acc, P, [], gd, P + acc + 1)
+        t["commit"] += time.perf_counter() - t0
+        del x, gd, S_scr
+    per_seq = sum(t.values())
+    agrees = bool(np.array_equal(gpu_tok, tree["tok"]) and np.array_equal(gpu_par, tree["parent"])
+                  and np.array_equal(gpu_rows, rows))
     cores = len(os.sched_getaffinity(0))
-    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": ("1 of %d sequences at the full shapes: tree build (%.2fs), 1 of %d attention layers at "
-                       "prefix %d (%.2fs), 1 of %d GDN layers (%.2fs), walk (%.2fs); step time extrapolated "
-                       "as %d x (build + %d attn + %d gdn + walk) = %.1fs; numpy fp64, BLAS on %d cores"
-                       % (cfg.n, t_build, cfg.n_attn, prefix, t_attn, cfg.n_gdn, t_gdn, t_acc, cfg.n, cfg.n_attn,
-                          cfg.n_gdn, t_step, cores))}
+    return {"value": 1.0 / (cfg.n * per_seq), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": ("sequence 0 of %d, whole round on the same inputs as the GPU round (copied from the device): "
+                       "tree build %.2fs, %d attention layers at prefix %d %.2fs, %d GDN layers %.2fs, walk %.2fs, "
+                       "commit %.2fs = %.1fs per sequence, 64 layers timed; step = %d sequences = %.1fs; numpy "
+                       "fp64, BLAS threads %s, %d host cores"
+                       % (cfg.n, t["build"], cfg.n_attn, P, t["attn"], cfg.n_gdn, t["gdn"], t["walk"], t["commit"],
+                          per_seq, cfg.n, cfg.n * per_seq, blas, cores)),
+            "blas_threads": blas[0] if blas else None,
+            "agrees_with_gpu_round": agrees, "accepted_seq0": int(acc)}
 
 
 def kernel_configs(a):
@@ -348,105 +401,109 @@ def main():
     ddt.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = HybridConfig(n=a.n, prefix=a.prefix,
-                       extra_cap=((4 if a.variants else 2) * a.steps + 2 * a.warmup + 6) * 16 + 64)
+    # every round commits at most L + 1 = 16 rows: room for the main rounds, the CPU
+    # leg's round and the two variants timed on this step object
+    rounds = 3 * (2 * (a.warmup + a.steps) + 2) + 4
+    cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=rounds * 16 + 64)
     step = HybridVerifyStep(cfg, dev)
     step.fill_random(seed=a.seed)
     print("bench: inputs ready (%.1f GB on device)" % (torch.cuda.memory_allocated(dev) / 1e9),
           file=sys.stderr, flush=True)
 
     names = ("build_tree", "tree_attn", "gdn_tree_step", "tree_accept", "commit")
-    ev = {k: [] for k in names}
 
-    def timed(name, fn):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        ev[name].append((s, e))
+    def measure(step, label):
+        """W untimed + K timed eager rounds with HIP events around every call, then the
+        round captured once in a HIP graph and replayed W + K times (the K replays give
+        steps/s).  Returns the per-kernel table, the rates and the prefixes seen."""
+        cfg = step.cfg
+        ev = {k: [] for k in names}
+        rows = torch.zeros((), dtype=torch.int64, device=dev)
 
-    def attn_call(lay):
-        if step.block_table is not None:
-            return lambda: ddt.tree_attn_paged(lay["q"], lay["k_cache"], lay["v_cache"], step.block_table,
-                                               step.prefix_len, lay["k_tree"], lay["v_tree"], step.tree["anc"],
-                                               ws=step.ws_attn, out=lay["out"])
-        if cfg.rope:
-            return lambda: ddt.tree_attn_rope(lay["q"], lay["k_new"], lay["v_new"], step.tree["depth"], cfg.rope[0],
-                                              cfg.rope[1], lay["k_cache"], lay["v_cache"], step.prefix_len,
-                                              step.tree["anc"], ws=step.ws_attn,
-                                              out={"o": lay["out"], "k_tree": lay["k_tree"], "v_tree": lay["v_tree"]})
-        return lambda: ddt.tree_attn(lay["q"], lay["k_cache"], lay["v_cache"], step.prefix_len, lay["k_tree"],
-                                     lay["v_tree"], step.tree["anc"], ws=step.ws_attn, out=lay["out"])
+        def timed(name, fn):
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()
+            fn()
+            e_.record()
+            ev[name].append((s_, e_))
 
-    def run_step(record):
-        if not record:
-            step()
-            return
-        timed("build_tree", step.build)
-        ia = ig = 0
-        for kind in step.pattern:
-            if kind == "attn":
-                lay = step.attn[ia]
-                ia += 1
-                timed("tree_attn", attn_call(lay))
-            else:
-                g = step.gdn[ig]
-                ig += 1
-                timed("gdn_tree_step", lambda: ddt.gdn_tree_step(g["x"], g["conv_w"], g["conv_state"], g["v"],
-                                                                 g["beta"], g["g"], g["S"], step.tree["parent"],
-                                                                 cfg.L, ws=step.ws_gdn, out=g["out"],
-                                                                 store_states=not cfg.replay))
-        timed("tree_accept", step.accept)
-        timed("commit", step.commit)
+        def attn_call(lay):
+            if step.block_table is not None:
+                return lambda: ddt.tree_attn_paged(lay["q"], lay["k_cache"], lay["v_cache"], step.block_table,
+                                                   step.prefix_len, lay["k_tree"], lay["v_tree"], step.tree["anc"],
+                                                   ws=step.ws_attn, out=lay["out"])
+            if cfg.rope:
+                return lambda: ddt.tree_attn_rope(lay["q"], lay["k_new"], lay["v_new"], step.tree["depth"],
+                                                  cfg.rope[0], cfg.rope[1], lay["k_cache"], lay["v_cache"],
+                                                  step.prefix_len, step.tree["anc"], ws=step.ws_attn,
+                                                  out={"o": lay["out"], "k_tree": lay["k_tree"],
+                                                       "v_tree": lay["v_tree"]})
+            return lambda: ddt.tree_attn(lay["q"], lay["k_cache"], lay["v_cache"], step.prefix_len, lay["k_tree"],
+                                         lay["v_tree"], step.tree["anc"], ws=step.ws_attn, out=lay["out"])
 
-    for _ in range(a.warmup):
-        run_step(False)
-    torch.cuda.synchronize(dev)
-    p0 = int(step.prefix_len.float().mean().item())
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        run_step(True)
-    torch.cuda.synchronize(dev)
-    dt = time.perf_counter() - t0
-    p1 = int(step.prefix_len.float().mean().item())
-    acc_mean = float(step.acc["acc_len"].float().mean().item())
+        def run_round():
+            timed("build_tree", step.build)
+            ia = ig = 0
+            for kind in step.pattern:
+                if kind == "attn":
+                    lay = step.attn[ia]
+                    ia += 1
+                    timed("tree_attn", attn_call(lay))
+                else:
+                    g = step.gdn[ig]
+                    ig += 1
+                    timed("gdn_tree_step", lambda: ddt.gdn_tree_step(
+                        g["x"], g["conv_w"], g["conv_state"], g["v"], g["beta"], g["g"], g["S"],
+                        step.tree["parent"], cfg.L, ws=step.ws_gdn, out=g["out"], store_states=not cfg.replay))
+            timed("tree_accept", step.accept)
+            timed("commit", step.commit)
+            rows.add_((step.acc["acc_len"].clamp(min=-1) + 1).sum())   # rows this round committed
 
-    # The same round captured once in a HIP graph and replayed (every length is read on
-    # the device, so a replay continues from the state the previous round left): the
-    # launch gaps of the eager rounds drop out, the work is identical.
-    graph_ok = not a.no_graph
-    if graph_ok:
-        try:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                step()
-        except RuntimeError as exc:  # capture refused: report the eager rounds instead
-            print("bench: HIP graph capture failed (%s); value from the eager rounds" % exc, file=sys.stderr,
-                  flush=True)
-            graph_ok = False
-            torch.cuda.synchronize(dev)
-    if graph_ok:
         for _ in range(a.warmup):
-            graph.replay()
+            step()
         torch.cuda.synchronize(dev)
-        tg = time.perf_counter()
+        p0 = int(step.prefix_len.float().mean().item())
+        t0 = time.perf_counter()
         for _ in range(a.steps):
-            graph.replay()
+            run_round()
         torch.cuda.synchronize(dev)
-        dtg = time.perf_counter() - tg
-        p2 = int(step.prefix_len.float().mean().item())
-        del graph
-    else:
-        dtg, p2 = dt, p1
+        dt = time.perf_counter() - t0
+        p1 = int(step.prefix_len.float().mean().item())
+        rows_per_round = float(rows.item()) / a.steps
 
-    alg = algorithmic(cfg, (p0 + p1) // 2)
-    kernels = {}
-    for k in names:
-        ms = [s.elapsed_time(e) for s, e in ev[k]]
-        per = sum(ms) / len(ms)
-        rec = {"ms_per_launch": round(per, 4), "launches_per_step": len(ms) // a.steps,
-               "ms_per_step": round(sum(ms) / a.steps, 4)}
-        if k in alg:
+        # The same round captured once in a HIP graph and replayed (every length is read on
+        # the device, so a replay continues from the state the previous round left): the
+        # launch gaps of the eager rounds drop out, the work is identical.
+        dtg, p2 = None, p1
+        if not a.no_graph:
+            try:
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    step()
+            except RuntimeError as exc:  # capture refused: report the eager rounds instead
+                print("bench: %s: HIP graph capture failed (%s); eager rounds only" % (label, exc),
+                      file=sys.stderr, flush=True)
+                graph = None
+                torch.cuda.synchronize(dev)
+            if graph is not None:
+                for _ in range(a.warmup):
+                    graph.replay()
+                torch.cuda.synchronize(dev)
+                tg = time.perf_counter()
+                for _ in range(a.steps):
+                    graph.replay()
+                torch.cuda.synchronize(dev)
+                dtg = time.perf_counter() - tg
+                p2 = int(step.prefix_len.float().mean().item())
+                del graph
+
+        alg = algorithmic(cfg, (p0 + p1) // 2, rows_per_round)
+        kernels = {}
+        for k in names:
+            ms = [s_.elapsed_time(e_) for s_, e_ in ev[k]]
+            per = sum(ms) / len(ms)
+            rec = {"ms_per_launch": round(per, 4), "launches_per_step": len(ms) // a.steps,
+                   "ms_per_step": round(sum(ms) / a.steps, 4)}
             b, fl = alg[k]
             rec["algorithmic_bytes"] = b
             rec["GBps"] = round(b / (per * 1e-3) / 1e9, 1)
@@ -454,81 +511,85 @@ def main():
             if fl:
                 rec["TFLOPps"] = round(fl / (per * 1e-3) / 1e12, 1)
                 rec["mfma_frac"] = round(rec["TFLOPps"] / BF16_PEAK_TFLOPS, 4)
-        kernels[k] = rec
-    dom = max(("gdn_tree_step", "tree_attn", "build_tree", "tree_accept"), key=lambda k: kernels[k]["ms_per_step"])
-    kd = kernels[dom]
-    if dom == "tree_attn":
-        roof = {"bound": "mfma", "achieved": kd["TFLOPps"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": kd["mfma_frac"]}
-    else:
-        roof = {"bound": "hbm", "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kd["hbm_frac"]}
-    roof["kernel"] = dom
-    roof["traffic"] = load_traffic(dom)
-    ka = kernels["tree_attn"]
-    kv_bytes = cfg.n * cfg.Hkv * ((p0 + p1) // 2 + cfg.T) * cfg.D * 4
-    attn = {"kv_bytes_per_launch": kv_bytes, "kv_GBps": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9, 1),
-            "kv_frac_of_hbm_peak": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "TFLOPps": ka.get("TFLOPps"), "mfma_frac": ka.get("mfma_frac")}
+            kernels[k] = rec
+        kernels["commit"]["rows_committed_per_round"] = round(rows_per_round, 2)
+        dom = max(("gdn_tree_step", "tree_attn", "build_tree", "tree_accept"),
+                  key=lambda k: kernels[k]["ms_per_step"])
+        kd = kernels[dom]
+        if dom == "tree_attn":
+            roof = {"bound": "mfma", "achieved": kd["TFLOPps"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": kd["mfma_frac"]}
+        else:
+            roof = {"bound": "hbm", "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": kd["hbm_frac"]}
+        roof["kernel"] = dom
+        ka = kernels["tree_attn"]
+        kv_bytes = cfg.n * cfg.Hkv * ((p0 + p1) // 2 + cfg.T) * cfg.D * 4
+        attn = {"kv_bytes_per_launch": kv_bytes,
+                "kv_GBps": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9, 1),
+                "kv_frac_of_hbm_peak": round(kv_bytes / (ka["ms_per_launch"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "TFLOPps": ka.get("TFLOPps"), "mfma_frac": ka.get("mfma_frac")}
+        return {"kernels": kernels, "roofline": roof, "tree_attn": attn, "dt_eager": dt, "dt_graph": dtg,
+                "prefix": (p0, p1, p2), "mean_accepted": float(step.acc["acc_len"].float().mean().item())}
 
-    # Variant: the same step with no per-node GDN state stored; the commit replays the
-    # accepted path on the committed state.  Reported beside the stored-state step.
-    # Second variant: also RoPE at prefix + depth inside the attention call (pre-rotation
-    # q and tree K/V in; rotate-half over all 256 channels, theta 10000).
-    # Third variant: the committed KV in pages of 16 positions scattered over a pool and the
-    # walk over sampled target tokens (a fresh step object with GDN replay, built after the
-    # others are released; temperature 1, noise drawn once).
+    main = measure(step, "main")
+    main["roofline"]["traffic"] = load_traffic(main["roofline"]["kernel"])
+
+    cpu = None
+    if not a.no_cpu:
+        print("bench: timing the CPU oracle on one whole sequence of a round (same inputs)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(step, a)
+
+    # Variants of the same step (the next rows of the path), each measured like the main
+    # step: the GDN tree step storing no node state with the commit replaying the accepted
+    # path; that plus RoPE at prefix + depth inside the attention call (pre-rotation q and
+    # tree K/V in; rotate-half over all 256 channels, theta 10000); and, on a fresh step
+    # object, the committed KV in pages of 16 positions scattered over a pool with the walk
+    # over sampled target tokens (temperature 1, noise drawn once).
     variant = None
-    if a.variants:
+    if not a.no_variants:
         variant = {}
 
-        def time_variant(vname):
-            for k in names:
-                ev[k].clear()
-            run_step(False)
-            torch.cuda.synchronize(dev)
-            t0 = time.perf_counter()
-            for _ in range(a.steps):
-                run_step(True)
-            torch.cuda.synchronize(dev)
-            dtv = time.perf_counter() - t0
+        def record(vname, m):
             variant[vname] = {
-                "steps_per_s": round(a.steps / dtv, 3), "ms_per_step": round(dtv / a.steps * 1e3, 3),
-                "kernels_ms_per_step": {k: round(sum(s.elapsed_time(e) for s, e in ev[k]) / a.steps, 4)
-                                        for k in names}}
+                "steps_per_s": round(a.steps / (m["dt_graph"] or m["dt_eager"]), 3),
+                "ms_per_step": round((m["dt_graph"] or m["dt_eager"]) / a.steps * 1e3, 3),
+                "eager_steps_per_s": round(a.steps / m["dt_eager"], 3),
+                "kernels": m["kernels"], "roofline": m["roofline"], "mean_accepted": round(m["mean_accepted"], 3)}
 
         for vname, mode in (("gdn_replay_on_commit", dict(replay=True)),
                             ("gdn_replay_and_rope_attention", dict(replay=True, rope=(cfg.D, 10000.0)))):
             step.set_mode(**mode)
-            time_variant(vname)
+            record(vname, measure(step, vname))
         step = None
         torch.cuda.empty_cache()
-        cfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=cfg.extra_cap, replay=True, page_size=16, sampled=True)
-        step = HybridVerifyStep(cfg, dev)
+        vcfg = HybridConfig(n=a.n, prefix=a.prefix, extra_cap=rounds * 16 + 64, replay=True, page_size=16,
+                            sampled=True)
+        step = HybridVerifyStep(vcfg, dev)
         step.fill_random(seed=a.seed)
-        time_variant("paged16_gdn_replay_sampled_walk")
+        record("paged16_gdn_replay_sampled_walk", measure(step, "paged"))
 
-    cpu = None
-    if not a.no_cpu:
-        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, a.prefix)
-
-    value = a.steps / dtg
+    dtg = main["dt_graph"]
+    value = a.steps / (dtg or main["dt_eager"])
+    p0, p1, p2 = main["prefix"]
     line = {
         "metric": "tree-verify steps/sec at B=64, 32K prefix; tree-attn KV GB/s vs HBM peak",
         "value": round(value, 3), "unit": "steps/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": round(dtg / a.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded device RNG draws)",
+        "ms_per_step": round((dtg or main["dt_eager"]) / a.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded device RNG draws)",
         "config": {"workload": "full hybrid verify step: 8 seqs, B=64, L=15, vocab 151936, prefix %d, "
                                "16 attn (24/4 heads, D 256) + 48 GDN (32 heads, dk=dv=128, C 8192, W 4) layers"
                                % a.prefix,
                    "global_batch": cfg.n, "seq_len": a.prefix, "parallelism": "single GPU"},
-        "roofline": roof, "tree_attn": attn, "kernels": kernels,
-        "timing": ("value and kernels: HIP events per call over K eager rounds" if not graph_ok else
+        "roofline": main["roofline"], "tree_attn": main["tree_attn"], "kernels": main["kernels"],
+        "timing": ("value and kernels: HIP events per call over K eager rounds" if dtg is None else
                    "value: K replays of one round captured in a HIP graph; kernels: HIP events per call "
                    "over K eager rounds run before it (the same work, launched one call at a time)"),
-        "eager": {"steps_per_s": round(a.steps / dt, 3), "ms_per_step": round(dt / a.steps * 1e3, 3),
-                  "prefix_during_timing": [p0, p1]},
-        "mean_accepted": round(acc_mean, 3), "prefix_during_timing": [p1, p2] if graph_ok else [p0, p1],
+        "eager": {"steps_per_s": round(a.steps / main["dt_eager"], 3),
+                  "ms_per_step": round(main["dt_eager"] / a.steps * 1e3, 3), "prefix_during_timing": [p0, p1]},
+        "mean_accepted": round(main["mean_accepted"], 3),
+        "prefix_during_timing": [p1, p2] if dtg is not None else [p0, p1],
         "cpu_baseline": cpu, "variants": variant,
     }
     print(json.dumps(line), flush=True)
