@@ -412,7 +412,7 @@ size_t gdn_workspace(int n, int T, int H, int dk) {
 }
 
 template <typename A, int DK>
-static void launch_gdn(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
+static hipError_t launch_gdn(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
                        const float* beta, const float* g, const float* S, float* S_scratch, void* o,
                        const int32_t* parent, int n, int T, int H, int C, int W, void* ws, hipStream_t st) {
   constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread
@@ -422,6 +422,12 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   float* qk = static_cast<float*>(ws);
   float* kq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + qk_b);
   int32_t* ord = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + qk_b + kq_b);
+  if (S_scratch == nullptr && conv_scratch == nullptr && sizeof(A) == 2) {
+    // no node state stored, bf16 activations: conv and delta rule in one kernel, in
+    // chunk form on the matrix cores (the fp32 configuration keeps the walk, whose
+    // rounding stays within its 1e-5 bound)
+    return launch_gdn_chunk(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, DK, W, DDT_BF16, st);
+  }
   const dim3 cgrid(n * T, (H + 256 / (DK / 4) - 1) / (256 / (DK / 4)));
   if (W == 4)
     hipLaunchKernelGGL((gdn_conv_kernel<A, DK, 4>), cgrid, dim3(256), 0, st, static_cast<const A*>(x), conv_w,
@@ -439,6 +445,7 @@ static void launch_gdn(const void* x, const float* conv_w, const void* conv_stat
   (void)attr;
   hipLaunchKernelGGL(kern, dim3(n * H, DK / R), dim3(256), smem, st, qk, kq, static_cast<const A*>(v), beta, g, S,
                      S_scratch, static_cast<A*>(o), ord, T, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
@@ -446,18 +453,16 @@ hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* 
                                 void* o, const int32_t* parent, int n, int T, int H, int dk, int C, int W,
                                 int act_dt, void* ws, hipStream_t st) {
 #define DDT_GDN(TY, DKV) \
-  launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H, C, W, ws, st)
+  return launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H, C, W, ws, st)
   if (act_dt == DDT_BF16) {
     if (dk == 32) DDT_GDN(uint16_t, 32);
-    else if (dk == 64) DDT_GDN(uint16_t, 64);
-    else DDT_GDN(uint16_t, 128);
-  } else {
-    if (dk == 32) DDT_GDN(float, 32);
-    else if (dk == 64) DDT_GDN(float, 64);
-    else DDT_GDN(float, 128);
+    if (dk == 64) DDT_GDN(uint16_t, 64);
+    DDT_GDN(uint16_t, 128);
   }
+  if (dk == 32) DDT_GDN(float, 32);
+  if (dk == 64) DDT_GDN(float, 64);
+  DDT_GDN(float, 128);
 #undef DDT_GDN
-  return hipGetLastError();
 }
 
 }  // namespace ddt

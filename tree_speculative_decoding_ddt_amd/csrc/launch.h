@@ -50,7 +50,9 @@ struct PagedKV {
   }
   // Rows of four wave-uniform positions: the four table entries come in through scalar
   // loads (lgkmcnt, so they do not join the vector-memory count of copies in flight),
-  // all issued before one wait.
+  // all issued before one wait.  The addresses are first copied into scratch SGPRs by
+  // scalar moves inside the asm, so each load reads SGPRs a scalar instruction wrote
+  // (whatever wrote the operands before, e.g. a v_readlane spill reload).
   __device__ __forceinline__ void rows_uniform4(int s, int h, int Hkv, const int (&p)[4], size_t (&out)[4]) const {
     const int32_t* e[4];
     int pu[4], id[4];
@@ -59,10 +61,12 @@ struct PagedKV {
       pu[i] = __builtin_amdgcn_readfirstlane(p[i]);
       e[i] = bt + (size_t)s * maxb + (pu[i] >> lps);
     }
+    uint64_t a0, a1, a2, a3;
     asm volatile(
+        "s_mov_b64 %4, %8\n\ts_mov_b64 %5, %9\n\ts_mov_b64 %6, %10\n\ts_mov_b64 %7, %11\n\t"
         "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\ts_load_dword %2, %6, 0x0\n\t"
         "s_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
-        : "=&s"(id[0]), "=&s"(id[1]), "=&s"(id[2]), "=&s"(id[3])
+        : "=&s"(id[0]), "=&s"(id[1]), "=&s"(id[2]), "=&s"(id[3]), "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3)
         : "s"(e[0]), "s"(e[1]), "s"(e[2]), "s"(e[3]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -90,6 +94,11 @@ hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* 
                                 const float* g, const float* S, float* S_scratch, void* o,
                                 const int32_t* parent, int n, int T, int H, int dk, int C,
                                 int W, int act_dt, void* ws, hipStream_t st);
+
+// ---- GDN tree step without stored node states (short conv included), chunk form
+hipError_t launch_gdn_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
+                            const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
+                            int T, int H, int dk, int W, int act_dt, hipStream_t st);
 
 // ---- GDN replay on commit
 hipError_t launch_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,

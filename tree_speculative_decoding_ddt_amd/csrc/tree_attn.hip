@@ -39,7 +39,7 @@ constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
 constexpr int kAttnMinSplit = 512;  // fewest prefix keys per split: a split's (lse, O) partials
                                     // cost about the traffic of 400 keys of K/V, but with few
                                     // sequences more splits fill more of the 256 CUs
-constexpr float kOver = 64.f;    // largest score above the softmax reference (log2 units)
+constexpr float kMaxRowSum = 0x1p64f;  // a pass whose row sum reaches this is redone (see below)
 constexpr int kPageTab = 1024;   // block-table entries a paged split stages in LDS
 
 // ------------------------------------------------------------------ scalar path
@@ -125,16 +125,24 @@ __global__ void __launch_bounds__(64) attn_scalar_kernel(const T* __restrict__ q
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at LDS
-// byte address lds_addr + 16*l.  Written as inline asm so that the compiler does not
-// treat the in-flight copy as aliasing every later LDS read (it would wait for all
-// outstanding copies before each read); the kernel counts vmcnt itself.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane
+// l's bytes land at LDS byte address lds_addr + 16*l.  Written as inline asm so that the
+// compiler does not treat the in-flight copy as aliasing every later LDS read (it would
+// wait for all outstanding copies before each read); the kernel counts vmcnt itself.
+// The source is a wave-uniform row base p plus this lane's byte offset voff, so the
+// address sums stay in scalar registers (no per-copy vector arithmetic).  The base is
+// first copied into scratch SGPRs by a scalar move inside the asm, so the load reads
+// SGPRs last written by a scalar instruction: an SGPR written by a vector instruction
+// (e.g. a spill reload with v_readlane) needs 5 wait states before a vector-memory
+// instruction reads it, and the compiler does not insert them around inline asm.
+__device__ __forceinline__ void dma16s(const void* p, uint32_t voff, uint32_t lds_addr) {
+  uint64_t tmp;
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_addr)
+      "s_mov_b64 %0, %3\n\ts_mov_b32 %1, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %0 offset:0\n\ts_mov_b32 m0, %1"
+      : "=&s"(tmp), "=&s"(saved)
+      : "v"(voff), "s"(p), "s"(lds_addr)
       : "memory");
 }
 // Workgroup barrier without a memory fence: copies into other LDS stages stay in flight.
@@ -159,8 +167,7 @@ __device__ __forceinline__ void dispatch_count(int n, F& f) {
 // ring holds tile it, whose S = K Q^T, softmax and O += V^T P^T all run in iteration it,
 // and tiles it+1..it+3 whose copies are in flight (three tiles ahead keep more bytes
 // in flight than deferring tile it's P.V to the next iteration and prefetching two).
-// The two waves of a SIMD overlap one's softmax with the other's matrix-core products;
-// a wave raises its priority for its product phases.
+// The two waves of a SIMD overlap one's softmax with the other's matrix-core products.
 template <int D, int NT, int NW, int PK, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k_cache,
@@ -269,8 +276,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
           if (pre) e = prow[k] * D;
         const uint32_t voff = (uint32_t)ln << 4;  // this lane's 16-byte chunk
         const uint32_t m = kb + (uint32_t)(row * RS);
-        dma16(reinterpret_cast<const uint8_t*>(Kg + e) + voff, m);
-        dma16(reinterpret_cast<const uint8_t*>(Vg + e) + voff, m + TILE);
+        dma16s(Kg + e, voff, m);
+        dma16s(Vg + e, voff, m + TILE);
       }
     }
   };
@@ -327,7 +334,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   f32x4 O[NT][DB];
   float m[NT];    // softmax reference of the row (log2 units), fixed for a pass
   float l[NT];    // this lane's share of the row sum (8 of the row's keys per tile)
-  float mxs[NT];  // largest exponent argument (score in log2 units - m) of the pass (sets a redo's m)
+  float mxs[NT];  // largest exponent argument (score in log2 units - m) of a tracking pass
   bf16x8 Pp[NT];  // P of the current tile, B operand of its P.V product
 
   // S^T blocks: Sacc[j][h] lane (l16, q4) element e = key 16h + 4*q4 + e of row l16.
@@ -407,12 +414,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
         sv[4 * h + e] = x;
       }
   };
-  // P = 2^(score*scale*log2e - m) against the fixed reference; `over` marks an exponent
-  // above kOver (P could overflow: the pass is redone with a larger reference)
-  bool over = false;
-  auto softmax = [&](auto NAc, const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend,
+  // P = 2^(score*scale*log2e - m) against the pass's fixed reference.  TRACK (only in a
+  // redo, see below) also records the largest exponent argument of each row.
+  auto softmax = [&](auto NAc, auto TRc, const f32x4 (&Sacc)[NT][2], bool masked, bool tree, int kb, int kend,
                      bf16x8 (&Pout)[NT]) {
     constexpr int NA = decltype(NAc)::value;
+    constexpr bool TRACK = decltype(TRc)::value;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       float sv[8];
@@ -422,11 +429,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       float a[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] = fmaf(sv[e], sl2, -m[j]);
-      float mx = a[0];
+      if constexpr (TRACK) {
+        float mx = a[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, a[e]);
-      mxs[j] = fmaxf(mxs[j], mx);
-      over |= mx > kOver;
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, a[e]);
+        mxs[j] = fmaxf(mxs[j], mx);
+      }
       float r = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -455,77 +463,94 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 #pragma unroll
     for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // The passes over this split's key tiles, for a wave that owns NA valid 16-row tiles
+  // One pass over this split's key tiles, for a wave that owns NA valid 16-row tiles
   // (its first NA; the rest lie past the last row): tiles past the rows run no products
   // (the K/V operand reads, shared by a wave's tiles, are skipped only when NA = 0), but
   // the wave still copies its share of every K/V tile and meets every barrier.
+  auto one_pass = [&](auto NAc, auto TRc, bool first) __attribute__((always_inline)) {
+    constexpr int NA = decltype(NAc)::value;
+    issue(0);  // every wave enters a pass with no copy in flight
+    if (n_all > 1) issue(1);
+    if (n_all > 2) issue(2);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      l[j] = 0.f;
+      mxs[j] = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // tile 0: S, then (first pass) the reference from its exact row max
+    {
+      sync_tile(0);
+      const bool tree = 0 >= n_pre;
+      const int kb = tree ? 0 : k_beg;
+      const int kend = tree ? Tn : k_end;
+      const bool masked = tree || kb + NK > kend;
+      f32x4 Sacc[NT][2];
+      s_phase(NAc, 0, Sacc);
+      if (first) {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+          float sv[8];
+          scores(Sacc, j, masked, tree, kb, kend, sv);
+          float mx = sv[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+          m[j] = row_max(mx) * sl2;  // every row sees at least one key of its first tile
+        }
+      }
+      softmax(NAc, TRc, Sacc, masked, tree, kb, kend, Pp);
+      pv_phase(NAc, 0);
+    }
+    int it = 1;
+    for (; it < n_full; ++it) {
+      sync_tile(it);
+      f32x4 Sacc[NT][2];
+      s_phase(NAc, it % NST, Sacc);
+      softmax(NAc, TRc, Sacc, false, false, 0, 0, Pp);
+      pv_phase(NAc, it % NST);
+    }
+    for (; it < n_all; ++it) {  // the prefix tail and the tree tiles, under the mask
+      sync_tile(it);
+      const bool tree = it >= n_pre;
+      const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
+      const int kend = tree ? Tn : k_end;
+      f32x4 Sacc[NT][2];
+      s_phase(NAc, it % NST, Sacc);
+      softmax(NAc, TRc, Sacc, true, tree, kb, kend, Pp);
+      pv_phase(NAc, it % NST);
+    }
+  };
+  // The reference of a row is the exact maximum of its first key tile, so later keys may
+  // lie above it.  A pass whose row sum l reached 2^64 (or overflowed) may have lost
+  // precision or range in P and O; it is redone, rarely and only for such inputs: a pass
+  // that tracks the largest exponent argument of every row, then a pass with every
+  // reference at the true row maximum (all exponents <= 0, so l <= the key count).
   auto passes = [&](auto NAc) {
     constexpr int NA = decltype(NAc)::value;
-    for (int pass = 0; n_all > 0; ++pass) {
-      issue(0);  // every wave enters a pass with no copy in flight
-      if (n_all > 1) issue(1);
-      if (n_all > 2) issue(2);
+    if (n_all == 0) return;
+    for (int pass = 0; pass < 3; ++pass) {
+      // pass 0: first-tile references; 1 (redo only): max tracking; 2: true maxima
+      if (pass == 1) one_pass(NAc, IntC<1>{}, false);
+      else one_pass(NAc, IntC<0>{}, pass == 0);
+      if (pass == 1) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        l[j] = 0.f;
-        mxs[j] = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) O[j][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NA; ++j) m[j] += fmaxf(row_max(mxs[j]), 0.f);
+        __syncthreads();
+        continue;
       }
-      // tile 0: S, then (first pass) the reference from its exact row max
-      {
-        sync_tile(0);
-        const bool tree = 0 >= n_pre;
-        const int kb = tree ? 0 : k_beg;
-        const int kend = tree ? Tn : k_end;
-        const bool masked = tree || kb + NK > kend;
-        f32x4 Sacc[NT][2];
-        s_phase(NAc, 0, Sacc);
-        if (pass == 0) {
+      if (pass == 2) break;
+      bool bad = false;
 #pragma unroll
-          for (int j = 0; j < NA; ++j) {
-            float sv[8];
-            scores(Sacc, j, masked, tree, kb, kend, sv);
-            float mx = sv[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-            m[j] = row_max(mx) * sl2;  // every row sees at least one key of its first tile
-          }
-        }
-        softmax(NAc, Sacc, masked, tree, kb, kend, Pp);
-        pv_phase(NAc, 0);
+      for (int j = 0; j < NA; ++j) {
+        float lt = l[j];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        bad |= !(lt < kMaxRowSum);
       }
-      int it = 1;
-      for (; it < n_full; ++it) {
-        sync_tile(it);
-        f32x4 Sacc[NT][2];
-        __builtin_amdgcn_s_setprio(1);
-        s_phase(NAc, it % NST, Sacc);
-        __builtin_amdgcn_s_setprio(0);
-        softmax(NAc, Sacc, false, false, 0, 0, Pp);
-        __builtin_amdgcn_s_setprio(1);
-        pv_phase(NAc, it % NST);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      for (; it < n_all; ++it) {  // the prefix tail and the tree tiles, under the mask
-        sync_tile(it);
-        const bool tree = it >= n_pre;
-        const int kb = tree ? (it - n_pre) * NK : k_beg + it * NK;
-        const int kend = tree ? Tn : k_end;
-        f32x4 Sacc[NT][2];
-        s_phase(NAc, it % NST, Sacc);
-        softmax(NAc, Sacc, true, tree, kb, kend, Pp);
-        pv_phase(NAc, it % NST);
-      }
-      // one block-wide vote per pass: redo with references at the true row maxima
-      if (__any(over)) redo_vote = pass + 1;
-      __syncthreads();
-      const bool redo = redo_vote == pass + 1;
-      __syncthreads();
-      if (!redo) break;
-      over = false;
-#pragma unroll
-      for (int j = 0; j < NA; ++j) m[j] += fmaxf(row_max(mxs[j]), 0.f);
+      if (__any(bad)) redo_vote = 1;
+      __syncthreads();  // the vote, and every wave done with the last pass's stages
+      if (redo_vote == 0) break;
     }
   };
   int na = 0;  // wave-uniform: the valid tiles are a prefix of tile[]
