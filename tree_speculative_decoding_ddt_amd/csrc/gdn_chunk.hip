@@ -81,74 +81,135 @@ template <> __device__ __forceinline__ void load8<float>(const float* p, float (
 }
 }  // namespace
 
-constexpr int kChunkMaxTT = 5;   // 16-row tiles of nodes: T <= 80
+constexpr int kChunkMaxTT = 5;   // 16-row tiles of nodes
 constexpr int kChunkMaxW = 8;    // conv width
 constexpr int kChunkMaxT = 65;   // nodes (budget <= 64 plus the root)
 
-// LDS layout (bytes) for T nodes (row stride RSB = 2*dk + 16 for bf16 rows):
-//   KQ     K hi, K lo, Q hi, Q lo: [T+1] rows each (row T stays zero: the rows of a
-//          16-row tile past the last node read it); after P1 the right-hand sides / w
-//          [T][dv] and the o base [T][dv] (fp32) take this area
-//   scalars parent, g, beta, G, M_tt, depth, depth order, depth histogram/fill [T];
-//          depth starts [T+1]; conv windows [T][8] int
-//   big    during the conv: the x stage [T + W-1][2*dk] (act); then R [T][TS] fp32
-//          (r_tj, TS = T rounded up to 4) and the records [T][T] x 16 B (P2 on)
+// Node t keeps one record per proper ancestor, nearest first: slot t(t-1)/2 + k holds
+// its (k+1)-th ancestor (k = 0: the parent).  Parents precede their children, so t has
+// at most t ancestors and T(T-1)/2 slots hold every record.
+__host__ __device__ inline int rec_base(int t) { return t * (t - 1) / 2; }
+
+// LDS layout (bytes) for T nodes (bf16 row stride RSB = 2*dk + 16):
+//   KQ      K hi, K lo, Q hi, Q lo: [T+1] rows each (row T stays zero: the rows of a
+//           16-row tile past the last node read it); from P2 on, w [T][WS] and the o base
+//           [T][WS] (fp32, WS = dv + 4) take this area
+//   scalars parent, g, beta, G, M_tt, depth, nodes per depth, depth order [T]; first
+//           position of each depth [T+1]; the largest depth
+//   win     conv windows [T][8]: stage rows, tap W-1-b reads entry b
+//   rec     the records [T(T-1)/2] x (ancestor row, r_tj then beta_t r_tj k_j.k_t,
+//           r_tj k_j.q_t, unused)
+//   stage   x rows [T][2*dk] (q part, k part) then the committed conv rows [W-1][2*dk],
+//           padded to whole 4 KB rounds of the block's LDS DMA
 struct ChunkLayout {
-  int TS, rows, off_sc, off_win, off_big, off_rec, total;
+  int rows, WS, off_sc, off_win, off_rec, off_stage, total;
 };
-__host__ __device__ inline ChunkLayout chunk_layout(int T, int dk, int W, int esize) {
+__host__ __device__ inline ChunkLayout chunk_layout(int T, int dk, int W) {
   ChunkLayout c;
   const int RSB = 2 * dk + 16;
-  c.TS = (T + 3) / 4 * 4;
   c.rows = T + 1;
-  const int kq = 4 * c.rows * RSB, st = 2 * T * dk * 4;
-  c.off_sc = ((kq > st ? kq : st) + 15) / 16 * 16;
-  c.off_win = c.off_sc + ((8 * T + T + 1) * 4 + 15) / 16 * 16;
-  c.off_big = c.off_win + T * kChunkMaxW * 4;
-  const int stage = (T + W - 1) * 2 * dk * esize;
-  c.off_rec = c.off_big + (T * c.TS * 4 + 15) / 16 * 16;
-  const int after = c.off_rec + T * T * 16;
-  c.total = (c.off_big + stage > after) ? c.off_big + stage : after;
+  c.WS = dk + 4;
+  const int kq = 4 * c.rows * RSB, wo = 2 * T * c.WS * 4;
+  c.off_sc = ((kq > wo ? kq : wo) + 15) / 16 * 16;
+  c.off_win = c.off_sc + (9 * ((T + 3) & ~3) + 8) * 4;
+  c.off_rec = c.off_win + T * kChunkMaxW * 4;
+  c.off_stage = c.off_rec + rec_base(T) * 16;
+  c.total = c.off_stage + ((T + W - 1) * 2 * dk * 2 + 4095) / 4096 * 4096;  // whole DMA rounds
   return c;
 }
 
-template <typename A, int DK>
-__global__ void __launch_bounds__(256) gdn_chunk_kernel(const A* __restrict__ x, const float* __restrict__ conv_w,
-                                                        const A* __restrict__ conv_state, const A* __restrict__ v,
-                                                        const float* __restrict__ beta, const float* __restrict__ g,
-                                                        const float* __restrict__ S, A* __restrict__ o,
-                                                        const int32_t* __restrict__ parent, int Tn, int H, int W) {
+// WT = 4: conv width exactly 4; WT = 8: any width up to 8 (taps past W weigh 0)
+template <int DK, int WT>
+__global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restrict__ x, const float* __restrict__ conv_w,
+                                                        const uint16_t* __restrict__ conv_state,
+                                                        const uint16_t* __restrict__ v, const float* __restrict__ beta,
+                                                        const float* __restrict__ g, const float* __restrict__ S,
+                                                        uint16_t* __restrict__ o, const int32_t* __restrict__ parent,
+                                                        int Tn, int H, int W) {
   constexpr int DV = DK, RSB = 2 * DK + 16, NCS = DK / 32, NRT = DV / 16;
-  constexpr int RTW = (NRT + 3) / 4;  // 16-column tiles of S0 per wave
-  constexpr int NG = DK / 8;          // lanes per (node, q or k) in the conv: 8 channels each
-  constexpr int NPR = 256 / (2 * NG); // nodes per conv round
-  constexpr int CPW = DV / 4;         // solve: columns a wave owns
-  constexpr int LPN = CPW / 2;        // lanes per node (2 columns per lane)
-  constexpr int NPW = 64 / LPN;       // nodes of one depth per wave step
-  constexpr int ROW8 = 2 * DK / 8;    // 16-byte chunks (8 activations) of a staged row
+  constexpr int RTW = (NRT + 3) / 4;   // 16-row tiles of S0 per wave
+  constexpr int NG = DK / 8;           // conv: lanes per (node, q or k part), 8 channels each
+  constexpr int NPR = 256 / (2 * NG);  // conv: nodes per pass of the block
+  constexpr int ROW8 = 2 * DK / 8;     // 16-byte chunks of a staged row
+  constexpr int kStageIt = ((kChunkMaxT + kChunkMaxW - 1) * ROW8 + 255) / 256;
+  constexpr int CPW = DV / 4;          // solve: columns a wave owns
+  constexpr int LPN = CPW / 4;         // solve: lanes per node, 4 columns each
+  constexpr int NGP = 64 / LPN;        // solve: nodes a wave holds side by side
+  constexpr int NS = (kChunkMaxT + NGP - 1) / NGP;  // solve: node slots per lane
   extern __shared__ __align__(16) uint8_t lds[];
   const int s = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
   const int C = 2 * H * DK;
-  const ChunkLayout L = chunk_layout(Tn, DK, W, (int)sizeof(A));
-  const int NTT = (Tn + 15) / 16, TS = L.TS, RW = L.rows;
+  const ChunkLayout L = chunk_layout(Tn, DK, W);
+  const int NTT = (Tn + 15) / 16, RW = L.rows, WS = L.WS;
+  const int TP4 = (Tn + 3) & ~3;  // scalar arrays start 16-byte aligned
   int* par = reinterpret_cast<int*>(lds + L.off_sc);
-  float* gg = reinterpret_cast<float*>(par + Tn);
-  float* be = gg + Tn;
-  float* Gam = be + Tn;
-  float* Md = Gam + Tn;
-  int* dep = reinterpret_cast<int*>(Md + Tn);
-  int* ord = dep + Tn;
-  int* cnt = ord + Tn;     // depth histogram, then the fill counters
-  int* lstart = cnt + Tn;  // [Tn + 1]
+  float* gg = reinterpret_cast<float*>(par + TP4);
+  float* be = gg + TP4;
+  float* Gam = be + TP4;
+  float* Md = Gam + TP4;
+  int* dep = reinterpret_cast<int*>(Md + TP4);
+  int* cnt = dep + TP4;     // nodes per depth, then the fill counters of the depth order
+  int* ord = cnt + TP4;     // the nodes by depth
+  int* lstart = ord + TP4;  // [T + 1]: position of the first node of each depth in ord
+  int* maxdep = lstart + TP4 + 4;
   int* win = reinterpret_cast<int*>(lds + L.off_win);
-  A* stage = reinterpret_cast<A*>(lds + L.off_big);  // [Tn + W-1][2*DK]: x rows, then conv rows
-  float* Rm = reinterpret_cast<float*>(lds + L.off_big);
-  float4* rec = reinterpret_cast<float4*>(lds + L.off_rec);  // [t][depth]: (row, A_tj, M_tj, -)
+  float4* rec = reinterpret_cast<float4*>(lds + L.off_rec);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + L.off_stage);
 
-  // ---- P0: every global load of the block first (addresses clamped into range)
+  // ---- P0.  The node scalars and, by LDS DMA, the stage first; then (after the first
+  // barrier, which waits for those) S0 and v, which arrive during the walk and the conv.
+  // Every address is clamped into range.
+  const int tn = min(tid, Tn - 1);
+  const int pr = parent[(size_t)s * Tn + tn];
+  const float gr = g[((size_t)s * Tn + tn) * H + h], br = beta[((size_t)s * Tn + tn) * H + h];
+  // the stage, 16-byte chunk idx = 256*k + tid: a wave fills 1 KB at a time; chunks past
+  // the last repeat it into the stage's padding
+  const int nst = (Tn + W - 1) * ROW8;
+#pragma unroll
+  for (int k = 0; k < kStageIt; ++k) {
+    if (256 * k >= nst) break;
+    const int idx = min(tid + 256 * k, nst - 1);
+    const int row = idx / ROW8, ch = idx % ROW8;
+    const int chan = ch < ROW8 / 2 ? h * DK + 8 * ch : H * DK + h * DK + 8 * (ch - ROW8 / 2);
+    const uint16_t* src = row < Tn ? x + ((size_t)s * Tn + row) * C + chan
+                                   : conv_state + ((size_t)s * (W - 1) + (row - Tn)) * C + chan;
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                              reinterpret_cast<uintptr_t>(stage + (size_t)(256 * k + 64 * wave) * 8)),
+                                     16, 0, 0);
+  }
+  // this thread's conv channels: 8 of the head's q (half 0) or k (half 1) channels
+  const int cg = tid % NG, half = (tid / NG) & 1, tsub = tid / (2 * NG);
+  const int c0 = half * H * DK + h * DK + 8 * cg;  // channel in x
+  const int s0 = half * DK + 8 * cg;               // channel in a staged row
+  float cw[8][WT];
+  if constexpr (WT == 4) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4 q = *reinterpret_cast<const float4*>(conv_w + (size_t)(c0 + e) * 4);
+      cw[e][0] = q.x; cw[e][1] = q.y; cw[e][2] = q.z; cw[e][3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < WT; ++c) cw[e][c] = conv_w[(size_t)(c0 + e) * W + min(c, W - 1)];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < WT; ++c) cw[e][c] = c < W ? cw[e][c] : 0.f;
+  }
+  par[tn] = pr;
+  gg[tn] = gr;
+  be[tn] = br;
+  cnt[tn] = 0;
+  if (tid < 4 * (RSB / 16))  // row T of K hi, K lo, Q hi, Q lo: zero
+    *reinterpret_cast<uint4*>(lds + (tid / (RSB / 16)) * RW * RSB + Tn * RSB + (tid % (RSB / 16)) * 16) =
+        make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  // S0 rows r = 16*rt + l16, columns 32*cs + 8*q4 .. +7: the A operands of S0 [K|Q]
   const float* S0 = S + ((size_t)s * H + h) * DV * DK;
   float sop[RTW][NCS][8];
 #pragma unroll
@@ -157,175 +218,118 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const A* __restrict__ x,
 #pragma unroll
     for (int cs = 0; cs < NCS; ++cs) load8<float>(S0 + (size_t)(16 * rt + l16) * DK + 32 * cs + 8 * q4, sop[w][cs]);
   }
-  float vv[RTW][kChunkMaxTT][4];
+  // v of node 16*ti + l16, columns 16*rt + 4*q4 .. +3 (the layout of S0 [K|Q]'s result)
+  uint2 vv[RTW][kChunkMaxTT];
 #pragma unroll
   for (int w = 0; w < RTW; ++w) {
     const int rt = min(wave + 4 * w, NRT - 1);
 #pragma unroll
-    for (int ti = 0; ti < kChunkMaxTT; ++ti)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = min(16 * ti + 4 * q4 + e, Tn - 1);
-        vv[w][ti][e] = Elem<A>::load(v, (((size_t)s * Tn + t) * H + h) * DV + 16 * rt + l16);
-      }
-  }
-  // this thread's conv channels: 8 of the head's q (half 0) or k (half 1) channels
-  const int cg = tid % NG, half = (tid / NG) & 1, tsub = tid / (2 * NG);
-  const int c0 = half * H * DK + h * DK + 8 * cg;  // channel in x
-  const int s0 = half * DK + 8 * cg;               // channel in the stage
-  float cw[8][kChunkMaxW];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int c = 0; c < kChunkMaxW; ++c) cw[e][c] = conv_w[(size_t)(c0 + e) * W + min(c, W - 1)];
-  // the stage: rows 0..T-1 are x, rows T..T+W-2 the committed conv rows; chunk k of a row
-  // is 8 activations of the q part (k < ROW8/2) or the k part
-  constexpr int kStageIt = ((kChunkMaxT + kChunkMaxW - 1) * ROW8 + 255) / 256;
-  const int nst = (Tn + W - 1) * ROW8;
-  uint4 sv[kStageIt * (int)sizeof(A) / 2];  // 16 bytes per chunk for bf16, 32 for fp32
-#pragma unroll
-  for (int k = 0; k < kStageIt; ++k) {
-    const int idx = min(tid + 256 * k, nst - 1);
-    const int row = idx / ROW8, ch = idx % ROW8;
-    const int chan = ch < ROW8 / 2 ? h * DK + 8 * ch : H * DK + h * DK + 8 * (ch - ROW8 / 2);
-    const A* src = row < Tn ? x + ((size_t)s * Tn + row) * C + chan
-                            : conv_state + ((size_t)s * (W - 1) + (row - Tn)) * C + chan;
-    if constexpr (sizeof(A) == 2) {
-      sv[k] = *reinterpret_cast<const uint4*>(src);
-    } else {
-      sv[2 * k] = *reinterpret_cast<const uint4*>(src);
-      sv[2 * k + 1] = *reinterpret_cast<const uint4*>(src + 4);
+    for (int ti = 0; ti < kChunkMaxTT; ++ti) {
+      const int t = min(16 * ti + l16, Tn - 1);
+      vv[w][ti] = *reinterpret_cast<const uint2*>(v + (((size_t)s * Tn + t) * H + h) * DV + 16 * rt + 4 * q4);
     }
   }
-  int pr = 0;
-  float gr = 0.f, br = 0.f;
+  // per node, one walk up the parent chain: conv window (the node, its ancestors, then
+  // the committed conv rows, newest first), depth, G_t and the records (row, r_tj)
   if (tid < Tn) {
-    const size_t ti = ((size_t)s * Tn + tid) * H + h;
-    pr = parent[(size_t)s * Tn + tid];
-    gr = g[ti];
-    br = beta[ti];
-  }
-#pragma unroll
-  for (int k = 0; k < kStageIt; ++k) {
-    const int idx = tid + 256 * k;
-    if (idx < nst) {
-      if constexpr (sizeof(A) == 2) {
-        reinterpret_cast<uint4*>(stage)[idx] = sv[k];
-      } else {
-        reinterpret_cast<uint4*>(stage)[2 * idx] = sv[2 * k];
-        reinterpret_cast<uint4*>(stage)[2 * idx + 1] = sv[2 * k + 1];
-      }
-    }
-  }
-  if (tid < Tn) {
-    par[tid] = pr;
-    gg[tid] = gr;
-    be[tid] = br;
-    cnt[tid] = 0;
-  }
-  for (int i = tid; i < 4 * RSB / 16; i += 256)  // row T of K hi, K lo, Q hi, Q lo: zero
-    *reinterpret_cast<uint4*>(lds + (i / (RSB / 16)) * RW * RSB + Tn * RSB + (i % (RSB / 16)) * 16) =
-        make_uint4(0, 0, 0, 0);
-  __syncthreads();
-  // per node: conv window (back b: stage row; the committed conv rows come after the
-  // node rows, newest last), depth, G_t; the depth histogram
-  if (tid < Tn) {
-    const int t = tid;
-    int cur = t, in_tree = 1, beyond = 0;
-    for (int b = 0; b < W; ++b) {
-      int r = t;
-      if (b > 0) {
-        if (in_tree) {
-          const int p = par[cur];
-          if (p >= 0 && p < cur) cur = p;
-          else in_tree = 0;
-        }
-        r = in_tree ? cur : Tn + (W - 1 - (++beyond));
-      }
-      win[t * kChunkMaxW + b] = r;
-    }
+    const int t = tid, rb = rec_base(t);
+    int a = t, k = 0;
     float prod = 1.f;
-    int a = t, d = 0;
+    win[t * kChunkMaxW] = t;
     while (true) {
       const int p = par[a];
-      if (!(p >= 0 && p < a)) break;
-      prod *= gg[a];
+      const float ga = gg[a];
+      if (!(p >= 0 && p < a)) {
+        Gam[t] = prod * ga;
+        break;
+      }
+      prod *= ga;
       a = p;
-      ++d;
+      rec[rb + k] = make_float4(__int_as_float(a), prod, 0.f, 0.f);
+      ++k;
+      if (k < W) win[t * kChunkMaxW + k] = a;
     }
-    Gam[t] = prod * gg[a];
-    dep[t] = d;
-    atomicAdd(&cnt[d], 1);
+    for (int b = k + 1; b < W; ++b) win[t * kChunkMaxW + b] = Tn + W - 1 - (b - k);
+    dep[t] = k;
+    atomicAdd(&cnt[k], 1);
   }
   __syncthreads();
-  // depth starts (one thread: at most T depths) while the others run the conv
-  if (tid == 0) {
-    int acc = 0, d = 0;
-    for (; d < Tn && cnt[d] > 0; ++d) {
-      lstart[d] = acc;
-      acc += cnt[d];
-      cnt[d] = 0;  // reused as the fill counter of depth d
+  if (wave == 0) {  // depth starts: an exclusive scan of the histogram over 64 lanes (+ depth 64)
+    int c = lane < Tn ? cnt[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(c, off, 64);
+      if (lane >= off) c += u;
     }
-    lstart[d] = Tn;
+    // c = nodes of depth <= lane
+    if (lane < Tn) lstart[lane + 1] = c;
+    // the largest depth: the last nonempty one (depth 64 only in a chain of 65)
+    const uint64_t nz = __ballot(lane < Tn && cnt[lane] > 0);
+    if (lane == 0) {
+      lstart[0] = 0;
+      lstart[Tn] = Tn;  // depth Tn - 1 (a chain of 65) lies past the 64 lanes
+      *maxdep = (Tn > 64 && cnt[64] > 0) ? 64 : 63 - __builtin_clzll(nz);
+    }
   }
-  // the short conv of the head's q and k channels from the stage (NPR nodes per round)
-  for (int t0 = 0; t0 < Tn; t0 += NPR) {
-    const int t = min(t0 + tsub, Tn - 1);
-    float y[8];
+  // the short conv of the head's q and k channels from the stage, two nodes per thread
+  // and pass; SiLU; k L2-normalised, q scaled; stored as bf16 high and low parts
+  for (int t0 = 0; t0 < Tn; t0 += 2 * NPR) {
+    float y[2][8];
+    int tt[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      tt[u] = min(t0 + tsub + u * NPR, Tn - 1);
 #pragma unroll
-    for (int c = 0; c < kChunkMaxW; ++c) {  // tap c multiplies the row W-1-c back
-      if (c >= W) break;
-      const int r = win[t * kChunkMaxW + (W - 1 - c)];
-      float xv[8];
-      load8<A>(stage + (size_t)r * (2 * DK) + s0, xv);
+      for (int e = 0; e < 8; ++e) y[u][e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] += cw[e][c] * xv[e];
+      for (int c = 0; c < WT; ++c) {  // tap c multiplies the row W-1-c back
+        const int b = WT == 4 ? 3 - c : max(W - 1 - c, 0);
+        const int r = win[tt[u] * kChunkMaxW + b];
+        float xv[8];
+        load8<uint16_t>(stage + (size_t)r * (2 * DK) + s0, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[u][e] += cw[e][c] * xv[e];
+      }
     }
-    float ss = 0.f;
+    float ss[2] = {0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = y[e] / (1.f + __expf(-y[e]));
-      ss += y[e] * y[e];
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[u][e] = y[u][e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[u][e]));
+        ss[u] += y[u][e] * y[u][e];
+      }
     // k: L2 norm over the head's dk channels (the NG lanes of this node and half)
 #pragma unroll
-    for (int off = NG / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    const float sc = half ? 1.f / sqrtf(ss + 1e-6f) : rsqrtf((float)DK);
+    for (int off = NG / 2; off > 0; off >>= 1) {
+      ss[0] += __shfl_xor(ss[0], off, 64);
+      ss[1] += __shfl_xor(ss[1], off, 64);
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] *= sc;
-    if (t0 + tsub < Tn) {
+    for (int u = 0; u < 2; ++u) {
+      const float sc = half ? 1.f / sqrtf(ss[u] + 1e-6f) : rsqrtf((float)DK);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[u][e] *= sc;
       cbf16x8 hi, lo;
-      split8(y, hi, lo);
-      const int base = (half ? 0 : 2) * RW * RSB + t * RSB + cg * 16;  // K hi/lo first, then Q hi/lo
+      split8(y[u], hi, lo);
+      const int base = (half ? 0 : 2) * RW * RSB + tt[u] * RSB + cg * 16;  // K hi/lo first, then Q hi/lo
       *reinterpret_cast<cbf16x8*>(lds + base) = hi;
       *reinterpret_cast<cbf16x8*>(lds + base + RW * RSB) = lo;
     }
   }
-  __syncthreads();  // the stage is dead: R and the records take its area
-  for (int i = tid; i < Tn * TS; i += 256) Rm[i] = 0.f;
-  if (tid < Tn) ord[lstart[dep[tid]] + atomicAdd(&cnt[dep[tid]], 1)] = tid;
   __syncthreads();
-  // r_tj along each node's parent chain; rec[t][depth of j] starts with the row j
-  if (tid < Tn) {
-    const int t = tid;
-    float prod = 1.f;
-    int a = t, d = dep[t];
-    Rm[t * TS + t] = 1.f;
-    while (true) {
-      const int p = par[a];
-      if (!(p >= 0 && p < a)) break;
-      prod *= gg[a];
-      a = p;
-      --d;
-      Rm[t * TS + a] = prod;
-      rec[t * Tn + d] = make_float4(__int_as_float(a), 0.f, 0.f, 0.f);
-    }
-  }
+  if (tid < Tn) cnt[tid] = 0;  // the fill counters (every read of the histogram is done)
+  __syncthreads();
+  if (tid < Tn) ord[lstart[dep[tid]] + atomicAdd(&cnt[dep[tid]], 1)] = tid;
 
-  // ---- P1: S0 [K|Q] and the Gram products (results stay in registers).  A tile's rows
-  // past the last node read row T, which is zero.
+  // ---- P1: S0 [K|Q] as D[r][t] (lane: node column 16*ti + l16, rows 16*rt + 4*q4 + e)
+  // and the Gram products (results stay in registers).  A tile's rows past the last
+  // node read row T, which is zero.
+  cbf16x8 sh[RTW][NCS], sl[RTW][NCS];
+#pragma unroll
+  for (int w = 0; w < RTW; ++w)
+#pragma unroll
+    for (int cs = 0; cs < NCS; ++cs) split8(sop[w][cs], sh[w][cs], sl[w][cs]);
   cf32x4 acc[RTW][kChunkMaxTT][2];
 #pragma unroll
   for (int w = 0; w < RTW; ++w)
@@ -336,27 +340,25 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const A* __restrict__ x,
   const uint8_t* Qhi = lds + 2 * RW * RSB;
   const uint8_t* Qlo = lds + 3 * RW * RSB;
 #pragma unroll
-  for (int w = 0; w < RTW; ++w) {
-    if (wave + 4 * w >= NRT) continue;
+  for (int cs = 0; cs < NCS; ++cs) {
 #pragma unroll
-    for (int cs = 0; cs < NCS; ++cs) {
-      // B = S0^T: column r = 16*rt + l16, k-range c = 32*cs + 8*q4 .. +7
-      cbf16x8 bh, bl;
-      split8(sop[w][cs], bh, bl);
+    for (int ti = 0; ti < kChunkMaxTT; ++ti) {
+      if (ti >= NTT) break;
+      const int ro = min(16 * ti + l16, Tn) * RSB + 64 * cs + 16 * q4;
+      const cbf16x8 kh = *reinterpret_cast<const cbf16x8*>(Khi + ro);
+      const cbf16x8 kl = *reinterpret_cast<const cbf16x8*>(Klo + ro);
+      const cbf16x8 qh = *reinterpret_cast<const cbf16x8*>(Qhi + ro);
+      const cbf16x8 ql = *reinterpret_cast<const cbf16x8*>(Qlo + ro);
 #pragma unroll
-      for (int ti = 0; ti < kChunkMaxTT; ++ti) {
-        if (ti >= NTT) break;
-        const int ro = min(16 * ti + l16, Tn) * RSB + 64 * cs + 16 * q4;
-        const cbf16x8 kh = *reinterpret_cast<const cbf16x8*>(Khi + ro);
-        const cbf16x8 kl = *reinterpret_cast<const cbf16x8*>(Klo + ro);
-        const cbf16x8 qh = *reinterpret_cast<const cbf16x8*>(Qhi + ro);
-        const cbf16x8 ql = *reinterpret_cast<const cbf16x8*>(Qlo + ro);
-        acc[w][ti][0] = mfma3(kh, kl, bh, bl, acc[w][ti][0]);
-        acc[w][ti][1] = mfma3(qh, ql, bh, bl, acc[w][ti][1]);
+      for (int w = 0; w < RTW; ++w) {
+        if (wave + 4 * w >= NRT) continue;
+        acc[w][ti][0] = mfma3(sh[w][cs], sl[w][cs], kh, kl, acc[w][ti][0]);
+        acc[w][ti][1] = mfma3(sh[w][cs], sl[w][cs], qh, ql, acc[w][ti][1]);
       }
     }
   }
-  // Gram blocks (ti, tj), tj <= ti, dealt to the waves: K_t . K_j and Q_t . K_j
+  // Gram blocks (ti, tj), tj <= ti, dealt to the waves: K_t . K_j and Q_t . K_j as
+  // D[t][j] (lane: j = 16*tj + l16, t = 16*ti + 4*q4 + e)
   constexpr int kMaxPairs = (kChunkMaxTT * (kChunkMaxTT + 1) / 2 + 3) / 4;  // per wave
   const int NP = NTT * (NTT + 1) / 2;
   cf32x4 gk[kMaxPairs][2];
@@ -386,34 +388,64 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const A* __restrict__ x,
   }
   __syncthreads();  // every wave is done with q/k: their area now takes w and the o base
 
-  // ---- P2: right-hand sides, o base (D layout: column l16, rows 4*q4 + e) and the
-  // records (ancestor row, beta_t r_tj (k_j . k_t), r_tj (k_j . q_t)) by ancestor depth
-  float* Wm = reinterpret_cast<float*>(lds);  // [T][DV]: right-hand sides, then w
-  float* Ob = Wm + Tn * DV;                   // [T][DV]: G_t S0 q_t
-  float bt[kChunkMaxTT][4], Gt[kChunkMaxTT][4];
+  // ---- P2: right-hand sides beta_t (v_t - G_t S0 k_t), the o base G_t S0 q_t, M_tt, and
+  // the records' coefficients
+  float* Wm = reinterpret_cast<float*>(lds);  // [T][WS]: right-hand sides, then w
+  float* Ob = Wm + Tn * WS;                   // [T][WS]: G_t S0 q_t
+  float bt[kChunkMaxTT], Gt[kChunkMaxTT];
 #pragma unroll
-  for (int ti = 0; ti < kChunkMaxTT; ++ti)
+  for (int ti = 0; ti < kChunkMaxTT; ++ti) {
+    const int tc = min(16 * ti + l16, Tn - 1);
+    bt[ti] = be[tc];
+    Gt[ti] = Gam[tc];
+  }
+  // the records: every read first (clamped), then the predicated writes.  The four rows
+  // t = 16*ti + 4*q4 .. +3 of a pair are one 16-byte read of each scalar array.
+  int rix[kMaxPairs][4];
+  float bet[kMaxPairs][4];
+#pragma unroll
+  for (int k = 0; k < kMaxPairs; ++k) {
+    const int t0 = 16 * pti[k] + 4 * q4;
+    const int4 d4 = *reinterpret_cast<const int4*>(&dep[t0]);
+    const float4 b4 = *reinterpret_cast<const float4*>(&be[t0]);
+    const int dj = dep[min(16 * ptj[k] + l16, Tn - 1)];
+    const int dt[4] = {d4.x, d4.y, d4.z, d4.w};
+    bet[k][0] = b4.x; bet[k][1] = b4.y; bet[k][2] = b4.z; bet[k][3] = b4.w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = min(16 * ti + 4 * q4 + e, Tn - 1);
-      bt[ti][e] = be[t];
-      Gt[ti][e] = Gam[t];
+      // t's record at distance dep[t] - dep[j] holds t's ancestor at j's depth: j's
+      // own when j is an ancestor of t (rows past the last node are never written)
+      const int kk = dt[e] - 1 - dj;
+      rix[k][e] = (t0 + e < Tn && kk >= 0 && kk < t0 + e) ? rec_base(t0 + e) + kk : -1;
     }
+  }
+  float4 rr[kMaxPairs][4];
 #pragma unroll
-  for (int w = 0; w < RTW; ++w) {
-    const int rt = wave + 4 * w;
-    if (rt >= NRT) continue;
-    const int r = 16 * rt + l16;
+  for (int k = 0; k < kMaxPairs; ++k)
 #pragma unroll
-    for (int ti = 0; ti < kChunkMaxTT; ++ti) {
-      if (ti >= NTT) break;
+    for (int e = 0; e < 4; ++e) rr[k][e] = rec[max(rix[k][e], 0)];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * ti + 4 * q4 + e;
-        if (t < Tn) {
-          Wm[t * DV + r] = bt[ti][e] * (vv[w][ti][e] - Gt[ti][e] * acc[w][ti][0][e]);
-          Ob[t * DV + r] = Gt[ti][e] * acc[w][ti][1][e];
-        }
+  for (int ti = 0; ti < kChunkMaxTT; ++ti) {
+    const int t = 16 * ti + l16;
+#pragma unroll
+    for (int w = 0; w < RTW; ++w) {
+      const int rt = wave + 4 * w;
+      if (rt >= NRT) continue;
+      const uint2 q = vv[w][ti];
+      const float v4[4] = {__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+                           __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u)};
+      float4 wv, ov;
+      wv.x = bt[ti] * (v4[0] - Gt[ti] * acc[w][ti][0][0]);
+      wv.y = bt[ti] * (v4[1] - Gt[ti] * acc[w][ti][0][1]);
+      wv.z = bt[ti] * (v4[2] - Gt[ti] * acc[w][ti][0][2]);
+      wv.w = bt[ti] * (v4[3] - Gt[ti] * acc[w][ti][0][3]);
+      ov.x = Gt[ti] * acc[w][ti][1][0];
+      ov.y = Gt[ti] * acc[w][ti][1][1];
+      ov.z = Gt[ti] * acc[w][ti][1][2];
+      ov.w = Gt[ti] * acc[w][ti][1][3];
+      if (t < Tn) {
+        *reinterpret_cast<float4*>(&Wm[t * WS + 16 * rt + 4 * q4]) = wv;
+        *reinterpret_cast<float4*>(&Ob[t * WS + 16 * rt + 4 * q4]) = ov;
       }
     }
   }
@@ -421,107 +453,128 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const A* __restrict__ x,
   for (int k = 0; k < kMaxPairs; ++k) {
     if (wave + 4 * k >= NP) continue;
     const int j = 16 * ptj[k] + l16;
-    const int jc = min(j, Tn - 1);
-    const int dj = dep[jc];
-    float rr[4], bb[4];
-    int dt[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = min(16 * pti[k] + 4 * q4 + e, Tn - 1);
-      rr[e] = Rm[t * TS + jc];
-      bb[e] = be[t];
-      dt[e] = dep[t];
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * pti[k] + 4 * q4 + e;
       if (t < Tn && j == t) Md[t] = gk[k][1][e];  // r_tt = 1
-      // the slot of depth dep[j] < dep[t] holds t's ancestor there: j owns it if it is
-      // that row (r_tj may be 0 when a g on the way is 0: then so are both coefficients)
-      if (t < Tn && j < t && dj < dt[e]) {
-        float4* rp = &rec[t * Tn + dj];
-        if (__float_as_int(rp->x) == j) {
-          rp->y = bb[e] * rr[e] * gk[k][0][e];
-          rp->z = rr[e] * gk[k][1][e];
-        }
+      if (rix[k][e] >= 0 && __float_as_int(rr[k][e].x) == j) {
+        const float r = rr[k][e].y;
+        rec[rix[k][e]].y = bet[k][e] * r * gk[k][0][e];
+        rec[rix[k][e]].z = r * gk[k][1][e];
       }
     }
   }
   __syncthreads();
 
-  // ---- P3: the solve, depth by depth, barrier-free: wave `wave` owns columns
-  // [CPW*wave, CPW*(wave+1)), a lane 2 of them, NPW nodes of one depth at once
+  // ---- P3: the solve, depth by depth, without barriers: wave `wave` owns columns
+  // [CPW*wave, CPW*(wave+1)), a lane 4 of them for NS nodes (slots), NGP nodes side by
+  // side, slot i holding positions NGP*i .. NGP*i + NGP-1 of the depth order.  At depth e
+  // the nodes there are final (w written, o stored); then every deeper node takes its
+  // depth-e ancestor's term, whose record was fetched one depth ahead.  The depth order
+  // makes the slots of one depth a contiguous range and those of deeper nodes a suffix,
+  // so whole slots (groups of GS) are skipped where no lane has work.
   {
-    const int nsub = lane / LPN;
-    const int rc = CPW * wave + 2 * (lane % LPN);
-    for (int d = 0;; ++d) {
-      const int beg = __builtin_amdgcn_readfirstlane(lstart[d]);
-      if (beg >= Tn) break;
-      const int end = __builtin_amdgcn_readfirstlane(lstart[d + 1]);
-      for (int i0 = beg; i0 < end; i0 += NPW) {
-        const int k = i0 + nsub;
-        const int t = ord[min(k, end - 1)];
-        float aw0 = 0.f, aw1 = 0.f, ao0 = 0.f, ao1 = 0.f;
-        // d ancestors, one per shallower depth, four at a time (records first, then rows)
-        for (int e0 = 0; e0 < d; e0 += 4) {
-          float4 rv[4];
+    constexpr int GS = 3;
+    const int ng = lane / LPN, c = CPW * wave + 4 * (lane % LPN);
+    const int nd = __builtin_amdgcn_readfirstlane(*maxdep);
+    float4 aw[NS], ao[NS], rv[NS];
+    float md[NS];
+    int dp[NS], tt[NS];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) rv[u] = rec[t * Tn + min(e0 + u, d - 1)];
-          float2 wv[4];
+    for (int i = 0; i < NS; ++i) {
+      const int pos = NGP * i + ng;
+      tt[i] = ord[min(pos, Tn - 1)];
+    }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) wv[u] = *reinterpret_cast<const float2*>(&Wm[__float_as_int(rv[u].x) * DV + rc]);
+    for (int i = 0; i < NS; ++i) dp[i] = NGP * i + ng < Tn ? dep[tt[i]] : -1;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float sa = e0 + u < d ? rv[u].y : 0.f, sm = e0 + u < d ? rv[u].z : 0.f;
-            aw0 += sa * wv[u].x;
-            aw1 += sa * wv[u].y;
-            ao0 += sm * wv[u].x;
-            ao1 += sm * wv[u].y;
-          }
+    for (int i = 0; i < NS; ++i) {
+      aw[i] = *reinterpret_cast<const float4*>(&Wm[tt[i] * WS + c]);
+      ao[i] = *reinterpret_cast<const float4*>(&Ob[tt[i] * WS + c]);
+      md[i] = Md[tt[i]];
+      rv[i] = rec[rec_base(tt[i]) + max(dp[i] - 1, 0)];
+    }
+    int lo = 0;  // lstart[e]
+    for (int e = 0;; ++e) {
+      const int hi = __builtin_amdgcn_readfirstlane(lstart[e + 1]);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (NGP * (i + 1) <= lo || NGP * i >= hi) continue;  // no node of depth e in slot i
+        if (dp[i] != e) continue;
+        const int t = tt[i];
+        *reinterpret_cast<float4*>(&Wm[t * WS + c]) = aw[i];
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16(ao[i].x + md[i] * aw[i].x) | ((uint32_t)f32_to_bf16(ao[i].y + md[i] * aw[i].y) << 16);
+        u.y = (uint32_t)f32_to_bf16(ao[i].z + md[i] * aw[i].z) | ((uint32_t)f32_to_bf16(ao[i].w + md[i] * aw[i].w) << 16);
+        *reinterpret_cast<uint2*>(o + (((size_t)s * Tn + t) * H + h) * DV + c) = u;
+      }
+      if (e >= nd) break;
+      // slots from i0 on hold nodes deeper than e
+      const int i0 = hi / NGP;
+#pragma unroll
+      for (int g0 = 0; g0 < NS; g0 += GS) {
+        if (g0 + GS <= i0) continue;
+        float4 wv[GS];
+        float ca[GS], cm[GS];
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+          const int i = g0 + u;
+          if (i >= NS) break;
+          const bool act = dp[i] > e;
+          const int row = act ? __float_as_int(rv[i].x) : tt[i];
+          ca[u] = act ? rv[i].y : 0.f;
+          cm[u] = act ? rv[i].z : 0.f;
+          wv[u] = *reinterpret_cast<const float4*>(&Wm[row * WS + c]);
+          rv[i] = rec[rec_base(tt[i]) + max(dp[i] - 2 - e, 0)];  // the record of depth e + 1
         }
-        if (k < end) {
-          const float2 rh = *reinterpret_cast<const float2*>(&Wm[t * DV + rc]);
-          const float2 ob = *reinterpret_cast<const float2*>(&Ob[t * DV + rc]);
-          const float md = Md[t];
-          const float w0 = rh.x - aw0, w1 = rh.y - aw1;
-          *reinterpret_cast<float2*>(&Wm[t * DV + rc]) = make_float2(w0, w1);
-          const size_t oi = (((size_t)s * Tn + t) * H + h) * DV + rc;
-          Elem<A>::store(o, oi, ob.x + ao0 + md * w0);
-          Elem<A>::store(o, oi + 1, ob.y + ao1 + md * w1);
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+          const int i = g0 + u;
+          if (i >= NS) break;
+          aw[i].x -= ca[u] * wv[u].x;
+          aw[i].y -= ca[u] * wv[u].y;
+          aw[i].z -= ca[u] * wv[u].z;
+          aw[i].w -= ca[u] * wv[u].w;
+          ao[i].x += cm[u] * wv[u].x;
+          ao[i].y += cm[u] * wv[u].y;
+          ao[i].z += cm[u] * wv[u].z;
+          ao[i].w += cm[u] * wv[u].w;
         }
       }
+      lo = hi;
     }
   }
 }
 
-size_t gdn_chunk_lds_bytes(int T, int dk, int W, int esize) { return (size_t)chunk_layout(T, dk, W, esize).total; }
+size_t gdn_chunk_lds_bytes(int T, int dk, int W) { return (size_t)chunk_layout(T, dk, W).total; }
 
-template <typename A, int DK>
+template <int DK, int WT>
 static void launch_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
                          const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
                          int T, int H, int W, hipStream_t st) {
-  auto kern = gdn_chunk_kernel<A, DK>;
+  auto kern = gdn_chunk_kernel<DK, WT>;
   // the dynamic LDS limit is raised once per kernel, to the largest size any call uses
   // (a host-side attribute, not a stream operation: calls stay capturable in a graph)
   static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)gdn_chunk_lds_bytes(kChunkMaxT, DK, kChunkMaxW,
-                                                                        (int)sizeof(A))) == hipSuccess;
+                                               (int)gdn_chunk_lds_bytes(kChunkMaxT, DK, kChunkMaxW)) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL(kern, dim3(n * H), dim3(256), gdn_chunk_lds_bytes(T, DK, W, (int)sizeof(A)), st, static_cast<const A*>(x), conv_w,
-                     static_cast<const A*>(conv_state), static_cast<const A*>(v), beta, g, S, static_cast<A*>(o),
-                     parent, T, H, W);
+  hipLaunchKernelGGL(kern, dim3(n * H), dim3(256), gdn_chunk_lds_bytes(T, DK, W), st,
+                     static_cast<const uint16_t*>(x), conv_w, static_cast<const uint16_t*>(conv_state),
+                     static_cast<const uint16_t*>(v), beta, g, S, static_cast<uint16_t*>(o), parent, T, H, W);
 }
 
 hipError_t launch_gdn_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
                             const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
                             int T, int H, int dk, int W, int act_dt, hipStream_t st) {
-#define DDT_CHUNK(TY, DKV) launch_chunk<TY, DKV>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, st)
   // bf16 activations only (fp32 ones keep the node-by-node walk); T <= 65, W <= 8
   if (act_dt != DDT_BF16 || T < 1 || T > kChunkMaxT || W < 1 || W > kChunkMaxW) return hipErrorInvalidValue;
-  if (dk == 32) DDT_CHUNK(uint16_t, 32);
-  else if (dk == 64) DDT_CHUNK(uint16_t, 64);
-  else if (dk == 128) DDT_CHUNK(uint16_t, 128);
+#define DDT_CHUNK(DKV)                                                                                       \
+  (W == 4 ? launch_chunk<DKV, 4>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, st)            \
+          : launch_chunk<DKV, 8>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, st))
+  if (dk == 32) DDT_CHUNK(32);
+  else if (dk == 64) DDT_CHUNK(64);
+  else if (dk == 128) DDT_CHUNK(128);
   else return hipErrorInvalidValue;
 #undef DDT_CHUNK
   return hipGetLastError();
