@@ -9,16 +9,18 @@
 //
 // Kernels
 //  1. topk_partial  grid (n*L rows, S chunks).  One HBM pass (16-byte loads): each block
-//     holds its chunk (<= 16384 logits) in registers as order-preserving integer keys,
-//     computes the chunk's (max, sum exp) and selects its exact top-K by (value desc, id asc):
-//     a lower bound from the per-thread maxima (per wave, by ballots) filters the chunk;
-//     the keys that pass (typically about a hundred) are compacted into LDS as unique
-//     64-bit (key, -offset) words and ranked by counting.  When more than 512 pass (many
-//     ties near the top), an LDS radix select over the filtered keys finds the K-th value
-//     and a second radix select over chunk offsets resolves ties at that value.
-//  2. topk_merge    grid (n*L), one thread per compare-exchange.  Bitonic-sorts the S*K
-//     chunk candidates as 64-bit (value, -id) keys, keeps the best K, combines the chunk
-//     (max, sum) pairs into the row's log-sum-exp and writes lp = z - lse in fp32.
+//     holds its chunk (<= 8192 logits) in registers as raw words, computes the chunk's
+//     (max, sum exp) and a lower bound for its top keff from the per-thread maximum keys
+//     (per wave, by ballots): at least keff keys reach it.  Every key at or above the
+//     bound (typically about a hundred) is written out unordered as a candidate word
+//     (order-preserving key, chunk offset).  When more than the chunk's capacity pass
+//     (many ties near the top), an LDS radix select over the keys finds the exact keff-th
+//     value and a second radix select over chunk offsets resolves ties at that value.
+//  2. topk_merge    grid (n*L).  The row's K-th largest key is at least every chunk's
+//     bound (of a chunk with K keys above it), so only candidates at or above the largest
+//     bound take part; they are ranked by counting as 64-bit (key, complement of the id)
+//     words, after a radix select of the K-th word when more than one per thread remain.
+//     The chunk (max, sum) pairs give the row's log-sum-exp; lp = z - lse in fp32.
 //  3. heap_expand   grid (n), one wavefront.  The frontier (<= B+1 entries) lives in
 //     registers, one slot per lane; each pop is a wave-wide max over 64-bit keys
 //     (score desc, token asc, parent row asc) -- exact integer comparisons, so the
@@ -31,10 +33,9 @@
 namespace ddt {
 
 constexpr int kTopkThreads = 256;
-constexpr int kEmax = 64;                              // keys per thread
-constexpr int kChunkMax = kTopkThreads * kEmax;        // 16384 logits per block
-constexpr int kSortMax = 2048;                         // merge capacity (S*K)
-constexpr int kCand = 2 * kTopkThreads;                // compacted keys of the usual case
+constexpr int kEmax = 32;                              // logits per thread
+constexpr int kChunkMax = kTopkThreads * kEmax;        // 8192 logits per block
+constexpr int kCand = 192;                             // candidate words a chunk may write
 
 // --- block-wide digit search over a 256-bin LDS histogram (wave 0 only).
 // Finds the bin where the running count (from the top bin down when `desc`, else from
@@ -73,17 +74,33 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
   }
 }
 
-template <typename T, int KBITS, bool VECLOAD>
-__global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(3))) topk_partial_kernel(const T* __restrict__ logits, int V, int chunk,
-                                                                    int K, float* __restrict__ cval,
-                                                                    int32_t* __restrict__ cid,
+// A chunk candidate: the key in the high bits, the chunk offset (< 2^13) in the low ones.
+template <int KBITS> struct CandWord { typedef uint64_t type; };
+template <> struct CandWord<16> { typedef uint32_t type; };
+
+// the value of a key: the dropped low bits of a 16-bit key are zeros for a positive
+// value and ones for a negative one (the key of a negative value is its complement)
+template <int KBITS> __device__ __forceinline__ float key_value(uint32_t k) {
+  uint32_t kf = k << (32 - KBITS);
+  if (KBITS < 32 && !(kf & 0x80000000u)) kf |= (1u << (32 - KBITS)) - 1u;
+  return key_float(kf);
+}
+
+template <typename T, int KBITS, bool VECLOAD, int EMAX>
+__global__ void __launch_bounds__(kTopkThreads) topk_partial_kernel(const T* __restrict__ logits, int V, int chunk,
+                                                                    int K, int cap,
+                                                                    typename CandWord<KBITS>::type* __restrict__ cand,
+                                                                    int32_t* __restrict__ ccount,
+                                                                    uint32_t* __restrict__ ctau,
                                                                     float2* __restrict__ stat) {
+  typedef typename CandWord<KBITS>::type CW;
   const int row = blockIdx.x, c = blockIdx.y, S = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int beg = c * chunk;
   const int cnt = min(chunk, V - beg);
   const int keff = min(K, cnt);
   const T* p = logits + (size_t)row * V + beg;
+  CW* out = cand + ((size_t)row * S + c) * cap;
 
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmaxs[kTopkThreads / 64];
@@ -91,7 +108,6 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
   __shared__ float2 red[kTopkThreads / 64];
   __shared__ int out_cnt;
   __shared__ uint32_t wpass[kTopkThreads / 64];
-  __shared__ uint64_t cand[kCand];
 
   // chunk offset of register j: element-wise, or VEC consecutive elements per 16-byte load
   constexpr int VEC = 16 / (int)sizeof(T);
@@ -100,53 +116,97 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
     else return tid + kTopkThreads * j;
   };
 
-  // 1. load the chunk as keys (exact: KBITS is the width of T), per-thread max key
-  uint32_t key[kEmax];
-  uint32_t tmax = 0;
+  // 1. load the chunk as raw words (two bf16 or one fp32 per dword) and keys on the fly
+  constexpr int NW = EMAX * (int)sizeof(T) / 4;
+  uint32_t raw[NW];
+  // every load is issued unconditionally at a clamped address (no load waits behind a
+  // branch); elements past the chunk's end are masked by elem(j) < cnt below
   if constexpr (VECLOAD) {
-    // the chunk start and the row are 16-byte aligned (V and the chunk length are multiples of VEC)
+    // the chunk start and the row are 16-byte aligned and cnt is a multiple of VEC (V and
+    // the chunk length are), so a vector starting inside the chunk ends inside it
 #pragma unroll
-    for (int jv = 0; jv < kEmax / VEC; ++jv) {
-      const int e0 = VEC * (tid + kTopkThreads * jv);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (e0 + VEC <= cnt) w = *reinterpret_cast<const uint4*>(p + e0);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const int e = e0 + i;
-        float v;
-        if constexpr (sizeof(T) == 2) v = bf16_to_f32(static_cast<uint16_t>(i & 1 ? u[i >> 1] >> 16 : u[i >> 1] & 0xffffu));
-        else v = __uint_as_float(u[i]);
-        if (e0 + VEC > cnt && e < cnt) v = Elem<T>::load(p, e);  // ragged end of the chunk
-        const uint32_t k = e < cnt ? float_key(v) >> (32 - KBITS) : 0u;
-        key[jv * VEC + i] = k;
-        tmax = k > tmax ? k : tmax;
-      }
+    for (int jv = 0; jv < EMAX / VEC; ++jv) {
+      const int e0 = min(VEC * (tid + kTopkThreads * jv), cnt - VEC);
+      const uint4 w = *reinterpret_cast<const uint4*>(p + e0);
+      raw[4 * jv] = w.x;
+      raw[4 * jv + 1] = w.y;
+      raw[4 * jv + 2] = w.z;
+      raw[4 * jv + 3] = w.w;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kEmax; ++j) {
-      const int e = elem(j);
-      const uint32_t k = e < cnt ? float_key(Elem<T>::load(p, e)) >> (32 - KBITS) : 0u;
-      key[j] = k;
-      tmax = k > tmax ? k : tmax;
+    for (int j = 0; j < EMAX; ++j) {
+      const int e = min(elem(j), cnt - 1);
+      uint32_t b;
+      if constexpr (sizeof(T) == 2) b = reinterpret_cast<const uint16_t*>(p)[e];
+      else b = reinterpret_cast<const uint32_t*>(p)[e];
+      if constexpr (sizeof(T) == 2) {
+        if (j & 1) raw[j >> 1] |= b << 16;
+        else raw[j >> 1] = b;
+      } else {
+        raw[j] = b;
+      }
     }
   }
-  // the value of a key: the dropped low bits of a 16-bit key are zeros for a positive
-  // value and ones for a negative one (the key of a negative value is its complement)
-  auto kval = [](uint32_t k) {
-    uint32_t kf = k << (32 - KBITS);
-    if (KBITS < 32 && !(kf & 0x80000000u)) kf |= (1u << (32 - KBITS)) - 1u;
-    return key_float(kf);
+  auto val = [&](int j) -> float {
+    if constexpr (sizeof(T) == 2) return __uint_as_float((j & 1) ? (raw[j >> 1] & 0xffff0000u) : (raw[j >> 1] << 16));
+    else return __uint_as_float(raw[j]);
   };
-  // this thread's (max, sum exp): the max from the largest key, then one exp per element
+  // bf16 in 16-byte vectors: the keys of a dword's two logits at once, packed as two
+  // 16-bit halves (b ^ 0xffff for a negative b, b | 0x8000 otherwise), the keys of a
+  // vector past the chunk's end (cnt is a multiple of VEC) masked to 0
+  constexpr bool PK = sizeof(T) == 2 && VECLOAD;
+  uint32_t kp[PK ? NW : 1];
+  auto vvalid = [&](int jv) { return VEC * (tid + kTopkThreads * jv) < cnt; };
+  if constexpr (PK) {
+#pragma unroll
+    for (int jv = 0; jv < EMAX / VEC; ++jv) {
+      const uint32_t vm = vvalid(jv) ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = raw[4 * jv + q];
+        kp[4 * jv + q] = (w ^ (((w >> 15) & 0x10001u) * 0x7fffu + 0x80008000u)) & vm;
+      }
+    }
+  }
+  auto key = [&](int j) -> uint32_t {
+    if constexpr (PK) return (j & 1) ? kp[j >> 1] >> 16 : kp[j >> 1] & 0xffffu;
+    else return elem(j) < cnt ? float_key(val(j)) >> (32 - KBITS) : 0u;
+  };
+
+  // this thread's largest key, then (max, sum exp) with one exp per element
+  uint32_t tmax = 0;
+  if constexpr (PK) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mx = {0, 0};
+#pragma unroll
+    for (int q = 0; q < NW; ++q) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, kp[q]));
+    tmax = max((uint32_t)mx.x, (uint32_t)mx.y);
+  } else {
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j) tmax = max(tmax, key(j));
+  }
   float m = -INFINITY, sum = 0.f;
   if (tmax != 0) {
-    m = kval(tmax);
+    m = key_value<KBITS>(tmax);
     if (m != -INFINITY) {
+      if constexpr (PK) {
 #pragma unroll
-      for (int j = 0; j < kEmax; ++j)
-        if (elem(j) < cnt) sum += __expf(kval(key[j]) - m);
+        for (int jv = 0; jv < EMAX / VEC; ++jv) {  // a vector's 8 terms, kept or dropped whole
+          // exp(v - m) as 2^(v log2 e - m log2 e)
+          const float ml = m * 1.4426950408889634f;
+          float s8 = 0.f;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) s8 += __builtin_amdgcn_exp2f(fmaf(val(VEC * jv + i), 1.4426950408889634f, -ml));
+          sum += vvalid(jv) ? s8 : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j) {  // branch-free: masked elements add 0
+          const float ex = __expf(val(j) - m);
+          sum += elem(j) < cnt ? ex : 0.f;
+        }
+      }
     }
   }
   // (max, sum) over the block
@@ -158,6 +218,21 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
     m = mm;
   }
   if (lane == 0) red[wave] = make_float2(m, sum);
+
+  // 2. lower bound: each wave finds the c-th largest of its 64 per-thread maxima
+  // (c = ceil(keff / waves)) bit by bit with ballots; the smallest of the waves' values
+  // is a bound that at least keff thread maxima, hence at least keff keys, reach
+  {
+    constexpr int NWV = kTopkThreads / 64;
+    const uint32_t cw = (uint32_t)((keff + NWV - 1) / NWV);
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = KBITS - 1; b >= 0; --b) {
+      const uint32_t cb = t | (1u << b);
+      if ((uint32_t)__popcll(__ballot(tmax >= cb)) >= cw) t = cb;
+    }
+    if (lane == 0) tmaxs[wave] = t;
+  }
   __syncthreads();
   if (tid == 0) {
     float mm = red[0].x, ss = red[0].y;
@@ -169,34 +244,22 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
     }
     stat[(size_t)row * S + c] = make_float2(mm, ss);
   }
-
-  // 2. lower bound: each wave finds the c-th largest of its 64 per-thread maxima
-  // (c = ceil(keff / waves)) bit by bit with ballots; the smallest of the waves' values
-  // is a bound that at least keff thread maxima, hence at least keff keys, reach
-  {
-    constexpr int NWV = kTopkThreads / 64;
-    const uint32_t c = (uint32_t)((keff + NWV - 1) / NWV);
-    uint32_t t = 0;
-#pragma unroll
-    for (int b = KBITS - 1; b >= 0; --b) {
-      const uint32_t cand = t | (1u << b);
-      if ((uint32_t)__popcll(__ballot(tmax >= cand)) >= c) t = cand;
-    }
-    if (lane == 0) tmaxs[wave] = t;
-  }
-  __syncthreads();
   uint32_t tau = tmaxs[0];
 #pragma unroll
   for (int w = 1; w < kTopkThreads / 64; ++w) tau = tmaxs[w] < tau ? tmaxs[w] : tau;
-  const size_t base = ((size_t)row * S + c) * K;
 
-  // 3a. usual case: the keys at or above tau (at least keff of them, typically about a
-  // hundred per chunk) fit in LDS.  They are compacted there as unique 64-bit words
-  // (key, complement of the chunk offset) and each is ranked by counting the words above
-  // it: rank < keff are the chunk's top keff by (value desc, id asc), emitted in order.
+  // 3a. usual case: every key at or above tau (at least keff of them, typically about a
+  // hundred per chunk) is a candidate, written unordered; the merge ranks them
+  // masked keys are 0: with tau > 0 the key test alone excludes them.  In range:
+  // element by element, or (packed keys) vector by vector
+  const bool tpos = tau > 0;
+  auto inrange = [&](int j) {
+    if constexpr (PK) return vvalid(j / VEC);
+    else return elem(j) < cnt;
+  };
   uint32_t npass = 0;
 #pragma unroll
-  for (int j = 0; j < kEmax; ++j) npass += (elem(j) < cnt && key[j] >= tau) ? 1u : 0u;
+  for (int j = 0; j < EMAX; ++j) npass += ((tpos || inrange(j)) && key(j) >= tau) ? 1u : 0u;
   uint32_t incl = npass;  // inclusive prefix over the wave's lanes
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -212,45 +275,32 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
     total += x;
     off += w < wave ? x : 0u;
   }
-  if (total <= (uint32_t)kCand) {  // block-uniform
+  // the bound holds for the row only when the chunk has K keys at or above it
+  const uint32_t bound = keff == K ? tau : 0u;
+  if (total <= (uint32_t)cap) {  // block-uniform
 #pragma unroll
-    for (int j = 0; j < kEmax; ++j) {
+    for (int j = 0; j < EMAX; ++j) {
       const int e = elem(j);
-      if (e < cnt && key[j] >= tau) cand[off++] = (static_cast<uint64_t>(key[j]) << 32) | (0xffffffffu - (uint32_t)e);
+      const uint32_t k = key(j);
+      if ((tpos || inrange(j)) && k >= tau) out[off++] = (static_cast<CW>(k) << (KBITS == 16 ? 16 : 32)) | (CW)e;
     }
-    __syncthreads();
-    const uint64_t w0 = tid < (int)total ? cand[tid] : 0ull;
-    const uint64_t w1 = tid + kTopkThreads < (int)total ? cand[tid + kTopkThreads] : 0ull;
-    uint32_t r0 = 0, r1 = 0;
-    for (uint32_t i = 0; i < total; ++i) {
-      const uint64_t x = cand[i];
-      r0 += x > w0 ? 1u : 0u;
-      r1 += x > w1 ? 1u : 0u;
+    if (tid == 0) {
+      ccount[(size_t)row * S + c] = (int)total;
+      ctau[(size_t)row * S + c] = bound;
     }
-    if (tid < (int)total && r0 < (uint32_t)keff) {
-      cval[base + r0] = kval(static_cast<uint32_t>(w0 >> 32));
-      cid[base + r0] = beg + (int)(0xffffffffu - (uint32_t)w0);
-    }
-    if (tid + kTopkThreads < (int)total && r1 < (uint32_t)keff) {
-      cval[base + r1] = kval(static_cast<uint32_t>(w1 >> 32));
-      cid[base + r1] = beg + (int)(0xffffffffu - (uint32_t)w1);
-    }
-    if (tid >= keff && tid < K) cid[base + tid] = -1;
     return;
   }
-  // 3b. otherwise (many keys tied near the top, e.g. a flat row): radix select below
-
-  // 3. radix select of the keff-th largest key among keys >= tau
+  // 3b. otherwise (many keys tied near the top, e.g. a flat row): the exact top keff by
+  // radix select, the keff-th largest key among keys >= tau
   uint32_t prefix = 0, pmask = 0, need = keff, count_eq = 0;
 #pragma unroll
   for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kEmax; ++j) {
-      const uint32_t k = key[j];
-      if (elem(j) < cnt && k >= tau && (k & pmask) == prefix)
-        atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    for (int j = 0; j < EMAX; ++j) {
+      const uint32_t k = key(j);
+      if (elem(j) < cnt && k >= tau && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) find_digit(hist, need, true, sel);
@@ -272,9 +322,9 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
       hist[tid] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kEmax; ++j) {
+      for (int j = 0; j < EMAX; ++j) {
         const uint32_t e = elem(j);
-        if ((int)e < cnt && key[j] == kth && (e & msk2) == pre2) atomicAdd(&hist[(e >> shift) & 255u], 1u);
+        if ((int)e < cnt && key(j) == kth && (e & msk2) == pre2) atomicAdd(&hist[(e >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (wave == 0) find_digit(hist, need2, false, sel);
@@ -286,104 +336,290 @@ __global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_
     off_th = pre2;
   }
 
-  // 5. emit exactly keff candidates (unordered); pad to K with id -1
+  // 5. emit exactly keff candidates (unordered)
   if (tid == 0) out_cnt = 0;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kEmax; ++j) {
+  for (int j = 0; j < EMAX; ++j) {
     const uint32_t e = elem(j);
-    const uint32_t k = key[j];
+    const uint32_t k = key(j);
     if ((int)e < cnt && (k > kth || (k == kth && e <= off_th))) {
       const int pos = atomicAdd(&out_cnt, 1);
-      if (pos < K) {
-        cval[base + pos] = Elem<T>::load(p, e);
-        cid[base + pos] = beg + (int)e;
-      }
+      if (pos < keff) out[pos] = (static_cast<CW>(k) << (KBITS == 16 ? 16 : 32)) | (CW)e;
     }
-  }
-  if (tid >= keff && tid < K) cid[base + tid] = -1;
-}
-
-__global__ void __launch_bounds__(1024) topk_merge_kernel(const float* __restrict__ cval,
-                                                         const int32_t* __restrict__ cid,
-                                                         const float2* __restrict__ stat, int S, int K,
-                                                         int sortN, int32_t* __restrict__ top_id,
-                                                         float* __restrict__ top_lp) {
-  const int row = blockIdx.x, tid = threadIdx.x;
-  __shared__ uint64_t sk[kSortMax];
-  __shared__ float lse_s;
-  const int N = S * K;
-  for (int i = tid; i < sortN; i += blockDim.x) {
-    uint64_t k = 0;
-    if (i < N) {
-      const int id = cid[(size_t)row * N + i];
-      if (id >= 0)
-        k = (static_cast<uint64_t>(float_key(cval[(size_t)row * N + i])) << 32) | (0xffffffffu - (uint32_t)id);
-    }
-    sk[i] = k;
   }
   if (tid == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, stat[(size_t)row * S + c].x);
-    float tot = 0.f;
-    for (int c = 0; c < S; ++c) {
-      const float2 st = stat[(size_t)row * S + c];
-      if (st.x != -INFINITY) tot += st.y * __expf(st.x - M);
-    }
-    lse_s = M + __logf(tot);
-  }
-  __syncthreads();
-  // bitonic sort, descending: in each stage, pair p compares i (bit j of i clear) with i + j
-  for (int k = 2; k <= sortN; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int pr = tid; pr < sortN / 2; pr += blockDim.x) {
-        const int i = (pr / j) * 2 * j + (pr % j);
-        const int ixj = i + j;
-        const uint64_t a = sk[i], b = sk[ixj];
-        const bool desc = (i & k) == 0;
-        if (desc ? (a < b) : (a > b)) {
-          sk[i] = b;
-          sk[ixj] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  const float lse = lse_s;
-  for (int i = tid; i < K; i += blockDim.x) {
-    const uint64_t k = sk[i];
-    if (k != 0) {
-      top_id[(size_t)row * K + i] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
-      top_lp[(size_t)row * K + i] = key_float((uint32_t)(k >> 32)) - lse;
-    } else {
-      top_id[(size_t)row * K + i] = -1;
-      top_lp[(size_t)row * K + i] = -INFINITY;
-    }
+    ccount[(size_t)row * S + c] = keff;
+    ctau[(size_t)row * S + c] = keff == K ? kth : 0u;
   }
 }
 
-// One frontier entry: a candidate node (score, token, parent row, depth, rank among the
-// depth's top-K) and its next-ranked sibling's (log-prob, token), fetched when the entry
-// is made so that a pop reads no LDS on its critical path.
-struct Slot {
-  float score, nlp;
-  int tok, par, dep, rank, ntok;
-  bool valid;
-};
+constexpr int kMergeThreads = 512;
+constexpr int kMergeMax = 8192;  // candidates of one row (S * cap)
+constexpr int kHistBins = 2048;  // key range [bound, largest key] counted bin by bin
 
-__device__ __forceinline__ uint64_t slot_key(const Slot& s) {
-  if (!s.valid) return 0;
-  const uint32_t lo = ((0xfffffu - (uint32_t)s.tok) << 7) | (127u - (uint32_t)s.par);
-  return (static_cast<uint64_t>(float_key(s.score)) << 32) | lo;
+// One block per (sequence, depth) row.  The row's K-th largest key is at least every
+// chunk's bound (of a chunk with K keys at or above it), so only candidates at or above
+// the largest bound take part, as 64-bit words (key, complement of the vocabulary id).
+// A radix select over their keys finds the K-th largest key; the words above it and
+// the ties at it are ranked by counting (a radix select over the id part first when the
+// ties do not fit one per thread).
+template <int KBITS>
+__global__ void __launch_bounds__(kMergeThreads) topk_merge_kernel(const typename CandWord<KBITS>::type* __restrict__ cand,
+                                                                  const int32_t* __restrict__ ccount,
+                                                                  const uint32_t* __restrict__ ctau,
+                                                                  const float2* __restrict__ stat, int S, int K,
+                                                                  int cap, int chunk, int V,
+                                                                  int32_t* __restrict__ top_id,
+                                                                  float* __restrict__ top_lp) {
+  typedef typename CandWord<KBITS>::type CW;
+  constexpr int SH = KBITS == 16 ? 16 : 32;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint64_t fk[kMergeMax];
+  __shared__ uint64_t top[kMergeThreads];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel[3];
+  __shared__ int nf, ntop;
+  __shared__ int cbeg[129];       // first candidate of each chunk in the row's list
+  __shared__ uint32_t ctau_s[2];  // largest bound, largest kept key
+  __shared__ uint32_t hist2[kHistBins];
+  __shared__ float2 st_s[128];
+  __shared__ float lse_s;
+  // the chunks' counts, bounds and (max, sum) pairs, one chunk per thread (S <= 128)
+  if (tid < 64) {
+    int nc0 = 0, nc1 = 0;
+    uint32_t b = 0;
+    if (tid < S) {
+      nc0 = ccount[(size_t)row * S + tid];
+      b = ctau[(size_t)row * S + tid];
+      st_s[tid] = stat[(size_t)row * S + tid];
+    }
+    if (tid + 64 < S) {
+      nc1 = ccount[(size_t)row * S + tid + 64];
+      b = max(b, ctau[(size_t)row * S + tid + 64]);
+      st_s[tid + 64] = stat[(size_t)row * S + tid + 64];
+    }
+    // exclusive prefix of the counts over chunk order (lanes hold chunks l and l + 64)
+    int inc = nc0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    const int tot0 = __shfl(inc, 63, 64);
+    int inc1 = nc1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc1, o, 64);
+      if (lane >= o) inc1 += t;
+    }
+    cbeg[tid] = inc - nc0;
+    cbeg[tid + 64] = tot0 + inc1 - nc1;
+    if (tid == 63) cbeg[128] = tot0 + inc1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, o, 64));
+    if (tid == 0) {
+      ctau_s[0] = b;
+      ctau_s[1] = 0;
+      nf = 0;
+      ntop = 0;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // the row's log-sum-exp from the chunks' (max, sum) pairs
+    const float2 a = lane < S ? st_s[lane] : make_float2(-INFINITY, 0.f);
+    const float2 b = lane + 64 < S ? st_s[lane + 64] : make_float2(-INFINITY, 0.f);
+    float M = fmaxf(a.x, b.x);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float tot = (a.x != -INFINITY ? a.y * __expf(a.x - M) : 0.f) + (b.x != -INFINITY ? b.y * __expf(b.x - M) : 0.f);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+    if (lane == 0) lse_s = M + __logf(tot);
+  }
+  const uint32_t tau = ctau_s[0];
+  // gather the candidates at or above tau as (key, complement of the id).  Slot
+  // u = c * cap + j holds word j of chunk c; the S * cap <= kMergeMax slots are dealt to
+  // the threads, and every load is issued before the first is used.
+  constexpr int U = kMergeMax / kMergeThreads;
+  CW xs[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int slot = tid + kMergeThreads * u;
+    const int c = min(slot / cap, S - 1), j = slot - c * cap;
+    xs[u] = cand[((size_t)row * S + c) * cap + min(j, cap - 1)];
+  }
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int slot = tid + kMergeThreads * u;
+    const int c = slot / cap, j = slot - c * cap;
+    const bool in = c < S && j < cbeg[c + 1] - cbeg[c];
+    const uint32_t k = (uint32_t)(xs[u] >> SH);
+    const bool keep = in && k >= tau;
+    const uint32_t id = (uint32_t)(c * chunk) + (uint32_t)(xs[u] & (((CW)1 << SH) - 1));
+    const uint64_t w = (static_cast<uint64_t>(k) << 32) | (0xffffffffu - id);
+    kmax = keep ? max(kmax, k) : kmax;
+    const uint64_t bal = __ballot(keep);
+    if (bal == 0) continue;  // wave-uniform
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&nf, (int)__popcll(bal));
+    base = __shfl(base, 0, 64);
+    if (keep) fk[base + __popcll(bal & ((1ull << lane) - 1))] = w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  if (lane == 0) atomicMax(&ctau_s[1], kmax);
+  __syncthreads();
+  const int M = nf;
+  const int keff = min(K, V);
+  const float lse = lse_s;
+  auto emit = [&](int r, uint64_t w) {
+    top_id[(size_t)row * K + r] = (int32_t)(0xffffffffu - (uint32_t)w);
+    top_lp[(size_t)row * K + r] = key_value<KBITS>((uint32_t)(w >> 32)) - lse;
+  };
+  // the keff-th largest key kth: by a histogram over [tau, kmax] when that range is
+  // short (the usual case: the top of a row spans few bf16 values), else by 8-bit digits
+  uint32_t kth = 0, above = 0;
+  const uint32_t krange = ctau_s[1] - tau + 1;
+  if (krange <= kHistBins) {
+    for (int b = tid; b < (int)krange; b += kMergeThreads) hist2[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < M; i += kMergeThreads) atomicAdd(&hist2[(uint32_t)(fk[i] >> 32) - tau], 1u);
+    __syncthreads();
+    if (wave == 0) {  // from the top bin down: the bin where the running count reaches keff
+      constexpr int PER = kHistBins / 64;
+      const int b0 = (int)krange - 1 - PER * lane;  // lane l scans bins b0, b0 - 1, ...
+      uint32_t h[PER], tot = 0;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        h[q] = b0 - q >= 0 ? hist2[b0 - q] : 0u;
+        tot += h[q];
+      }
+      uint32_t inc = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+      }
+      uint32_t acc = inc - tot;
+      if (acc < (uint32_t)keff && (uint32_t)keff <= inc) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          if (acc + h[q] >= (uint32_t)keff) {
+            sel[0] = tau + (uint32_t)(b0 - q);
+            sel[1] = acc;  // keys above kth
+            break;
+          }
+          acc += h[q];
+        }
+      }
+    }
+    __syncthreads();
+    kth = sel[0];
+    above = sel[1];
+  } else {
+    uint32_t kmask = 0, need = keff;
+    for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < M; i += kMergeThreads) {
+        const uint32_t k = (uint32_t)(fk[i] >> 32);
+        if ((k & kmask) == kth) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) find_digit(hist, need, true, sel);
+      __syncthreads();
+      need -= sel[1];
+      kth |= sel[0] << shift;
+      kmask |= 255u << shift;
+    }
+    above = (uint32_t)keff - need;
+  }
+  // every word with a key above kth, and the ties at kth, ranked by counting among
+  // themselves (all other words are smaller)
+  for (int i = tid; i < M; i += kMergeThreads) {
+    const uint64_t w = fk[i];
+    if ((uint32_t)(w >> 32) >= kth) {
+      const int at = atomicAdd(&ntop, 1);
+      if (at < kMergeThreads) top[at] = w;
+    }
+  }
+  __syncthreads();
+  const int C = ntop;
+  if (C <= kMergeThreads) {  // block-uniform
+    if (tid < C) {
+      const uint64_t w = top[tid];
+      int r = 0;
+      for (int i = 0; i < C; ++i) r += top[i] > w ? 1 : 0;
+      if (r < keff) emit(r, w);
+    }
+  } else {
+    // many ties at the keff-th key: the keff-th largest word by 8-bit digits of the
+    // id part (the key part is kth), then the words at or above it ranked by counting
+    uint32_t prefix = 0, pmask = 0, need2 = (uint32_t)keff - above;  // ties to take
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < M; i += kMergeThreads) {
+        const uint64_t w = fk[i];
+        const uint32_t lo = (uint32_t)w;
+        if ((uint32_t)(w >> 32) == kth && (lo & pmask) == prefix) atomicAdd(&hist[(lo >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) find_digit(hist, need2, true, sel);
+      __syncthreads();
+      need2 -= sel[1];
+      prefix |= sel[0] << shift;
+      pmask |= 255u << shift;
+    }
+    const uint64_t wth = (static_cast<uint64_t>(kth) << 32) | prefix;
+    if (tid == 0) ntop = 0;
+    __syncthreads();
+    for (int i = tid; i < M; i += kMergeThreads) {
+      const uint64_t w = fk[i];
+      if (w >= wth) top[atomicAdd(&ntop, 1)] = w;  // exactly keff words
+    }
+    __syncthreads();
+    if (tid < keff) {
+      const uint64_t w = top[tid];
+      int r = 0;
+      for (int i = 0; i < keff; ++i) r += top[i] > w ? 1 : 0;
+      emit(r, w);
+    }
+  }
+  for (int r = keff + tid; r < K; r += kMergeThreads) {
+    top_id[(size_t)row * K + r] = -1;
+    top_lp[(size_t)row * K + r] = -INFINITY;
+  }
+}
+
+// 64-bit key of a frontier entry: score desc, then token asc, then parent row asc.
+__device__ __forceinline__ uint64_t frontier_key(float score, int tok, int par) {
+  const uint32_t lo = ((0xfffffu - (uint32_t)tok) << 7) | (127u - (uint32_t)par);
+  return (static_cast<uint64_t>(float_key(score)) << 32) | lo;
+}
+
+// Largest 32-bit value over the wave, by DPP within rows of 16 and reads of 4 lanes.
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+  v = max(v, DDT_DPP_U32(v, 0x128));  // row_ror:8
+  v = max(v, DDT_DPP_U32(v, 0x124));  // row_ror:4
+  v = max(v, DDT_DPP_U32(v, 0x122));  // row_ror:2
+  v = max(v, DDT_DPP_U32(v, 0x121));  // row_ror:1
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // One wavefront per sequence, T = B+1 <= 65.  The frontier has one slot per lane: the
 // seed takes slot 0, pop i puts the popped node's sibling in the popped slot and its best
 // child in slot i at most (a fresh slot per pop), and the child of the last pop is never
-// popped, so 64 slots suffice.  Every step of a pop is lane-local, a DPP move or a scalar
-// read of one lane (readlane): the wave-wide max of the frontier keys, the winner's
-// fields, the parent's score and mask (node i's are kept by lane i), and the best child of
-// depth d (lane d).  The wave needs no barrier.
+// popped, so 64 slots suffice.  A slot also holds its next-ranked sibling's (token,
+// log-prob), read when the slot is filled, so that a pop reads no LDS on its critical
+// path.  A pop: the wave-wide max of the slots' 32-bit score keys (DPP), the 64-bit key
+// (token, parent) only among lanes tied on the score, the winner's fields by readlane,
+// and the two new entries written by lane selects (no divergent branch).  Node i's row,
+// score and ancestor mask are kept by lane i (node 64 in scalars) and stored at the end.
 __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restrict__ top_id,
                                                          const float* __restrict__ top_lp, int L, int K,
                                                          int T, const int32_t* __restrict__ root_token,
@@ -394,103 +630,159 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   extern __shared__ uint8_t smem[];
   float* lp = reinterpret_cast<float*>(smem);                  // [L][K]
   int32_t* ids = reinterpret_cast<int32_t*>(lp + L * K);       // [L][K]
-  for (int i = lane; i < L * K; i += 64) {
-    lp[i] = top_lp[(size_t)s * L * K + i];
-    ids[i] = top_id[(size_t)s * L * K + i];
-  }
-  const size_t ob = (size_t)s * T;
-  for (int i = lane; i < T; i += 64) {
-    tok[ob + i] = (i == 0) ? root_token[s] : -1;
-    parent[ob + i] = -1;
-    depth[ob + i] = (i == 0) ? 0 : -1;
-    score[ob + i] = (i == 0) ? 0.f : -INFINITY;
-    anc[ob + i] = 0;
+  for (int i0 = 0; i0 < L * K; i0 += 8 * 64) {  // eight loads of each in flight per lane
+    float a[8];
+    int b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + 64 * u + lane, L * K - 1);
+      a[u] = top_lp[(size_t)s * L * K + i];
+      b[u] = top_id[(size_t)s * L * K + i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + 64 * u + lane, L * K - 1);
+      lp[i] = a[u];
+      ids[i] = b[u];
+    }
   }
   __syncthreads();
 
   // best candidate of depth d + 1 (rank 0) in lane d
   const float blp = lane < L ? lp[lane * K] : -INFINITY;
   const int btok = lane < L ? ids[lane * K] : -1;
-  // built nodes: score and ancestor mask of node i held by lane i (i <= 63 are read)
-  float nsc = 0.f;
+  // node i (i <= 63) in lane i: token, parent, depth, score, ancestor mask
+  int ntk_o = lane == 0 ? root_token[s] : -1, npar = -1, ndep = lane == 0 ? 0 : -1;
+  float nsc = lane == 0 ? 0.f : -INFINITY;
   uint64_t nan = 0ull;
+  int tok64 = -1, par64 = -1, dep64 = -1;  // node 64
+  float sc64 = -INFINITY;
+  uint64_t anc64 = 0ull;
 
-  Slot sl;
-  sl.valid = false;
-  sl.score = sl.nlp = 0.f;
-  sl.tok = sl.par = sl.dep = sl.rank = sl.ntok = 0;
+  // the slot in this lane
+  float s_sc = 0.f, s_nlp = -INFINITY;
+  int s_tok = 0, s_par = 0, s_dep = 0, s_rk = 0, s_ntk = -1;
+  bool s_ok = false;
   int nslots = 0;
-  // (fields assigned one by one: a reference chosen at run time would put the slot in
-  // scratch memory)
-  auto put = [&](int idx, float sc, int tk, int pr, int dp, int rk) {
-    if (idx == lane) {
-      sl.score = sc; sl.tok = tk; sl.par = pr; sl.dep = dp; sl.rank = rk; sl.valid = true;
-      const int nx = (dp - 1) * K + rk + 1;
-      sl.ntok = rk + 1 < K ? ids[nx] : -1;
-      sl.nlp = rk + 1 < K ? lp[nx] : -INFINITY;
-    }
-  };
   const int tok0 = __builtin_amdgcn_readlane(btok, 0);
-  if (T > 1 && L >= 1 && tok0 >= 0)
-    put(nslots++, 0.f + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), 0)), tok0,
-        0, 1, 0);
+  if (T > 1 && L >= 1 && tok0 >= 0) {
+    const float sc0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), 0));
+    const int nt = 1 < K ? ids[1] : -1;
+    const float nl = 1 < K ? lp[1] : -INFINITY;
+    if (lane == 0) {
+      s_sc = sc0; s_tok = tok0; s_par = 0; s_dep = 1; s_rk = 0; s_ntk = nt; s_nlp = nl; s_ok = true;
+    }
+    nslots = 1;
+  }
 
   for (int i = 1; i < T; ++i) {
-    const uint64_t k = slot_key(sl);
-    const uint64_t best = wave_max_u64_uniform(k);
-    if (best == 0) break;
-    const int owner = __builtin_amdgcn_readfirstlane((int)__ffsll((unsigned long long)__ballot(k == best && k != 0)) - 1);
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl.score), owner));
-    const int tk = __builtin_amdgcn_readlane(sl.tok, owner), pr = __builtin_amdgcn_readlane(sl.par, owner);
-    const int dp = __builtin_amdgcn_readlane(sl.dep, owner), rk = __builtin_amdgcn_readlane(sl.rank, owner);
-    const int ntk = __builtin_amdgcn_readlane(sl.ntok, owner);
-    const float nlp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl.nlp), owner));
+    const uint32_t k32 = s_ok ? max(float_key(s_sc), 1u) : 0u;  // 0: an empty slot
+    const uint32_t m32 = wave_max_u32_uniform(k32);
+    if (m32 == 0) break;
+    uint64_t tie = __ballot(s_ok && k32 == m32);
+    int owner;
+    if (__popcll(tie) == 1) {
+      owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(tie));
+    } else {  // equal scores: token asc, then parent row asc
+      const bool inn = s_ok && k32 == m32;
+      const uint64_t k = inn ? frontier_key(s_sc, s_tok, s_par) : 0ull;
+      const uint64_t best = wave_max_u64_uniform(k);
+      owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(__ballot(inn && k == best)));
+    }
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sc), owner));
+    const int tk = __builtin_amdgcn_readlane(s_tok, owner), pr = __builtin_amdgcn_readlane(s_par, owner);
+    const int dp = __builtin_amdgcn_readlane(s_dep, owner), rk = __builtin_amdgcn_readlane(s_rk, owner);
+    const int ntk = __builtin_amdgcn_readlane(s_ntk, owner);
+    const float nlp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_nlp), owner));
     const uint64_t a = readlane_u64(nan, pr) | (1ull << (i - 1));
-    if (lane == 0) {
-      tok[ob + i] = tk; parent[ob + i] = pr; depth[ob + i] = dp; score[ob + i] = sc; anc[ob + i] = a;
+    const float psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nsc), pr));
+    // node i's row
+    if (i < 64) {
+      const bool me = lane == i;
+      ntk_o = me ? tk : ntk_o;
+      npar = me ? pr : npar;
+      ndep = me ? dp : ndep;
+      nsc = me ? sc : nsc;
+      nan = me ? a : nan;
+    } else {
+      tok64 = tk; par64 = pr; dep64 = dp; sc64 = sc; anc64 = a;
     }
-    if (lane == i) {  // node 64 (never a parent) is not kept
-      nsc = sc;
-      nan = a;
-    }
+    // the next-ranked siblings of the two new entries, both read at once (clamped
+    // addresses; a rank past K has none)
+    const int nxs = min((dp - 1) * K + rk + 2, L * K - 1), nxc = min(dp * K + 1, L * K - 1);
+    const int nts_r = ids[nxs], ntc_r = ids[nxc];
+    const float nls_r = lp[nxs], nlc_r = lp[nxc];
     // the popped slot takes the next-ranked sibling, or empties
-    if (lane == owner) sl.valid = false;
+    const bool own = lane == owner;
     if (ntk >= 0) {
-      const float psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nsc), pr));
-      put(owner, psc + nlp, ntk, pr, dp, rk + 1);
+      const int nt = rk + 2 < K ? nts_r : -1;
+      const float nl = rk + 2 < K ? nls_r : -INFINITY;
+      s_sc = own ? psc + nlp : s_sc;
+      s_tok = own ? ntk : s_tok;
+      s_rk = own ? rk + 1 : s_rk;
+      s_ntk = own ? nt : s_ntk;
+      s_nlp = own ? nl : s_nlp;
+    } else {
+      s_ok = own ? false : s_ok;
     }
     // the best child goes to a fresh slot (none after the last pop)
     if (i + 1 < T && dp < L) {
       const int ctk = __builtin_amdgcn_readlane(btok, dp);
-      if (ctk >= 0)
-        put(nslots++, sc + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), dp)), ctk,
-            i, dp + 1, 0);
+      if (ctk >= 0) {
+        const float cl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), dp));
+        const int nt = 1 < K ? ntc_r : -1;
+        const float nl = 1 < K ? nlc_r : -INFINITY;
+        const bool fr = lane == nslots;
+        s_sc = fr ? sc + cl : s_sc;
+        s_tok = fr ? ctk : s_tok;
+        s_par = fr ? i : s_par;
+        s_dep = fr ? dp + 1 : s_dep;
+        s_rk = fr ? 0 : s_rk;
+        s_ntk = fr ? nt : s_ntk;
+        s_nlp = fr ? nl : s_nlp;
+        s_ok = fr ? true : s_ok;
+        ++nslots;
+      }
     }
+  }
+  // the rows: node i from lane i (rows not reached keep tok -1, depth -1, score -inf)
+  const size_t ob = (size_t)s * T;
+  if (lane < T) {
+    tok[ob + lane] = ntk_o;
+    parent[ob + lane] = npar;
+    depth[ob + lane] = ndep;
+    score[ob + lane] = nsc;
+    anc[ob + lane] = nan;
+  }
+  if (T > 64 && lane == 0) {
+    tok[ob + 64] = tok64;
+    parent[ob + 64] = par64;
+    depth[ob + 64] = dep64;
+    score[ob + 64] = sc64;
+    anc[ob + 64] = anc64;
   }
 }
 
 BuildPlan plan_build_tree(int n, int L, int V, int B, int K) {
   BuildPlan p = {};
   p.K = K;
+  // enough chunks to give the chip about a thousand blocks, each of at least 2048 logits
   int S = cdiv(V, kChunkMax);
-  const int want = cdiv(512, n * L);
+  const int want = cdiv(1024, n * L);
   const int smax_len = V / 2048 > 1 ? V / 2048 : 1;
   if (want > S) S = want < smax_len ? want : (smax_len > S ? smax_len : S);
-  if (S * K > kSortMax) S = kSortMax / K;
-  // the merge sorts S*K candidates; above 1024 its cost outgrows what more chunks save
-  // in the scan, so stay at 1024 when the chunk size allows
-  const int smin = cdiv(V, kChunkMax);
-  if (S * K > 1024 && smin * K <= 1024) S = 1024 / K > smin ? 1024 / K : smin;
+  if (S > 128) S = 128;
   p.chunk = (cdiv(V, S) + 7) / 8 * 8;
   p.S = cdiv(V, p.chunk);
-  int sn = 1;
-  while (sn < p.S * K) sn <<= 1;
-  p.sortN = sn;
+  // a row's candidates fit the merge's LDS (cap >= 64 >= K since S <= 128); a chunk
+  // typically passes about a hundred keys (above cap: the exact path, which writes K)
+  p.cap = kMergeMax / p.S < kCand ? kMergeMax / p.S : kCand;
   const size_t rows = (size_t)n * L;
+  const size_t cw = 4;  // bytes per candidate word for bf16 logits (8 for fp32: see off_cid)
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
-  p.off_ckey = off; off += al(rows * p.S * K * sizeof(float));
-  p.off_cid = off;  off += al(rows * p.S * K * sizeof(int32_t));
+  p.off_ckey = off; off += al(rows * p.S * p.cap * 2 * cw);  // room for 8-byte words
+  p.off_cid = off;  off += al(rows * p.S * (sizeof(int32_t) + sizeof(uint32_t)));  // counts, bounds
   p.off_stat = off; off += al(rows * p.S * sizeof(float2));
   p.off_tid = off;  off += al(rows * K * sizeof(int32_t));
   p.off_tlp = off;  off += al(rows * K * sizeof(float));
@@ -502,28 +794,34 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
                              const int32_t* root_token, int32_t* tok, int32_t* parent, int32_t* depth,
                              float* score, uint64_t* anc, void* ws, hipStream_t st) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  float* cval = reinterpret_cast<float*>(w + plan.off_ckey);
-  int32_t* cid = reinterpret_cast<int32_t*>(w + plan.off_cid);
+  void* cand = w + plan.off_ckey;
+  int32_t* ccount = reinterpret_cast<int32_t*>(w + plan.off_cid);
+  uint32_t* ctau = reinterpret_cast<uint32_t*>(ccount + (size_t)n * L * plan.S);
   float2* stat = reinterpret_cast<float2*>(w + plan.off_stat);
   int32_t* tid = reinterpret_cast<int32_t*>(w + plan.off_tid);
   float* tlp = reinterpret_cast<float*>(w + plan.off_tlp);
   const dim3 g1(n * L, plan.S);
   const int vec = dt == DDT_BF16 ? 8 : 4;
   const bool vload = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 && V % vec == 0 && plan.chunk % vec == 0;
-#define DDT_TOPK(TY, KB, VL)                                                                                     \
-  hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL>), g1, dim3(kTopkThreads), 0, st, static_cast<const TY*>(logits), \
-                     V, plan.chunk, plan.K, cval, cid, stat)
+  const bool small = plan.chunk <= 16 * kTopkThreads;
+#define DDT_TOPK(TY, KB, VL, EM)                                                                                 \
+  hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL, EM>), g1, dim3(kTopkThreads), 0, st,                       \
+                     static_cast<const TY*>(logits), V, plan.chunk, plan.K, plan.cap,                             \
+                     static_cast<typename CandWord<KB>::type*>(cand), ccount, ctau, stat)
   if (dt == DDT_BF16) {
-    if (vload) DDT_TOPK(uint16_t, 16, true);
-    else DDT_TOPK(uint16_t, 16, false);
+    if (vload) { if (small) DDT_TOPK(uint16_t, 16, true, 16); else DDT_TOPK(uint16_t, 16, true, kEmax); }
+    else { if (small) DDT_TOPK(uint16_t, 16, false, 16); else DDT_TOPK(uint16_t, 16, false, kEmax); }
+    hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(n * L), dim3(kMergeThreads), 0, st,
+                       static_cast<const uint32_t*>(cand), ccount, ctau, stat, plan.S, plan.K, plan.cap, plan.chunk,
+                       V, tid, tlp);
   } else {
-    if (vload) DDT_TOPK(float, 32, true);
-    else DDT_TOPK(float, 32, false);
+    if (vload) { if (small) DDT_TOPK(float, 32, true, 16); else DDT_TOPK(float, 32, true, kEmax); }
+    else { if (small) DDT_TOPK(float, 32, false, 16); else DDT_TOPK(float, 32, false, kEmax); }
+    hipLaunchKernelGGL(topk_merge_kernel<32>, dim3(n * L), dim3(kMergeThreads), 0, st,
+                       static_cast<const uint64_t*>(cand), ccount, ctau, stat, plan.S, plan.K, plan.cap, plan.chunk,
+                       V, tid, tlp);
   }
 #undef DDT_TOPK
-  // one thread per compare-exchange of a sorting stage (sortN / 2 <= 1024)
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(n * L), dim3(plan.sortN / 2 < 64 ? 64 : plan.sortN / 2), 0, st, cval,
-                     cid, stat, plan.S, plan.K, plan.sortN, tid, tlp);
   const size_t smem = (size_t)L * plan.K * (sizeof(float) + sizeof(int32_t));
   hipLaunchKernelGGL(heap_expand_kernel, dim3(n), dim3(64), smem, st, tid, tlp, L, plan.K, B + 1, root_token,
                      tok, parent, depth, score, anc);
