@@ -69,7 +69,7 @@ static int build_args(int n, int L, int V, int B, int K, ddt::BuildPlan* plan) {
   DDT_CHECK(V <= (1 << 20), DDT_ERR_UNSUPPORTED, "ddt_build_tree: V=%d exceeds 2^20", V);
   const int keff = k < V ? k : V;
   *plan = ddt::plan_build_tree(n, L, V, B, keff);
-  DDT_CHECK(plan->chunk <= 16384 && plan->cap >= keff, DDT_ERR_UNSUPPORTED,
+  DDT_CHECK(plan->chunk <= 16384 && plan->cap / 2 >= keff, DDT_ERR_UNSUPPORTED,
             "ddt_build_tree: V=%d with K=%d does not fit the chunked top-K", V, k);
   return DDT_OK;
 }

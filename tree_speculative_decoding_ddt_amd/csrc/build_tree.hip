@@ -9,7 +9,7 @@
 //
 // Kernels
 //  1. topk_partial  grid (n*L rows, S chunks).  One HBM pass (16-byte loads): each block
-//     holds its chunk (<= 8192 logits) in registers as raw words, computes the chunk's
+//     holds its chunk (<= 8192 logits, 16384 when there are many rows) in registers as raw words, computes the chunk's
 //     (max, sum exp) and a lower bound for its top keff from the per-thread maximum keys
 //     (per wave, by ballots): at least keff keys reach it.  Every key at or above the
 //     bound (typically about a hundred) is written out unordered as a candidate word
@@ -74,7 +74,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
   }
 }
 
-// A chunk candidate: the key in the high bits, the chunk offset (< 2^13) in the low ones.
+// A chunk candidate: the key in the high bits, the chunk offset (< 2^14) in the low ones.
 template <int KBITS> struct CandWord { typedef uint64_t type; };
 template <> struct CandWord<16> { typedef uint32_t type; };
 
@@ -766,22 +766,25 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
 BuildPlan plan_build_tree(int n, int L, int V, int B, int K) {
   BuildPlan p = {};
   p.K = K;
-  // enough chunks to give the chip about a thousand blocks, each of at least 2048 logits
+  // chunks of up to 8192 logits; 16384 when the rows alone give the chip several
+  // thousand blocks; more, smaller chunks (at least 2048 logits) when the rows are few
   int S = cdiv(V, kChunkMax);
+  if ((long)n * L * S >= 8192 && V > kChunkMax) S = cdiv(V, 2 * kChunkMax);
   const int want = cdiv(1024, n * L);
   const int smax_len = V / 2048 > 1 ? V / 2048 : 1;
   if (want > S) S = want < smax_len ? want : (smax_len > S ? smax_len : S);
-  if (S > 128) S = 128;
+  if (S > 64) S = 64;
   p.chunk = (cdiv(V, S) + 7) / 8 * 8;
   p.S = cdiv(V, p.chunk);
-  // a row's candidates fit the merge's LDS (cap >= 64 >= K since S <= 128); a chunk
-  // typically passes about a hundred keys (above cap: the exact path, which writes K)
+  // candidate space per chunk: cap 4-byte words (bf16 logits) or cap / 2 8-byte words
+  // (fp32).  A row's candidates fit the merge's LDS, and cap / 2 >= 64 >= K (S <= 64).
+  // A chunk typically passes about a hundred keys; above its space it takes the exact
+  // path, which writes K.
   p.cap = kMergeMax / p.S < kCand ? kMergeMax / p.S : kCand;
   const size_t rows = (size_t)n * L;
-  const size_t cw = 4;  // bytes per candidate word for bf16 logits (8 for fp32: see off_cid)
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
-  p.off_ckey = off; off += al(rows * p.S * p.cap * 2 * cw);  // room for 8-byte words
+  p.off_ckey = off; off += al(rows * p.S * p.cap * 4);
   p.off_cid = off;  off += al(rows * p.S * (sizeof(int32_t) + sizeof(uint32_t)));  // counts, bounds
   p.off_stat = off; off += al(rows * p.S * sizeof(float2));
   p.off_tid = off;  off += al(rows * K * sizeof(int32_t));
@@ -803,23 +806,31 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
   const dim3 g1(n * L, plan.S);
   const int vec = dt == DDT_BF16 ? 8 : 4;
   const bool vload = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 && V % vec == 0 && plan.chunk % vec == 0;
-  const bool small = plan.chunk <= 16 * kTopkThreads;
-#define DDT_TOPK(TY, KB, VL, EM)                                                                                 \
-  hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL, EM>), g1, dim3(kTopkThreads), 0, st,                       \
-                     static_cast<const TY*>(logits), V, plan.chunk, plan.K, plan.cap,                             \
-                     static_cast<typename CandWord<KB>::type*>(cand), ccount, ctau, stat)
+  const bool small = plan.chunk <= 16 * kTopkThreads, big = plan.chunk > kChunkMax;
+  const int cap = dt == DDT_BF16 ? plan.cap : plan.cap / 2;  // words of 4 or 8 bytes
+#define DDT_TOPK(TY, KB, VL)                                                                                     \
+  {                                                                                                              \
+    auto* cw_ = static_cast<typename CandWord<KB>::type*>(cand);                                                 \
+    if (small)                                                                                                   \
+      hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL, 16>), g1, dim3(kTopkThreads), 0, st,                   \
+                         static_cast<const TY*>(logits), V, plan.chunk, plan.K, cap, cw_, ccount, ctau, stat);   \
+    else if (big)                                                                                                \
+      hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL, 2 * kEmax>), g1, dim3(kTopkThreads), 0, st,            \
+                         static_cast<const TY*>(logits), V, plan.chunk, plan.K, cap, cw_, ccount, ctau, stat);   \
+    else                                                                                                         \
+      hipLaunchKernelGGL((topk_partial_kernel<TY, KB, VL, kEmax>), g1, dim3(kTopkThreads), 0, st,                \
+                         static_cast<const TY*>(logits), V, plan.chunk, plan.K, cap, cw_, ccount, ctau, stat);   \
+  }
   if (dt == DDT_BF16) {
-    if (vload) { if (small) DDT_TOPK(uint16_t, 16, true, 16); else DDT_TOPK(uint16_t, 16, true, kEmax); }
-    else { if (small) DDT_TOPK(uint16_t, 16, false, 16); else DDT_TOPK(uint16_t, 16, false, kEmax); }
+    if (vload) DDT_TOPK(uint16_t, 16, true) else DDT_TOPK(uint16_t, 16, false)
     hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(n * L), dim3(kMergeThreads), 0, st,
-                       static_cast<const uint32_t*>(cand), ccount, ctau, stat, plan.S, plan.K, plan.cap, plan.chunk,
-                       V, tid, tlp);
+                       static_cast<const uint32_t*>(cand), ccount, ctau, stat, plan.S, plan.K, cap, plan.chunk, V,
+                       tid, tlp);
   } else {
-    if (vload) { if (small) DDT_TOPK(float, 32, true, 16); else DDT_TOPK(float, 32, true, kEmax); }
-    else { if (small) DDT_TOPK(float, 32, false, 16); else DDT_TOPK(float, 32, false, kEmax); }
+    if (vload) DDT_TOPK(float, 32, true) else DDT_TOPK(float, 32, false)
     hipLaunchKernelGGL(topk_merge_kernel<32>, dim3(n * L), dim3(kMergeThreads), 0, st,
-                       static_cast<const uint64_t*>(cand), ccount, ctau, stat, plan.S, plan.K, plan.cap, plan.chunk,
-                       V, tid, tlp);
+                       static_cast<const uint64_t*>(cand), ccount, ctau, stat, plan.S, plan.K, cap, plan.chunk, V,
+                       tid, tlp);
   }
 #undef DDT_TOPK
   const size_t smem = (size_t)L * plan.K * (sizeof(float) + sizeof(int32_t));

@@ -15,7 +15,7 @@ struct BuildPlan {
   int S;          // chunks per (sequence, depth) row
   int chunk;      // elements per chunk (multiple of 8)
   int K;          // candidates per depth
-  int cap;        // candidate words a chunk may write (S * cap <= 8192)
+  int cap;        // candidate words a chunk may write: cap of 4 bytes (bf16), cap / 2 of 8 (fp32)
   size_t off_ckey, off_cid, off_stat, off_tid, off_tlp, total;
 };
 BuildPlan plan_build_tree(int n, int L, int V, int B, int K);
