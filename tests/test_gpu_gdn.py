@@ -92,6 +92,13 @@ def test_full_batch_sampled_heads():
     run_case(33, 8, 64, 15, 32, 128, 4, "bf16", check_heads=[0, 17, 31])
 
 
+def test_full_batch_all_heads_reduced_budget():
+    # the workload's batch and heads (8 sequences, 32 heads of 128) at budget 24: every
+    # head's o and state scratch compared
+    say("gdn bf16 n=8 H=32 dk=128 B=24, all heads")
+    run_case(34, 8, 24, 10, 32, 128, 4, "bf16")
+
+
 def test_deep_chain_and_deep_trees():
     # every row is processed whatever its depth: a 64-deep chain (all 65 rows, depth bound
     # 63), 63-deep chains, and random trees about 40 deep with many branch points
