@@ -614,12 +614,14 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
 // One wavefront per sequence, T = B+1 <= 65.  The frontier has one slot per lane: the
 // seed takes slot 0, pop i puts the popped node's sibling in the popped slot and its best
 // child in slot i at most (a fresh slot per pop), and the child of the last pop is never
-// popped, so 64 slots suffice.  A slot also holds its next-ranked sibling's (token,
-// log-prob), read when the slot is filled, so that a pop reads no LDS on its critical
-// path.  A pop: the wave-wide max of the slots' 32-bit score keys (DPP), the 64-bit key
-// (token, parent) only among lanes tied on the score, the winner's fields by readlane,
-// and the two new entries written by lane selects (no divergent branch).  Node i's row,
-// score and ancestor mask are kept by lane i (node 64 in scalars) and stored at the end.
+// popped, so 64 slots suffice.  A pop's chain is short: the wave-wide max of the slots'
+// 32-bit score keys (DPP; the 64-bit key (token, parent) only among lanes tied on the
+// score), the winner's fields by readlane, and the two new entries written by lane
+// selects.  The new sibling's score is the parent's score (kept in the slot) plus its
+// log-prob (prefetched when the slot was made); the best child comes from the lanes of
+// the depth (ranks 0 and 1 of depth d + 1 in lane d); the one LDS read, the new
+// sibling's own next sibling, is merged one pop later.  Node i's row, score and
+// ancestor mask are kept by lane i (node 64 in scalars) and stored at the end.
 __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restrict__ top_id,
                                                          const float* __restrict__ top_lp, int L, int K,
                                                          int T, const int32_t* __restrict__ root_token,
@@ -630,17 +632,17 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   extern __shared__ uint8_t smem[];
   float* lp = reinterpret_cast<float*>(smem);                  // [L][K]
   int32_t* ids = reinterpret_cast<int32_t*>(lp + L * K);       // [L][K]
-  for (int i0 = 0; i0 < L * K; i0 += 8 * 64) {  // eight loads of each in flight per lane
-    float a[8];
-    int b[8];
+  for (int i0 = 0; i0 < L * K; i0 += 16 * 64) {  // sixteen loads of each in flight per lane
+    float a[16];
+    int b[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = min(i0 + 64 * u + lane, L * K - 1);
       a[u] = top_lp[(size_t)s * L * K + i];
       b[u] = top_id[(size_t)s * L * K + i];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = min(i0 + 64 * u + lane, L * K - 1);
       lp[i] = a[u];
       ids[i] = b[u];
@@ -648,29 +650,37 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   }
   __syncthreads();
 
-  // best candidate of depth d + 1 (rank 0) in lane d
-  const float blp = lane < L ? lp[lane * K] : -INFINITY;
-  const int btok = lane < L ? ids[lane * K] : -1;
+  // ranks 0 and 1 of depth d + 1 in lane d
+  const float bl0 = lane < L ? lp[lane * K] : -INFINITY;
+  const int bt0 = lane < L ? ids[lane * K] : -1;
+  const float bl1 = lane < L && 1 < K ? lp[lane * K + 1] : -INFINITY;
+  const int bt1 = lane < L && 1 < K ? ids[lane * K + 1] : -1;
   // node i (i <= 63) in lane i: token, parent, depth, score, ancestor mask
-  int ntk_o = lane == 0 ? root_token[s] : -1, npar = -1, ndep = lane == 0 ? 0 : -1;
-  float nsc = lane == 0 ? 0.f : -INFINITY;
-  uint64_t nan = 0ull;
+  int o_tok = lane == 0 ? root_token[s] : -1, o_par = -1, o_dep = lane == 0 ? 0 : -1;
+  float o_sc = lane == 0 ? 0.f : -INFINITY;
+  uint64_t o_anc = 0ull;
   int tok64 = -1, par64 = -1, dep64 = -1;  // node 64
   float sc64 = -INFINITY;
   uint64_t anc64 = 0ull;
 
-  // the slot in this lane
-  float s_sc = 0.f, s_nlp = -INFINITY;
-  int s_tok = 0, s_par = 0, s_dep = 0, s_rk = 0, s_ntk = -1;
+  // the slot in this lane: an entry (score, token, parent row, depth, rank), its parent's
+  // score and its next-ranked sibling (token, log-prob); everything a pop needs of the
+  // winner is in the winner's lane or, for the best child, in lanes of the depth
   bool s_ok = false;
+  float s_sc = 0.f, s_psc = 0.f, s_nlp = -INFINITY;
+  int s_tok = 0, s_par = 0, s_dep = 0, s_rk = 0, s_ntk = -1;
+  // the next sibling of a popped slot's new entry is read from LDS at the pop and
+  // merged at the next one, after the reduction that hides its latency
+  int pend_lane = -1, pend_tok = -1;
+  float pend_lp = -INFINITY;
   int nslots = 0;
-  const int tok0 = __builtin_amdgcn_readlane(btok, 0);
+  const int tok0 = __builtin_amdgcn_readlane(bt0, 0);
   if (T > 1 && L >= 1 && tok0 >= 0) {
-    const float sc0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), 0));
-    const int nt = 1 < K ? ids[1] : -1;
-    const float nl = 1 < K ? lp[1] : -INFINITY;
+    const float sc0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl0), 0));
+    const int nt = __builtin_amdgcn_readlane(bt1, 0);
+    const float nl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl1), 0));
     if (lane == 0) {
-      s_sc = sc0; s_tok = tok0; s_par = 0; s_dep = 1; s_rk = 0; s_ntk = nt; s_nlp = nl; s_ok = true;
+      s_sc = sc0; s_tok = tok0; s_par = 0; s_dep = 1; s_rk = 0; s_psc = 0.f; s_ntk = nt; s_nlp = nl; s_ok = true;
     }
     nslots = 1;
   }
@@ -679,7 +689,12 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
     const uint32_t k32 = s_ok ? max(float_key(s_sc), 1u) : 0u;  // 0: an empty slot
     const uint32_t m32 = wave_max_u32_uniform(k32);
     if (m32 == 0) break;
-    uint64_t tie = __ballot(s_ok && k32 == m32);
+    if (pend_lane >= 0) {
+      const bool me = lane == pend_lane;
+      s_ntk = me ? pend_tok : s_ntk;
+      s_nlp = me ? pend_lp : s_nlp;
+    }
+    const uint64_t tie = __ballot(s_ok && k32 == m32);
     int owner;
     if (__popcll(tie) == 1) {
       owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(tie));
@@ -689,70 +704,62 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
       const uint64_t best = wave_max_u64_uniform(k);
       owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(__ballot(inn && k == best)));
     }
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sc), owner));
+#define DDT_RLF(x) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), owner))
+    const float sc = DDT_RLF(s_sc), psc = DDT_RLF(s_psc), nlp = DDT_RLF(s_nlp);
+#undef DDT_RLF
     const int tk = __builtin_amdgcn_readlane(s_tok, owner), pr = __builtin_amdgcn_readlane(s_par, owner);
     const int dp = __builtin_amdgcn_readlane(s_dep, owner), rk = __builtin_amdgcn_readlane(s_rk, owner);
     const int ntk = __builtin_amdgcn_readlane(s_ntk, owner);
-    const float nlp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_nlp), owner));
-    const uint64_t a = readlane_u64(nan, pr) | (1ull << (i - 1));
-    const float psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nsc), pr));
-    // node i's row
-    if (i < 64) {
-      const bool me = lane == i;
-      ntk_o = me ? tk : ntk_o;
-      npar = me ? pr : npar;
-      ndep = me ? dp : ndep;
-      nsc = me ? sc : nsc;
-      nan = me ? a : nan;
-    } else {
-      tok64 = tk; par64 = pr; dep64 = dp; sc64 = sc; anc64 = a;
-    }
-    // the next-ranked siblings of the two new entries, both read at once (clamped
-    // addresses; a rank past K has none)
-    const int nxs = min((dp - 1) * K + rk + 2, L * K - 1), nxc = min(dp * K + 1, L * K - 1);
-    const int nts_r = ids[nxs], ntc_r = ids[nxc];
-    const float nls_r = lp[nxs], nlc_r = lp[nxc];
-    // the popped slot takes the next-ranked sibling, or empties
+    // the popped slot takes its next-ranked sibling (whose own next sibling is fetched
+    // now), or empties; the best child goes to a fresh slot (none after the last pop).
+    // Written without branches: every update is a lane select.
     const bool own = lane == owner;
-    if (ntk >= 0) {
-      const int nt = rk + 2 < K ? nts_r : -1;
-      const float nl = rk + 2 < K ? nls_r : -INFINITY;
-      s_sc = own ? psc + nlp : s_sc;
-      s_tok = own ? ntk : s_tok;
-      s_rk = own ? rk + 1 : s_rk;
-      s_ntk = own ? nt : s_ntk;
-      s_nlp = own ? nl : s_nlp;
-    } else {
-      s_ok = own ? false : s_ok;
-    }
-    // the best child goes to a fresh slot (none after the last pop)
-    if (i + 1 < T && dp < L) {
-      const int ctk = __builtin_amdgcn_readlane(btok, dp);
-      if (ctk >= 0) {
-        const float cl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, blp), dp));
-        const int nt = 1 < K ? ntc_r : -1;
-        const float nl = 1 < K ? nlc_r : -INFINITY;
-        const bool fr = lane == nslots;
-        s_sc = fr ? sc + cl : s_sc;
-        s_tok = fr ? ctk : s_tok;
-        s_par = fr ? i : s_par;
-        s_dep = fr ? dp + 1 : s_dep;
-        s_rk = fr ? 0 : s_rk;
-        s_ntk = fr ? nt : s_ntk;
-        s_nlp = fr ? nl : s_nlp;
-        s_ok = fr ? true : s_ok;
-        ++nslots;
-      }
+    const bool sib = ntk >= 0;
+    s_sc = own && sib ? psc + nlp : s_sc;
+    s_tok = own && sib ? ntk : s_tok;
+    s_rk = own && sib ? rk + 1 : s_rk;
+    s_ok = own && !sib ? false : s_ok;
+    const int nx = min(max((dp - 1) * K + rk + 2, 0), L * K - 1);
+    pend_tok = sib && rk + 2 < K ? ids[nx] : -1;
+    pend_lp = sib && rk + 2 < K ? lp[nx] : -INFINITY;
+    pend_lane = sib ? owner : -1;
+    const int dpc = min(dp, 63);
+    const int ctk = __builtin_amdgcn_readlane(bt0, dpc);
+    const float clp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl0), dpc));
+    const int cnt = __builtin_amdgcn_readlane(bt1, dpc);
+    const float cnl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl1), dpc));
+    const bool chd = i + 1 < T && dp < L && ctk >= 0;
+    const bool fr = chd && lane == nslots;
+    s_sc = fr ? sc + clp : s_sc;
+    s_tok = fr ? ctk : s_tok;
+    s_par = fr ? i : s_par;
+    s_dep = fr ? dp + 1 : s_dep;
+    s_rk = fr ? 0 : s_rk;
+    s_psc = fr ? sc : s_psc;
+    s_ntk = fr ? cnt : s_ntk;
+    s_nlp = fr ? cnl : s_nlp;
+    s_ok = fr ? true : s_ok;
+    nslots += chd ? 1 : 0;
+    // node i's row (off the next pop's path)
+    const uint64_t a = readlane_u64(o_anc, pr) | (1ull << (i - 1));
+    const bool me = lane == i;
+    o_tok = me ? tk : o_tok;
+    o_par = me ? pr : o_par;
+    o_dep = me ? dp : o_dep;
+    o_sc = me ? sc : o_sc;
+    o_anc = me ? a : o_anc;
+    if (i == 64) {
+      tok64 = tk; par64 = pr; dep64 = dp; sc64 = sc; anc64 = a;
     }
   }
   // the rows: node i from lane i (rows not reached keep tok -1, depth -1, score -inf)
   const size_t ob = (size_t)s * T;
   if (lane < T) {
-    tok[ob + lane] = ntk_o;
-    parent[ob + lane] = npar;
-    depth[ob + lane] = ndep;
-    score[ob + lane] = nsc;
-    anc[ob + lane] = nan;
+    tok[ob + lane] = o_tok;
+    parent[ob + lane] = o_par;
+    depth[ob + lane] = o_dep;
+    score[ob + lane] = o_sc;
+    anc[ob + lane] = o_anc;
   }
   if (T > 64 && lane == 0) {
     tok[ob + 64] = tok64;
