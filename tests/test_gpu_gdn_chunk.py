@@ -34,10 +34,10 @@ def parents_of(rng, kind, n, B, L):
     return out
 
 
-def run(seed, n, B, L, H, dk, kind, heads=None):
+def run(seed, n, B, L, H, dk, kind, heads=None, W=4):
     rng = np.random.default_rng(seed)
     parents = parents_of(rng, kind, n, B, L)
-    x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, 4)
+    x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, W)
     xt, xe = up(x["x"], "bf16")
     vt, ve = up(x["v"], "bf16")
     cst, cse = up(x["conv_state"], "bf16")
@@ -67,6 +67,13 @@ def test_head_sizes(dk):
 def test_tree_shapes(kind):
     say("gdn chunk", kind)
     run(70, 2, 64, 63 if kind in ("chain", "deep") else 15, 4, 128, kind)
+
+
+@pytest.mark.parametrize("W", [2, 3, 5, 8])
+def test_conv_widths(W):
+    # widths other than 4 take the generic tap loop (taps past W weigh nothing)
+    say("gdn chunk W", W)
+    run(100 + W, 2, 40, 10, 2, 128, "random", W=W)
 
 
 def test_small_trees():
