@@ -75,14 +75,16 @@ __device__ void dfs_order(const int* par, int Tn, int* sz, int* nch, int* esib, 
     const int vp = (p >= 0 && p < tid) ? p : -1;
     const int my = sz[tid];
     int e = 0;
+    // branch-free and unrolled, so that the (broadcast) LDS reads of several j are in
+    // flight together
+#pragma unroll 8
     for (int j = 0; j < Tn; ++j) {
-      if (j == tid) continue;
-      const int pj = par[j];
+      const int pj = par[j], szj = sz[j];
       const int vpj = (pj >= 0 && pj < j) ? pj : -1;
-      if (vpj != vp) continue;
-      const bool before = sz[j] < my || (sz[j] == my && j < tid);
-      if (before) e += sz[j];
-      else light = 1;
+      const bool sib = vpj == vp && j != tid;
+      const bool before = szj < my || (szj == my && j < tid);
+      e += sib && before ? szj : 0;
+      light |= sib && !before;
     }
     esib[tid] = e;
     if (vp < 0) light = 0;  // the roots' order needs no stack: each reads the committed state
