@@ -214,10 +214,12 @@ int ddt_tree_attn_rope(const void* q, const void* k_new, const void* v_new, cons
  *   S [n][H][dv][dk] (f32, committed, read only), S_scratch [n][T][H][dv][dk] (f32, written)
  *   o [n][T][H][dv] (act_dt, written)
  *   parent [n][T] int32: parent[i] < i, or < 0 for a row that reads the committed state
- *   L: the tree's depth bound, 0 <= L <= 63 (validated only: every row is processed,
- *      whatever its depth by parent chain)
- *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q in fp32,
- *       and the tree's depth-first order)
+ *   L: the tree's depth bound, 0 <= L <= 63.  Every row is processed whatever its depth
+ *      by parent chain; L only selects the method (bf16 activations, states stored and
+ *      L <= 16: chunk form, every state formed from S and its path's w k^T terms;
+ *      otherwise the node-by-node walk).  Both agree to fp32 rounding.
+ *   ws: workspace of ddt_gdn_tree_step_workspace() bytes (per-node q, k and k.q, or k
+ *       and w, in fp32, the tree's depth-first order or depths, and the path records)
  * S_scratch and conv_scratch may both be NULL: then no node state is stored (o is still
  * written for every node) and the commit replays the accepted path with ddt_gdn_replay.
  * x, conv_state, conv_scratch, S, S_scratch and ws must be 16-byte aligned.

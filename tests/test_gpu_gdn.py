@@ -113,3 +113,33 @@ def test_deep_chain_and_deep_trees():
 def test_star_and_root_only():
     run_case(42, 2, 64, 1, 2, 128, 4, "bf16", kind="star")
     run_case(43, 2, 0, 1, 2, 64, 4, "f32")    # B = 0: the root alone
+
+
+def test_chunk_form_states():
+    # bf16 activations with the depth bound at most 24 form the node states from the chunk
+    # form (w and k of each path node); a tree deeper than the bound given still comes out
+    # right (the bound only picks the path)
+    say("gdn stored states, chunk form: chain 64 deep at bound 15, deep trees dk 64, root alone, W 5")
+    run_case(50, 2, 64, 15, 2, 128, 4, "bf16", kind="chain")
+    run_case(51, 3, 64, 20, 2, 64, 4, "bf16", kind="deep")
+    run_case(52, 2, 0, 1, 2, 128, 4, "bf16")
+    run_case(53, 2, 40, 12, 3, 64, 5, "bf16")
+
+
+def test_chunk_form_matches_walk_states():
+    # the same inputs through both ways of storing states (bound 15: chunk form; bound 63:
+    # the walk): states within fp32 rounding of each other, conv scratch identical
+    say("gdn stored states: chunk form vs walk")
+    rng = np.random.default_rng(54)
+    n, B, L, H, dk = 3, 64, 15, 4, 128
+    parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, 4)
+    dev = {k: up(x[k], "bf16" if k in ("x", "v", "conv_state") else "f32")[0] for k in x}
+    pt = up_int(parents)
+    args = (dev["x"], dev["conv_w"], dev["conv_state"], dev["v"], dev["beta"], dev["g"], dev["S"], pt)
+    a = ddt.gdn_tree_step(*args, 15)
+    b = ddt.gdn_tree_step(*args, 63)
+    torch.cuda.synchronize()
+    assert_close(down(a["S_scratch"]), down(b["S_scratch"]), "f32", "states chunk form vs walk")
+    assert_close(down(a["o"]), down(b["o"]), "bf16", "o chunk form vs walk")
+    np.testing.assert_array_equal(down(a["conv_scratch"]), down(b["conv_scratch"]))

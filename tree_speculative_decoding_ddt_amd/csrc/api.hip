@@ -334,7 +334,7 @@ int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state
                 aligned16(conv_scratch),
             DDT_ERR_ARG, "ddt_gdn_tree_step: workspace, state and activation buffers must be 16-byte aligned");
   return hip_status(ddt::launch_gdn_tree_step(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o,
-                                              parent, n, B + 1, H, dk, C, W, act_dt, ws,
+                                              parent, n, B + 1, L, H, dk, C, W, act_dt, ws,
                                               static_cast<hipStream_t>(stream)),
                     "ddt_gdn_tree_step");
 }

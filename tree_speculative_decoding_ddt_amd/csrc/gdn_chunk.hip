@@ -1,7 +1,8 @@
-// Short conv + Gated DeltaNet tree step without stored node states, in chunk form on the
-// matrix cores.
-// Sources: "DDTree on vLLM: candid research notes", section "Where the next step is"
-// (scratch-buffer GDN replay instead of one state per branch); "The architecture of
+// Short conv + Gated DeltaNet tree step in chunk form on the matrix cores: without stored
+// node states, or with them (formed afterwards, each from S0 and its path's terms).
+// Sources: "DDTree on vLLM: candid research notes", sections "Why hybrid attention makes
+// it hard" (each node's state and conv state written to scratch) and "Where the next step
+// is" (scratch-buffer GDN replay instead of one state per branch); "The architecture of
 // speculation", section "The DDTree Integration Challenge" (recompute rather than keep a
 // recurrent state per branch).
 //
@@ -16,7 +17,8 @@
 // so the dense work is S0 [K | Q] (T x dv from dk x dv) and the Gram products K K^T and
 // Q K^T (T x T), on the matrix cores, and what remains is a triangular solve over the
 // tree with dv right-hand sides, in which the nodes of one depth are independent.  No
-// node state is formed.
+// node state is formed here; with states stored (STORE) the kernel also writes the conv
+// scratch and leaves k, w and the path records for gdn_states_kernel.
 //
 // One block per (sequence, head), 4 waves.  Every global load of a phase is issued
 // before any of its results is used (unconditional loads at clamped addresses), so each
@@ -63,6 +65,12 @@ __device__ __forceinline__ cf32x4 mfma3(const cbf16x8& ah, const cbf16x8& al, co
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
 }
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and scalar) operations,
+// not for its global stores, which a __syncthreads() fence would wait out (the exports of
+// the stored-state variant are still in flight there).  The memory clobber keeps the
+// compiler from moving memory accesses across it; loads issued before it are still waited
+// for where their results are used.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // 8 consecutive activations as fp32
 template <typename A> __device__ __forceinline__ void load8(const A* p, float (&x)[8]);
 template <> __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
@@ -89,6 +97,24 @@ constexpr int kChunkMaxT = 65;   // nodes (budget <= 64 plus the root)
 // its (k+1)-th ancestor (k = 0: the parent).  Parents precede their children, so t has
 // at most t ancestors and T(T-1)/2 slots hold every record.
 __host__ __device__ inline int rec_base(int t) { return t * (t - 1) / 2; }
+
+// What the chunk kernel hands to gdn_states_kernel when node states are stored (device
+// arrays in the workspace; TRI = rec_base(T) record slots per tree):
+//   k [n][T][H][dk], w [n][T][H][dv]  the normalised keys and the solve's w (fp32)
+//   gam [n][T][H]                     G_t
+//   dep [n][T]                        proper ancestors of t (head independent)
+//   rows [n][TRI]                     t's (k+1)-th ancestor at slot rec_base(t) + k
+//   rho [n][H][TRI]                   r_tj of that ancestor
+// and the conv scratch [n][T][W-1][C], which the chunk kernel writes itself.
+struct ChunkStoreOut {
+  uint16_t* conv_scratch;
+  float* k;
+  float* w;
+  float* gam;
+  int32_t* dep;
+  int32_t* rows;
+  float* rho;
+};
 
 // LDS layout (bytes) for T nodes (bf16 row stride RSB = 2*dk + 16):
 //   KQ      K hi, K lo, Q hi, Q lo: [T+1] rows each (row T stays zero: the rows of a
@@ -118,14 +144,16 @@ __host__ __device__ inline ChunkLayout chunk_layout(int T, int dk, int W) {
   return c;
 }
 
-// WT = 4: conv width exactly 4; WT = 8: any width up to 8 (taps past W weigh 0)
-template <int DK, int WT>
+// WT = 4: conv width exactly 4; WT = 8: any width up to 8 (taps past W weigh 0).
+// STORE: also hand the per-node states to gdn_states_kernel (ChunkStoreOut) and write
+// the conv scratch.
+template <int DK, int WT, bool STORE>
 __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restrict__ x, const float* __restrict__ conv_w,
                                                         const uint16_t* __restrict__ conv_state,
                                                         const uint16_t* __restrict__ v, const float* __restrict__ beta,
                                                         const float* __restrict__ g, const float* __restrict__ S,
                                                         uint16_t* __restrict__ o, const int32_t* __restrict__ parent,
-                                                        int Tn, int H, int W) {
+                                                        int Tn, int H, int W, ChunkStoreOut so) {
   constexpr int DV = DK, RSB = 2 * DK + 16, NCS = DK / 32, NRT = DV / 16;
   constexpr int RTW = (NRT + 3) / 4;   // 16-row tiles of S0 per wave
   constexpr int NG = DK / 8;           // conv: lanes per (node, q or k part), 8 channels each
@@ -241,16 +269,22 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       const float ga = gg[a];
       if (!(p >= 0 && p < a)) {
         Gam[t] = prod * ga;
+        if (STORE) so.gam[((size_t)s * Tn + t) * H + h] = prod * ga;
         break;
       }
       prod *= ga;
       a = p;
       rec[rb + k] = make_float4(__int_as_float(a), prod, 0.f, 0.f);
+      if (STORE) {
+        so.rho[((size_t)s * H + h) * rec_base(Tn) + rb + k] = prod;
+        if (h == 0) so.rows[(size_t)s * rec_base(Tn) + rb + k] = a;
+      }
       ++k;
       if (k < W) win[t * kChunkMaxW + k] = a;
     }
     for (int b = k + 1; b < W; ++b) win[t * kChunkMaxW + b] = Tn + W - 1 - (b - k);
     dep[t] = k;
+    if (STORE && h == 0) so.dep[(size_t)s * Tn + t] = k;
     atomicAdd(&cnt[k], 1);
   }
   __syncthreads();
@@ -310,6 +344,11 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       const float sc = half ? 1.f / sqrtf(ss[u] + 1e-6f) : rsqrtf((float)DK);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[u][e] *= sc;
+      if (STORE && half) {  // the normalised k in fp32 (a clamped duplicate node writes the same values)
+        float* kd = so.k + (((size_t)s * Tn + tt[u]) * H + h) * DK + 8 * cg;
+        *reinterpret_cast<float4*>(kd) = make_float4(y[u][0], y[u][1], y[u][2], y[u][3]);
+        *reinterpret_cast<float4*>(kd + 4) = make_float4(y[u][4], y[u][5], y[u][6], y[u][7]);
+      }
       cbf16x8 hi, lo;
       split8(y[u], hi, lo);
       const int base = (half ? 0 : 2) * RW * RSB + tt[u] * RSB + cg * 16;  // K hi/lo first, then Q hi/lo
@@ -317,9 +356,29 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       *reinterpret_cast<cbf16x8*>(lds + base + RW * RSB) = lo;
     }
   }
-  __syncthreads();
+  if (STORE) {
+    // record slots of t past its dep[t] ancestors (t has t slots): a valid row (t) with
+    // ratio 0, so that the states kernel may read t's first slots before its depth
+    for (int t = 1; t < Tn; ++t)
+      for (int k = dep[t] + tid; k < t; k += 256) {
+        so.rho[((size_t)s * H + h) * rec_base(Tn) + rec_base(t) + k] = 0.f;
+        if (h == 0) so.rows[(size_t)s * rec_base(Tn) + rec_base(t) + k] = t;
+      }
+    // conv scratch of every node: its window's newest W-1 rows (back b in slot W-2-b),
+    // the head's q and k channels, copied from the stage
+    const int Wc = WT == 4 ? 4 : W;  // a constant divisor where the width is fixed
+    const int per_node = (Wc - 1) * ROW8;
+    for (int idx = tid; idx < Tn * per_node; idx += 256) {
+      const int t = idx / per_node, rem = idx % per_node, slot = rem / ROW8, ch = rem % ROW8;
+      const int r = win[t * kChunkMaxW + (Wc - 2 - slot)];
+      const int chan = ch < ROW8 / 2 ? h * DK + 8 * ch : H * DK + h * DK + 8 * (ch - ROW8 / 2);
+      *reinterpret_cast<uint4*>(so.conv_scratch + (((size_t)s * Tn + t) * (Wc - 1) + slot) * C + chan) =
+          *reinterpret_cast<const uint4*>(stage + (size_t)r * (2 * DK) + 8 * ch);
+    }
+  }
+  lds_barrier();
   if (tid < Tn) cnt[tid] = 0;  // the fill counters (every read of the histogram is done)
-  __syncthreads();
+  lds_barrier();
   if (tid < Tn) ord[lstart[dep[tid]] + atomicAdd(&cnt[dep[tid]], 1)] = tid;
 
   // ---- P1: S0 [K|Q] as D[r][t] (lane: node column 16*ti + l16, rows 16*rt + 4*q4 + e)
@@ -386,7 +445,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       gk[k][1] = mfma3(qh, ql, jh, jl, gk[k][1]);
     }
   }
-  __syncthreads();  // every wave is done with q/k: their area now takes w and the o base
+  lds_barrier();  // every wave is done with q/k: their area now takes w and the o base
 
   // ---- P2: right-hand sides beta_t (v_t - G_t S0 k_t), the o base G_t S0 q_t, M_tt, and
   // the records' coefficients
@@ -464,7 +523,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P3: the solve, depth by depth, without barriers: wave `wave` owns columns
   // [CPW*wave, CPW*(wave+1)), a lane 4 of them for NS nodes (slots), NGP nodes side by
@@ -503,6 +562,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
         if (dp[i] != e) continue;
         const int t = tt[i];
         *reinterpret_cast<float4*>(&Wm[t * WS + c]) = aw[i];
+        if (STORE) *reinterpret_cast<float4*>(so.w + (((size_t)s * Tn + t) * H + h) * DV + c) = aw[i];
         uint2 u;
         u.x = (uint32_t)f32_to_bf16(ao[i].x + md[i] * aw[i].x) | ((uint32_t)f32_to_bf16(ao[i].y + md[i] * aw[i].y) << 16);
         u.y = (uint32_t)f32_to_bf16(ao[i].z + md[i] * aw[i].z) | ((uint32_t)f32_to_bf16(ao[i].w + md[i] * aw[i].w) << 16);
@@ -546,13 +606,115 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   }
 }
 
+// Every node's state S_t = G_t S0 + sum_{i in path(t)} r_ti w_i k_i^T written out by
+// short-lived blocks, each R = RB*RPT rows (RPT*4 KB) of one (sequence, node, head)
+// state, blocks in the order of S_scratch.  Blocks that each write one small piece and
+// end keep the writes in flight over a narrow, advancing address range, as a fill does;
+// a block that writes a whole state (or a persistent block walking nodes) spreads them
+// over every state in flight.
+// The path is t itself (ratio 1) followed by its records, taken NB at a time: the block
+// stages each path node's k row and its ratio times the w of the block's rows in LDS
+// (one coalesced pass: 16 threads per path node), then a thread (4 columns of RPT
+// consecutive rows) adds r w k^T from LDS.  Every node's first record slots hold a valid
+// row (ratio 0 past its depth), so the first batch's rows and ratios are read with S0,
+// before the depth is known: a node less than NB deep waits on memory twice.
+constexpr int kStatesNB = 8;  // path nodes staged per batch
+
+template <int DK, int RPT>
+__global__ void __launch_bounds__(256) gdn_states_kernel(const float* __restrict__ S, const float* __restrict__ kf,
+                                                         const float* __restrict__ wf, const int32_t* __restrict__ rows,
+                                                         const float* __restrict__ rho, const float* __restrict__ gam,
+                                                         const int32_t* __restrict__ dep, float* __restrict__ S_scratch,
+                                                         int Tn, int H) {
+  constexpr int DV = DK, LPR = DK / 4, RB = 256 / LPR, R = RB * RPT, BPS = DV / R;
+  static_assert(BPS * R == DV, "a block covers whole rows of one state");
+  constexpr int NB = kStatesNB, TPN = 256 / NB;  // path nodes per batch; staging threads per node
+  constexpr int NK4 = DK / 4, NW4 = R / 4, NP4 = NK4 + NW4;  // 16-byte pieces per path node
+  __shared__ float4 kS[NB][NK4];
+  __shared__ __align__(16) float wS[NB][R];
+  const int TRI = rec_base(Tn);
+  const int state = blockIdx.x / BPS, r0 = (blockIdx.x % BPS) * R;  // state = (s*T + t)*H + h
+  const int h = state % H, st = state / H, s = st / Tn, t = st % Tn;
+  const int tid = threadIdx.x, c4 = tid % LPR, rr = (tid / LPR) * RPT;  // rows r0+rr .. +RPT-1
+  const int base = rec_base(t);
+  const int d = dep[st];  // t's records: base .. base + d - 1 (d <= t)
+  const float G = gam[state];
+  const float* S0 = S + ((size_t)s * H + h) * DV * DK;
+  float4 acc[RPT];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) acc[q] = *reinterpret_cast<const float4*>(S0 + (size_t)(r0 + rr + q) * DK + 4 * c4);
+  const int u = tid / TPN, pl = tid % TPN;  // staging: path node u of the batch, piece lane pl
+  for (int i0 = 0; i0 <= d; i0 += NB) {
+    // path entry i = i0 + u: t itself (i = 0) or record i-1; the first batch clamps to t's
+    // own slots (written for any t >= 1; slot 0 for the root), later ones to the depth
+    const int i = i0 + u;
+    const int kk = i0 == 0 ? min(max(i - 1, 0), max(t - 1, 0)) : min(i - 1, d - 1);
+    const bool rec = i > 0 && TRI > 0;
+    const int j = rec ? rows[(size_t)s * TRI + base + kk] : t;
+    const float cr = rec ? rho[((size_t)s * H + h) * TRI + base + kk] : 1.f;
+    const size_t js = ((size_t)s * Tn + j) * H + h;
+    float4 pc[(NP4 + TPN - 1) / TPN];
+#pragma unroll
+    for (int m = 0; m < (NP4 + TPN - 1) / TPN; ++m) {
+      const int o = min(pl + TPN * m, NP4 - 1);
+      pc[m] = o < NK4 ? *reinterpret_cast<const float4*>(kf + js * DK + 4 * o)
+                      : *reinterpret_cast<const float4*>(wf + js * DV + r0 + 4 * (o - NK4));
+    }
+    const float c = i <= d ? cr : 0.f;  // past t's path: weight 0
+    if (i0 > 0) __syncthreads();        // the previous batch's reads are done
+#pragma unroll
+    for (int m = 0; m < (NP4 + TPN - 1) / TPN; ++m) {
+      const int o = pl + TPN * m;
+      if (o < NK4) kS[u][o] = pc[m];
+      else if (o < NP4) *reinterpret_cast<float4*>(&wS[u][4 * (o - NK4)]) =
+          make_float4(c * pc[m].x, c * pc[m].y, c * pc[m].z, c * pc[m].w);
+    }
+    __syncthreads();
+    if (i0 == 0) {
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        acc[q].x *= G;
+        acc[q].y *= G;
+        acc[q].z *= G;
+        acc[q].w *= G;
+      }
+    }
+    const int nv = min(NB, d + 1 - i0);  // path nodes of this batch (uniform)
+#pragma unroll
+    for (int v = 0; v < NB; ++v) {
+      if (v >= nv) break;
+      const float4 kv = kS[v][c4];
+      float wv[RPT];
+      if constexpr (RPT == 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&wS[v][rr]);
+        wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) wv[q] = wS[v][rr + q];
+      }
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        acc[q].x += wv[q] * kv.x;
+        acc[q].y += wv[q] * kv.y;
+        acc[q].z += wv[q] * kv.z;
+        acc[q].w += wv[q] * kv.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const cf32x4 out = {acc[q].x, acc[q].y, acc[q].z, acc[q].w};
+    __builtin_nontemporal_store(out, reinterpret_cast<cf32x4*>(S_scratch + ((size_t)state * DV + r0 + rr + q) * DK + 4 * c4));
+  }
+}
+
 size_t gdn_chunk_lds_bytes(int T, int dk, int W) { return (size_t)chunk_layout(T, dk, W).total; }
 
-template <int DK, int WT>
+template <int DK, int WT, bool STORE>
 static void launch_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
                          const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
-                         int T, int H, int W, hipStream_t st) {
-  auto kern = gdn_chunk_kernel<DK, WT>;
+                         int T, int H, int W, const ChunkStoreOut& so, hipStream_t st) {
+  auto kern = gdn_chunk_kernel<DK, WT, STORE>;
   // the dynamic LDS limit is raised once per kernel, to the largest size any call uses
   // (a host-side attribute, not a stream operation: calls stay capturable in a graph)
   static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -561,22 +723,67 @@ static void launch_chunk(const void* x, const float* conv_w, const void* conv_st
   (void)attr;
   hipLaunchKernelGGL(kern, dim3(n * H), dim3(256), gdn_chunk_lds_bytes(T, DK, W), st,
                      static_cast<const uint16_t*>(x), conv_w, static_cast<const uint16_t*>(conv_state),
-                     static_cast<const uint16_t*>(v), beta, g, S, static_cast<uint16_t*>(o), parent, T, H, W);
+                     static_cast<const uint16_t*>(v), beta, g, S, static_cast<uint16_t*>(o), parent, T, H, W, so);
+}
+
+template <int DK, bool STORE>
+static void launch_chunk_w(const void* x, const float* conv_w, const void* conv_state, const void* v,
+                           const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
+                           int T, int H, int W, const ChunkStoreOut& so, hipStream_t st) {
+  if (W == 4)
+    launch_chunk<DK, 4, STORE>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);
+  else
+    launch_chunk<DK, 8, STORE>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);
+}
+
+static bool chunk_shape_ok(int act_dt, int T, int W, int dk) {
+  return act_dt == DDT_BF16 && T >= 1 && T <= kChunkMaxT && W >= 1 && W <= kChunkMaxW &&
+         (dk == 32 || dk == 64 || dk == 128);
 }
 
 hipError_t launch_gdn_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
                             const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
                             int T, int H, int dk, int W, int act_dt, hipStream_t st) {
   // bf16 activations only (fp32 ones keep the node-by-node walk); T <= 65, W <= 8
-  if (act_dt != DDT_BF16 || T < 1 || T > kChunkMaxT || W < 1 || W > kChunkMaxW) return hipErrorInvalidValue;
-#define DDT_CHUNK(DKV)                                                                                       \
-  (W == 4 ? launch_chunk<DKV, 4>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, st)            \
-          : launch_chunk<DKV, 8>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, st))
-  if (dk == 32) DDT_CHUNK(32);
-  else if (dk == 64) DDT_CHUNK(64);
-  else if (dk == 128) DDT_CHUNK(128);
-  else return hipErrorInvalidValue;
-#undef DDT_CHUNK
+  if (!chunk_shape_ok(act_dt, T, W, dk)) return hipErrorInvalidValue;
+  const ChunkStoreOut none = {};
+  if (dk == 32) launch_chunk_w<32, false>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, none, st);
+  else if (dk == 64) launch_chunk_w<64, false>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, none, st);
+  else launch_chunk_w<128, false>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, none, st);
+  return hipGetLastError();
+}
+
+constexpr int kStatesRPT = 4;  // 16 KB of states per block
+
+size_t gdn_chunk_store_bytes(int n, int T, int H) {
+  const size_t tri = (size_t)rec_base(T);
+  return ((size_t)n * tri * 4 + 255) / 256 * 256 + ((size_t)n * H * tri * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                                   const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
+                                   void* o, const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt,
+                                   float* kbuf, float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st) {
+  if (!chunk_shape_ok(act_dt, T, W, dk) || W < 2) return hipErrorInvalidValue;
+  ChunkStoreOut so;
+  so.conv_scratch = static_cast<uint16_t*>(conv_scratch);
+  so.k = kbuf;
+  so.w = wbuf;
+  so.gam = gam;
+  so.dep = dep;
+  so.rows = static_cast<int32_t*>(tables);
+  so.rho = reinterpret_cast<float*>(static_cast<uint8_t*>(tables) + ((size_t)n * rec_base(T) * 4 + 255) / 256 * 256);
+#define DDT_STORED(DKV)                                                                                           \
+  do {                                                                                                            \
+    constexpr int RPT = kStatesRPT * 1024 <= DKV * DKV ? kStatesRPT : DKV * DKV / 1024;                           \
+    launch_chunk_w<DKV, true>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);               \
+    hipLaunchKernelGGL((gdn_states_kernel<DKV, RPT>), dim3((unsigned)((size_t)n * T * H * DKV * DKV / (1024 * RPT))), \
+                       dim3(256), 0, st, S, kbuf, wbuf, so.rows, so.rho, gam, dep, S_scratch, T, H);             \
+  } while (0)
+  if (dk == 32) DDT_STORED(32);
+  else if (dk == 64) DDT_STORED(64);
+  else DDT_STORED(128);
+#undef DDT_STORED
   return hipGetLastError();
 }
 

@@ -10,7 +10,10 @@
 //   q = y[q-channels of h] * dk^-1/2;  k = y[k-channels of h] / sqrt(|k|^2 + 1e-6)
 //   S_i = g S_p + beta (v - g S_p k) k^T;  o_i = S_i q = g (S_p q) + beta (v - g S_p k) (k.q)
 //
-// Two kernels:
+// Node states stored (S_scratch, conv_scratch), bf16 activations, T <= 65 and a depth
+// bound L <= 16: the chunk form of gdn_chunk.hip (its kernel also writes the conv
+// scratch and hands w, k and the path records over) and gdn_states_kernel, which writes
+// every state from them.  Otherwise (fp32 activations, deeper bounds), two kernels:
 //  gdn_conv   grid (n*T, heads/HG): a block per node and group of heads, dk/4 lanes per
 //             head; gathers the node's conv window along its parent chain, writes the
 //             conv scratch (exact copies), and leaves q (scaled), k (normalised) and k.q
@@ -406,17 +409,28 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(const float* __restrict_
   }
 }
 
+// Workspace: q|k [n][T][H][2*dk] fp32, k.q [n][T][H], the depth-first order [n][T]; in the
+// chunk form with stored states the same areas hold k and w, G_t and the depths, and the
+// record tables follow.
 size_t gdn_workspace(int n, int T, int H, int dk) {
   const size_t qk = (size_t)n * T * H * 2 * dk * sizeof(float);
   const size_t kq = (size_t)n * T * H * sizeof(float);
   const size_t ord = (size_t)n * T * sizeof(int32_t);
-  return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256 + (ord + 255) / 256 * 256;
+  return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256 + (ord + 255) / 256 * 256 + gdn_chunk_store_bytes(n, T, H);
 }
+
+// Depth bound up to which node states are formed from the chunk form.  The states
+// kernel's work grows with each node's path length: on bushy trees (mean path about 5
+// rows at L 15) it writes the states in 0.22 ms per call against the walk's 0.24, while
+// trees whose nodes crowd the bound (a chain, a deep thin tree) cost it 0.25 ms at L 16
+// and 0.29 at L 24.  Any tree is computed correctly either way: the bound only picks the
+// path.
+constexpr int kChunkStoreMaxL = 16;
 
 template <typename A, int DK>
 static hipError_t launch_gdn(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch, const void* v,
                        const float* beta, const float* g, const float* S, float* S_scratch, void* o,
-                       const int32_t* parent, int n, int T, int H, int C, int W, void* ws, hipStream_t st) {
+                       const int32_t* parent, int n, int T, int L, int H, int C, int W, void* ws, hipStream_t st) {
   constexpr int CPT = DK >= 64 ? 8 : 4;   // columns per thread
   constexpr int R = 256 / (DK / CPT);     // state rows per block
   const size_t qk_b = ((size_t)n * T * H * 2 * DK * sizeof(float) + 255) / 256 * 256;
@@ -429,6 +443,15 @@ static hipError_t launch_gdn(const void* x, const float* conv_w, const void* con
     // chunk form on the matrix cores (the fp32 configuration keeps the walk, whose
     // rounding stays within its 1e-5 bound)
     return launch_gdn_chunk(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, DK, W, DDT_BF16, st);
+  }
+  if (S_scratch != nullptr && conv_scratch != nullptr && sizeof(A) == 2 && T <= 65 && W <= 8 &&
+      L <= kChunkStoreMaxL) {
+    // stored states, bf16 activations: the chunk form gives every node's w, then each
+    // state is written by short-lived blocks (k and w in the q|k area, G_t in the k.q
+    // area, depths in the order area)
+    return launch_gdn_chunk_stored(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H,
+                                   DK, W, DDT_BF16, qk, qk + (size_t)n * T * H * DK, kq, ord,
+                                   static_cast<uint8_t*>(ws) + qk_b + kq_b + ((size_t)n * T * 4 + 255) / 256 * 256, st);
   }
   const dim3 cgrid(n * T, (H + 256 / (DK / 4) - 1) / (256 / (DK / 4)));
   if (W == 4)
@@ -452,10 +475,10 @@ static hipError_t launch_gdn(const void* x, const float* conv_w, const void* con
 
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
                                 const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
-                                void* o, const int32_t* parent, int n, int T, int H, int dk, int C, int W,
+                                void* o, const int32_t* parent, int n, int T, int L, int H, int dk, int C, int W,
                                 int act_dt, void* ws, hipStream_t st) {
 #define DDT_GDN(TY, DKV) \
-  return launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H, C, W, ws, st)
+  return launch_gdn<TY, DKV>(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, L, H, C, W, ws, st)
   if (act_dt == DDT_BF16) {
     if (dk == 32) DDT_GDN(uint16_t, 32);
     if (dk == 64) DDT_GDN(uint16_t, 64);

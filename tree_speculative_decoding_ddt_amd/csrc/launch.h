@@ -92,13 +92,20 @@ size_t gdn_workspace(int n, int T, int H, int dk);
 hipError_t launch_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state,
                                 void* conv_scratch, const void* v, const float* beta,
                                 const float* g, const float* S, float* S_scratch, void* o,
-                                const int32_t* parent, int n, int T, int H, int dk, int C,
+                                const int32_t* parent, int n, int T, int L, int H, int dk, int C,
                                 int W, int act_dt, void* ws, hipStream_t st);
 
-// ---- GDN tree step without stored node states (short conv included), chunk form
+// ---- GDN tree step in chunk form (short conv included): without stored node states, or
+// with them (then gdn_states_kernel writes them from what the chunk kernel leaves in
+// kbuf / wbuf / gam / dep and the record tables of gdn_chunk_store_bytes())
 hipError_t launch_gdn_chunk(const void* x, const float* conv_w, const void* conv_state, const void* v,
                             const float* beta, const float* g, const float* S, void* o, const int32_t* parent, int n,
                             int T, int H, int dk, int W, int act_dt, hipStream_t st);
+size_t gdn_chunk_store_bytes(int n, int T, int H);
+hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                                   const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
+                                   void* o, const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt,
+                                   float* kbuf, float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st);
 
 // ---- GDN replay on commit
 hipError_t launch_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,
