@@ -71,17 +71,8 @@ __device__ __forceinline__ cf32x4 mfma3(const cbf16x8& ah, const cbf16x8& al, co
 // compiler from moving memory accesses across it; loads issued before it are still waited
 // for where their results are used.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// 8 consecutive activations as fp32
+// 8 consecutive fp32 values
 template <typename A> __device__ __forceinline__ void load8(const A* p, float (&x)[8]);
-template <> __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(u[i] << 16);
-    x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
 template <> __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -269,25 +260,47 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       const float ga = gg[a];
       if (!(p >= 0 && p < a)) {
         Gam[t] = prod * ga;
-        if (STORE) so.gam[((size_t)s * Tn + t) * H + h] = prod * ga;
         break;
       }
       prod *= ga;
       a = p;
       rec[rb + k] = make_float4(__int_as_float(a), prod, 0.f, 0.f);
-      if (STORE) {
-        so.rho[((size_t)s * H + h) * rec_base(Tn) + rb + k] = prod;
-        if (h == 0) so.rows[(size_t)s * rec_base(Tn) + rb + k] = a;
-      }
       ++k;
       if (k < W) win[t * kChunkMaxW + k] = a;
     }
     for (int b = k + 1; b < W; ++b) win[t * kChunkMaxW + b] = Tn + W - 1 - (b - k);
     dep[t] = k;
-    if (STORE && h == 0) so.dep[(size_t)s * Tn + t] = k;
     atomicAdd(&cnt[k], 1);
   }
   __syncthreads();
+  if (STORE) {
+    // S0 and v (issued before the walk) are waited for here, before the exports: loads and
+    // stores retire in order, so a wait for them issued after the stores would also wait
+    // those out.  From here on the kernel loads nothing from global memory.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // G_t and the depth; every record slot of t (t slots): its (k+1)-th ancestor and r_tj,
+    // or past dep[t] a valid row (t) with ratio 0, so that the states kernel may read t's
+    // first slots before its depth
+    if (tid < Tn) {
+      so.gam[((size_t)s * Tn + tid) * H + h] = Gam[tid];
+      if (h == 0) so.dep[(size_t)s * Tn + tid] = dep[tid];
+    }
+    const int TRI = rec_base(Tn);
+    constexpr int kRecIt = (kChunkMaxT * (kChunkMaxT - 1) / 2 + 255) / 256;
+#pragma unroll
+    for (int i = 0; i < kRecIt; ++i) {
+      const int idx = min(tid + 256 * i, max(TRI - 1, 0));  // slot rec_base(t) + k
+      int t = (int)((1.f + sqrtf(1.f + 8.f * (float)idx)) * 0.5f);
+      t -= rec_base(t) > idx;
+      t += rec_base(t + 1) <= idx;
+      const int k = idx - rec_base(t), dt = dep[t];
+      const float4 r = rec[rec_base(t) + min(k, max(dt - 1, 0))];
+      if (tid + 256 * i < TRI) {
+        so.rho[((size_t)s * H + h) * TRI + idx] = k < dt ? r.y : 0.f;
+        if (h == 0) so.rows[(size_t)s * TRI + idx] = k < dt ? __float_as_int(r.x) : t;
+      }
+    }
+  }
   if (wave == 0) {  // depth starts: an exclusive scan of the histogram over 64 lanes (+ depth 64)
     int c = lane < Tn ? cnt[lane] : 0;
 #pragma unroll
@@ -319,8 +332,18 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       for (int c = 0; c < WT; ++c) {  // tap c multiplies the row W-1-c back
         const int b = WT == 4 ? 3 - c : max(W - 1 - c, 0);
         const int r = win[tt[u] * kChunkMaxW + b];
+        const uint4 raw = *reinterpret_cast<const uint4*>(stage + (size_t)r * (2 * DK) + s0);
+        // the conv scratch of the node: its window's newest W-1 rows, tap c (1 <= c <= W-1,
+        // back W-1-c) in slot c-1; a clamped duplicate node writes the same bytes
+        if (STORE && c >= 1 && (WT == 4 || c <= W - 1))
+          *reinterpret_cast<uint4*>(so.conv_scratch + (((size_t)s * Tn + tt[u]) * (W - 1) + (c - 1)) * C + c0) = raw;
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
         float xv[8];
-        load8<uint16_t>(stage + (size_t)r * (2 * DK) + s0, xv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[2 * i] = __uint_as_float(rw[i] << 16);
+          xv[2 * i + 1] = __uint_as_float(rw[i] & 0xffff0000u);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[u][e] += cw[e][c] * xv[e];
       }
@@ -354,26 +377,6 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       const int base = (half ? 0 : 2) * RW * RSB + tt[u] * RSB + cg * 16;  // K hi/lo first, then Q hi/lo
       *reinterpret_cast<cbf16x8*>(lds + base) = hi;
       *reinterpret_cast<cbf16x8*>(lds + base + RW * RSB) = lo;
-    }
-  }
-  if (STORE) {
-    // record slots of t past its dep[t] ancestors (t has t slots): a valid row (t) with
-    // ratio 0, so that the states kernel may read t's first slots before its depth
-    for (int t = 1; t < Tn; ++t)
-      for (int k = dep[t] + tid; k < t; k += 256) {
-        so.rho[((size_t)s * H + h) * rec_base(Tn) + rec_base(t) + k] = 0.f;
-        if (h == 0) so.rows[(size_t)s * rec_base(Tn) + rec_base(t) + k] = t;
-      }
-    // conv scratch of every node: its window's newest W-1 rows (back b in slot W-2-b),
-    // the head's q and k channels, copied from the stage
-    const int Wc = WT == 4 ? 4 : W;  // a constant divisor where the width is fixed
-    const int per_node = (Wc - 1) * ROW8;
-    for (int idx = tid; idx < Tn * per_node; idx += 256) {
-      const int t = idx / per_node, rem = idx % per_node, slot = rem / ROW8, ch = rem % ROW8;
-      const int r = win[t * kChunkMaxW + (Wc - 2 - slot)];
-      const int chan = ch < ROW8 / 2 ? h * DK + 8 * ch : H * DK + h * DK + 8 * (ch - ROW8 / 2);
-      *reinterpret_cast<uint4*>(so.conv_scratch + (((size_t)s * Tn + t) * (Wc - 1) + slot) * C + chan) =
-          *reinterpret_cast<const uint4*>(stage + (size_t)r * (2 * DK) + 8 * ch);
     }
   }
   lds_barrier();
@@ -562,7 +565,6 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
         if (dp[i] != e) continue;
         const int t = tt[i];
         *reinterpret_cast<float4*>(&Wm[t * WS + c]) = aw[i];
-        if (STORE) *reinterpret_cast<float4*>(so.w + (((size_t)s * Tn + t) * H + h) * DV + c) = aw[i];
         uint2 u;
         u.x = (uint32_t)f32_to_bf16(ao[i].x + md[i] * aw[i].x) | ((uint32_t)f32_to_bf16(ao[i].y + md[i] * aw[i].y) << 16);
         u.y = (uint32_t)f32_to_bf16(ao[i].z + md[i] * aw[i].z) | ((uint32_t)f32_to_bf16(ao[i].w + md[i] * aw[i].w) << 16);
@@ -602,6 +604,14 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
         }
       }
       lo = hi;
+    }
+    if (STORE) {
+      // w of every node, the wave's own columns (its own LDS writes: no barrier needed)
+      for (int idx = lane; idx < Tn * (CPW / 4); idx += 64) {
+        const int t = idx / (CPW / 4), cc = CPW * wave + 4 * (idx % (CPW / 4));
+        *reinterpret_cast<float4*>(so.w + (((size_t)s * Tn + t) * H + h) * DV + cc) =
+            *reinterpret_cast<const float4*>(&Wm[t * WS + cc]);
+      }
     }
   }
 }
