@@ -316,6 +316,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     else if (it + 1 < n_all) DDT_WAIT_VMCNT(2 * RPW);
     else DDT_WAIT_VMCNT(0);
     barrier_nofence();
+  };
+  // the copies of tile it+3 (into the stage of tile it-1, free since the barrier) are
+  // issued after tile it's first products, whose matrix-core time covers their scalar
+  // address work
+  auto refill = [&](int it) {
     if (it + 3 < n_all) issue(it + 3);
   };
 
@@ -488,6 +493,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       const bool masked = tree || kb + NK > kend;
       f32x4 Sacc[NT][2];
       s_phase(NAc, 0, Sacc);
+      refill(0);
       if (first) {
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
@@ -507,6 +513,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       sync_tile(it);
       f32x4 Sacc[NT][2];
       s_phase(NAc, it % NST, Sacc);
+      refill(it);
       softmax(NAc, TRc, Sacc, false, false, 0, 0, Pp);
       pv_phase(NAc, it % NST);
     }
@@ -517,6 +524,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
       const int kend = tree ? Tn : k_end;
       f32x4 Sacc[NT][2];
       s_phase(NAc, it % NST, Sacc);
+      refill(it);
       softmax(NAc, TRc, Sacc, true, tree, kb, kend, Pp);
       pv_phase(NAc, it % NST);
     }
