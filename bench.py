@@ -35,8 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix
-KERNEL_SOURCES = {
-    "gdn_tree_step": "gdn_tree.hip",
+KERNEL_SOURCES = {  # the sources whose kernels one call runs
+    "gdn_tree_step": ("gdn_tree.hip", "gdn_chunk.hip"),
     "tree_attn": "tree_attn.hip",
     "build_tree": "build_tree.hip",
     "tree_accept": "accept.hip",
@@ -75,8 +75,10 @@ def code_hash(text):
 
 
 def src_hash(name):
-    path = os.path.join(ROOT, "tree_speculative_decoding_ddt_amd", "csrc", KERNEL_SOURCES[name])
-    return code_hash(open(path).read())
+    files = KERNEL_SOURCES[name]
+    files = (files,) if isinstance(files, str) else files
+    return code_hash("\n".join(open(os.path.join(ROOT, "tree_speculative_decoding_ddt_amd", "csrc", f)).read()
+                               for f in files))
 
 
 def algorithmic(cfg, prefix_now, rows_per_round):

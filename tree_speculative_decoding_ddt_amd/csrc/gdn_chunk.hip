@@ -65,12 +65,6 @@ __device__ __forceinline__ cf32x4 mfma3(const cbf16x8& ah, const cbf16x8& al, co
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
 }
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and scalar) operations,
-// not for its global stores, which a __syncthreads() fence would wait out (the exports of
-// the stored-state variant are still in flight there).  The memory clobber keeps the
-// compiler from moving memory accesses across it; loads issued before it are still waited
-// for where their results are used.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // 8 consecutive fp32 values
 template <typename A> __device__ __forceinline__ void load8(const A* p, float (&x)[8]);
 template <> __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
@@ -274,10 +268,6 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   }
   __syncthreads();
   if (STORE) {
-    // S0 and v (issued before the walk) are waited for here, before the exports: loads and
-    // stores retire in order, so a wait for them issued after the stores would also wait
-    // those out.  From here on the kernel loads nothing from global memory.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     // G_t and the depth; every record slot of t (t slots): its (k+1)-th ancestor and r_tj,
     // or past dep[t] a valid row (t) with ratio 0, so that the states kernel may read t's
     // first slots before its depth
@@ -379,9 +369,9 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       *reinterpret_cast<cbf16x8*>(lds + base + RW * RSB) = lo;
     }
   }
-  lds_barrier();
+  __syncthreads();
   if (tid < Tn) cnt[tid] = 0;  // the fill counters (every read of the histogram is done)
-  lds_barrier();
+  __syncthreads();
   if (tid < Tn) ord[lstart[dep[tid]] + atomicAdd(&cnt[dep[tid]], 1)] = tid;
 
   // ---- P1: S0 [K|Q] as D[r][t] (lane: node column 16*ti + l16, rows 16*rt + 4*q4 + e)
@@ -448,7 +438,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       gk[k][1] = mfma3(qh, ql, jh, jl, gk[k][1]);
     }
   }
-  lds_barrier();  // every wave is done with q/k: their area now takes w and the o base
+  __syncthreads();  // every wave is done with q/k: their area now takes w and the o base
 
   // ---- P2: right-hand sides beta_t (v_t - G_t S0 k_t), the o base G_t S0 q_t, M_tt, and
   // the records' coefficients
@@ -526,7 +516,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       }
     }
   }
-  lds_barrier();
+  __syncthreads();
 
   // ---- P3: the solve, depth by depth, without barriers: wave `wave` owns columns
   // [CPW*wave, CPW*(wave+1)), a lane 4 of them for NS nodes (slots), NGP nodes side by
