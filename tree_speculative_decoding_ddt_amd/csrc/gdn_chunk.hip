@@ -20,7 +20,7 @@
 // node state is formed here; with states stored (STORE) the kernel also writes the conv
 // scratch and leaves k, w and the path records for gdn_states_kernel.
 //
-// One block per (sequence, head), 4 waves.  Every global load of a phase is issued
+// One block per (sequence, head), 8 waves.  Every global load of a phase is issued
 // before any of its results is used (unconditional loads at clamped addresses), so each
 // phase waits for memory once:
 //   P0  the head's x channels (q and k part) of every node and the committed conv rows
@@ -36,8 +36,8 @@
 //       dropped lo*lo term is 2^-18 relative)
 //   P2  right-hand sides beta_t (v_t - G_t S0 k_t), the base G_t S0 q_t, and per node and
 //       ancestor depth the record (ancestor row, solve coefficient, output coefficient)
-//   P3  the solve, depth by depth: a wave owns dv/4 columns (so it needs no barrier: the
-//       w it reads are its own), 512/dv nodes of one depth at a time, 2 columns per
+//   P3  the solve, depth by depth: a wave owns dv/8 columns (so it needs no barrier: the
+//       w it reads are its own), 2048/dv nodes of one depth at a time, 4 columns per
 //       lane; a node at depth d has exactly d ancestors, one per shallower depth.
 #include <math.h>
 
@@ -74,6 +74,8 @@ template <> __device__ __forceinline__ void load8<float>(const float* p, float (
 }
 }  // namespace
 
+constexpr int kChunkThreads = 512;                // threads per block (one per (sequence, head))
+constexpr int kChunkWaves = kChunkThreads / 64;
 constexpr int kChunkMaxTT = 5;   // 16-row tiles of nodes
 constexpr int kChunkMaxW = 8;    // conv width
 constexpr int kChunkMaxT = 65;   // nodes (budget <= 64 plus the root)
@@ -133,19 +135,20 @@ __host__ __device__ inline ChunkLayout chunk_layout(int T, int dk, int W) {
 // STORE: also hand the per-node states to gdn_states_kernel (ChunkStoreOut) and write
 // the conv scratch.
 template <int DK, int WT, bool STORE>
-__global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restrict__ x, const float* __restrict__ conv_w,
+__global__ void __launch_bounds__(kChunkThreads) gdn_chunk_kernel(const uint16_t* __restrict__ x, const float* __restrict__ conv_w,
                                                         const uint16_t* __restrict__ conv_state,
                                                         const uint16_t* __restrict__ v, const float* __restrict__ beta,
                                                         const float* __restrict__ g, const float* __restrict__ S,
                                                         uint16_t* __restrict__ o, const int32_t* __restrict__ parent,
                                                         int Tn, int H, int W, ChunkStoreOut so) {
   constexpr int DV = DK, RSB = 2 * DK + 16, NCS = DK / 32, NRT = DV / 16;
-  constexpr int RTW = (NRT + 3) / 4;   // 16-row tiles of S0 per wave
+  constexpr int NTH = kChunkThreads, NWV = kChunkWaves;
+  constexpr int RTW = (NRT + NWV - 1) / NWV;  // 16-row tiles of S0 per wave
   constexpr int NG = DK / 8;           // conv: lanes per (node, q or k part), 8 channels each
-  constexpr int NPR = 256 / (2 * NG);  // conv: nodes per pass of the block
+  constexpr int NPR = NTH / (2 * NG);  // conv: nodes per pass of the block
   constexpr int ROW8 = 2 * DK / 8;     // 16-byte chunks of a staged row
-  constexpr int kStageIt = ((kChunkMaxT + kChunkMaxW - 1) * ROW8 + 255) / 256;
-  constexpr int CPW = DV / 4;          // solve: columns a wave owns
+  constexpr int kStageIt = ((kChunkMaxT + kChunkMaxW - 1) * ROW8 + NTH - 1) / NTH;
+  constexpr int CPW = DV / NWV;        // solve: columns a wave owns
   constexpr int LPN = CPW / 4;         // solve: lanes per node, 4 columns each
   constexpr int NGP = 64 / LPN;        // solve: nodes a wave holds side by side
   constexpr int NS = (kChunkMaxT + NGP - 1) / NGP;  // solve: node slots per lane
@@ -178,19 +181,19 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   const int tn = min(tid, Tn - 1);
   const int pr = parent[(size_t)s * Tn + tn];
   const float gr = g[((size_t)s * Tn + tn) * H + h], br = beta[((size_t)s * Tn + tn) * H + h];
-  // the stage, 16-byte chunk idx = 256*k + tid: a wave fills 1 KB at a time; chunks past
+  // the stage, 16-byte chunk idx = NTH*k + tid: a wave fills 1 KB at a time; chunks past
   // the last repeat it into the stage's padding
   const int nst = (Tn + W - 1) * ROW8;
 #pragma unroll
   for (int k = 0; k < kStageIt; ++k) {
-    if (256 * k >= nst) break;
-    const int idx = min(tid + 256 * k, nst - 1);
+    if (NTH * k >= nst) break;
+    const int idx = min(tid + NTH * k, nst - 1);
     const int row = idx / ROW8, ch = idx % ROW8;
     const int chan = ch < ROW8 / 2 ? h * DK + 8 * ch : H * DK + h * DK + 8 * (ch - ROW8 / 2);
     const uint16_t* src = row < Tn ? x + ((size_t)s * Tn + row) * C + chan
                                    : conv_state + ((size_t)s * (W - 1) + (row - Tn)) * C + chan;
     __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                              reinterpret_cast<uintptr_t>(stage + (size_t)(256 * k + 64 * wave) * 8)),
+                                              reinterpret_cast<uintptr_t>(stage + (size_t)(NTH * k + 64 * wave) * 8)),
                                      16, 0, 0);
   }
   // this thread's conv channels: 8 of the head's q (half 0) or k (half 1) channels
@@ -227,7 +230,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   float sop[RTW][NCS][8];
 #pragma unroll
   for (int w = 0; w < RTW; ++w) {
-    const int rt = min(wave + 4 * w, NRT - 1);
+    const int rt = min(wave + NWV * w, NRT - 1);
 #pragma unroll
     for (int cs = 0; cs < NCS; ++cs) load8<float>(S0 + (size_t)(16 * rt + l16) * DK + 32 * cs + 8 * q4, sop[w][cs]);
   }
@@ -235,7 +238,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   uint2 vv[RTW][kChunkMaxTT];
 #pragma unroll
   for (int w = 0; w < RTW; ++w) {
-    const int rt = min(wave + 4 * w, NRT - 1);
+    const int rt = min(wave + NWV * w, NRT - 1);
 #pragma unroll
     for (int ti = 0; ti < kChunkMaxTT; ++ti) {
       const int t = min(16 * ti + l16, Tn - 1);
@@ -276,16 +279,16 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       if (h == 0) so.dep[(size_t)s * Tn + tid] = dep[tid];
     }
     const int TRI = rec_base(Tn);
-    constexpr int kRecIt = (kChunkMaxT * (kChunkMaxT - 1) / 2 + 255) / 256;
+    constexpr int kRecIt = (kChunkMaxT * (kChunkMaxT - 1) / 2 + NTH - 1) / NTH;
 #pragma unroll
     for (int i = 0; i < kRecIt; ++i) {
-      const int idx = min(tid + 256 * i, max(TRI - 1, 0));  // slot rec_base(t) + k
+      const int idx = min(tid + NTH * i, max(TRI - 1, 0));  // slot rec_base(t) + k
       int t = (int)((1.f + sqrtf(1.f + 8.f * (float)idx)) * 0.5f);
       t -= rec_base(t) > idx;
       t += rec_base(t + 1) <= idx;
       const int k = idx - rec_base(t), dt = dep[t];
       const float4 r = rec[rec_base(t) + min(k, max(dt - 1, 0))];
-      if (tid + 256 * i < TRI) {
+      if (tid + NTH * i < TRI) {
         so.rho[((size_t)s * H + h) * TRI + idx] = k < dt ? r.y : 0.f;
         if (h == 0) so.rows[(size_t)s * TRI + idx] = k < dt ? __float_as_int(r.x) : t;
       }
@@ -403,7 +406,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
       const cbf16x8 ql = *reinterpret_cast<const cbf16x8*>(Qlo + ro);
 #pragma unroll
       for (int w = 0; w < RTW; ++w) {
-        if (wave + 4 * w >= NRT) continue;
+        if (wave + NWV * w >= NRT) continue;
         acc[w][ti][0] = mfma3(sh[w][cs], sl[w][cs], kh, kl, acc[w][ti][0]);
         acc[w][ti][1] = mfma3(sh[w][cs], sl[w][cs], qh, ql, acc[w][ti][1]);
       }
@@ -411,14 +414,14 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   }
   // Gram blocks (ti, tj), tj <= ti, dealt to the waves: K_t . K_j and Q_t . K_j as
   // D[t][j] (lane: j = 16*tj + l16, t = 16*ti + 4*q4 + e)
-  constexpr int kMaxPairs = (kChunkMaxTT * (kChunkMaxTT + 1) / 2 + 3) / 4;  // per wave
+  constexpr int kMaxPairs = (kChunkMaxTT * (kChunkMaxTT + 1) / 2 + NWV - 1) / NWV;  // per wave
   const int NP = NTT * (NTT + 1) / 2;
   cf32x4 gk[kMaxPairs][2];
   int pti[kMaxPairs], ptj[kMaxPairs];
 #pragma unroll
   for (int k = 0; k < kMaxPairs; ++k) {
     gk[k][0] = gk[k][1] = cf32x4{0.f, 0.f, 0.f, 0.f};
-    const int p = wave + 4 * k;
+    const int p = wave + NWV * k;
     int ti = 0;
     while ((ti + 1) * (ti + 2) / 2 <= p) ++ti;
     pti[k] = ti;
@@ -481,7 +484,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
     const int t = 16 * ti + l16;
 #pragma unroll
     for (int w = 0; w < RTW; ++w) {
-      const int rt = wave + 4 * w;
+      const int rt = wave + NWV * w;
       if (rt >= NRT) continue;
       const uint2 q = vv[w][ti];
       const float v4[4] = {__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
@@ -503,7 +506,7 @@ __global__ void __launch_bounds__(256) gdn_chunk_kernel(const uint16_t* __restri
   }
 #pragma unroll
   for (int k = 0; k < kMaxPairs; ++k) {
-    if (wave + 4 * k >= NP) continue;
+    if (wave + NWV * k >= NP) continue;
     const int j = 16 * ptj[k] + l16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -721,7 +724,7 @@ static void launch_chunk(const void* x, const float* conv_w, const void* conv_st
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)gdn_chunk_lds_bytes(kChunkMaxT, DK, kChunkMaxW)) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL(kern, dim3(n * H), dim3(256), gdn_chunk_lds_bytes(T, DK, W), st,
+  hipLaunchKernelGGL(kern, dim3(n * H), dim3(kChunkThreads), gdn_chunk_lds_bytes(T, DK, W), st,
                      static_cast<const uint16_t*>(x), conv_w, static_cast<const uint16_t*>(conv_state),
                      static_cast<const uint16_t*>(v), beta, g, S, static_cast<uint16_t*>(o), parent, T, H, W, so);
 }
