@@ -145,7 +145,10 @@ __global__ void __launch_bounds__(kChunkThreads) gdn_chunk_kernel(const uint16_t
   constexpr int NTH = kChunkThreads, NWV = kChunkWaves;
   constexpr int RTW = (NRT + NWV - 1) / NWV;  // 16-row tiles of S0 per wave
   constexpr int NG = DK / 8;           // conv: lanes per (node, q or k part), 8 channels each
-  constexpr int NPR = NTH / (2 * NG);  // conv: nodes per pass of the block
+  constexpr int NPR = NTH / (2 * NG);  // conv: node slots of the block
+  // conv: nodes per thread and pass: one pass for any T <= 65 at the fixed width 4; two for
+  // the generic widths, whose 8 taps of weights take the registers
+  constexpr int NU = WT == 4 ? (kChunkMaxT + NPR - 1) / NPR : ((kChunkMaxT + NPR - 1) / NPR + 1) / 2;
   constexpr int ROW8 = 2 * DK / 8;     // 16-byte chunks of a staged row
   constexpr int kStageIt = ((kChunkMaxT + kChunkMaxW - 1) * ROW8 + NTH - 1) / NTH;
   constexpr int CPW = DV / NWV;        // solve: columns a wave owns
@@ -311,13 +314,13 @@ __global__ void __launch_bounds__(kChunkThreads) gdn_chunk_kernel(const uint16_t
       *maxdep = (Tn > 64 && cnt[64] > 0) ? 64 : 63 - __builtin_clzll(nz);
     }
   }
-  // the short conv of the head's q and k channels from the stage, two nodes per thread
-  // and pass; SiLU; k L2-normalised, q scaled; stored as bf16 high and low parts
-  for (int t0 = 0; t0 < Tn; t0 += 2 * NPR) {
-    float y[2][8];
-    int tt[2];
+  // the short conv of the head's q and k channels from the stage, NU nodes per thread and
+  // pass; SiLU; k L2-normalised, q scaled; stored as bf16 high and low parts
+  for (int t0 = 0; t0 < Tn; t0 += NU * NPR) {
+    float y[NU][8];
+    int tt[NU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       tt[u] = min(t0 + tsub + u * NPR, Tn - 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[u][e] = 0.f;
@@ -341,23 +344,17 @@ __global__ void __launch_bounds__(kChunkThreads) gdn_chunk_kernel(const uint16_t
         for (int e = 0; e < 8; ++e) y[u][e] += cw[e][c] * xv[e];
       }
     }
-    float ss[2] = {0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u) {
+      float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         y[u][e] = y[u][e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[u][e]));
-        ss[u] += y[u][e] * y[u][e];
+        ss += y[u][e] * y[u][e];
       }
-    // k: L2 norm over the head's dk channels (the NG lanes of this node and half)
-#pragma unroll
-    for (int off = NG / 2; off > 0; off >>= 1) {
-      ss[0] += __shfl_xor(ss[0], off, 64);
-      ss[1] += __shfl_xor(ss[1], off, 64);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float sc = half ? 1.f / sqrtf(ss[u] + 1e-6f) : rsqrtf((float)DK);
+      // k: L2 norm over the head's dk channels (the NG lanes of this node and half; DPP)
+      ss = group_sum<NG>(ss);
+      const float sc = half ? 1.f / sqrtf(ss + 1e-6f) : rsqrtf((float)DK);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[u][e] *= sc;
       if (STORE && half) {  // the normalised k in fp32 (a clamped duplicate node writes the same values)
