@@ -116,12 +116,13 @@ def test_star_and_root_only():
 
 
 def test_chunk_form_states():
-    # bf16 activations with the depth bound at most 24 form the node states from the chunk
+    # bf16 activations with the depth bound at most 16 form the node states from the chunk
     # form (w and k of each path node); a tree deeper than the bound given still comes out
-    # right (the bound only picks the path)
-    say("gdn stored states, chunk form: chain 64 deep at bound 15, deep trees dk 64, root alone, W 5")
+    # right (the bound only picks the path).  The deep trees at bound 16 have paths of up
+    # to 17 rows (three batches of the states kernel), the chain 65 (nine).
+    say("gdn stored states, chunk form: chain 64 deep at bound 15, deep trees dk 64 at bound 16, root alone, W 5")
     run_case(50, 2, 64, 15, 2, 128, 4, "bf16", kind="chain")
-    run_case(51, 3, 64, 20, 2, 64, 4, "bf16", kind="deep")
+    run_case(51, 3, 64, 16, 2, 64, 4, "bf16", kind="deep")
     run_case(52, 2, 0, 1, 2, 128, 4, "bf16")
     run_case(53, 2, 40, 12, 3, 64, 5, "bf16")
 

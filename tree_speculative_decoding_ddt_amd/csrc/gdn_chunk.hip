@@ -23,14 +23,16 @@
 // One block per (sequence, head), 8 waves.  Every global load of a phase is issued
 // before any of its results is used (unconditional loads at clamped addresses), so each
 // phase waits for memory once:
-//   P0  the head's x channels (q and k part) of every node and the committed conv rows
-//       staged in LDS, node scalars, each node's conv window (the node, its parent chain,
-//       then the committed conv rows), depth and G_t; the depth order by a
-//       histogram; the short conv and SiLU from LDS, k L2-normalised and q scaled, kept
-//       as bf16 high and low parts (x = hi + lo to 2^-17); then, the stage being dead,
-//       r_tj (products of g along the parent chain, so a zero g is exact too) and each
-//       node's ancestor at every depth.  The wave's S0 operands and v values are loaded
-//       into registers at the start, beside the stage.
+//   P0  the node scalars and, by LDS DMA, the stage (the head's x channels, q and k part,
+//       of every node, then the committed conv rows); after the first barrier the wave's
+//       S0 operands and v values are issued (they arrive during the walk).  One walk per
+//       node up its parent chain gives its conv window (the node, its ancestors, then the
+//       committed conv rows), its depth, G_t and its ancestor records (row, r_tj: products
+//       of g along the chain, so a zero g is exact too); the depth order by a histogram;
+//       the short conv and SiLU from the stage, k L2-normalised and q scaled, kept as
+//       bf16 high and low parts (x = hi + lo to 2^-17).  With STORE: G_t, the depths and
+//       the records are exported after the walk, the conv scratch and the fp32 k during
+//       the conv, and w after the solve.
 //   P1  S0 [K|Q] and the lower block triangle of K K^T and Q K^T with
 //       v_mfma_f32_16x16x32_bf16 as hi*hi + hi*lo + lo*hi (fp32 accumulation; the
 //       dropped lo*lo term is 2^-18 relative)
@@ -614,7 +616,7 @@ __global__ void __launch_bounds__(kChunkThreads) gdn_chunk_kernel(const uint16_t
 // over every state in flight.
 // The path is t itself (ratio 1) followed by its records, taken NB at a time: the block
 // stages each path node's k row and its ratio times the w of the block's rows in LDS
-// (one coalesced pass: 16 threads per path node), then a thread (4 columns of RPT
+// (one coalesced pass: 256/NB threads per path node), then a thread (4 columns of RPT
 // consecutive rows) adds r w k^T from LDS.  Every node's first record slots hold a valid
 // row (ratio 0 past its depth), so the first batch's rows and ratios are read with S0,
 // before the depth is known: a node less than NB deep waits on memory twice.
