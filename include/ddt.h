@@ -10,6 +10,8 @@
  *   ddt_tree_rope      the rotation step alone (for ddt_tree_attn_paged callers)
  *   ddt_tree_attn_paged the same over a paged committed cache (block table + page pool)
  *   ddt_gdn_tree_step  short conv + gated delta rule, every node from its parent
+ *   ddt_gdn_tree_step_deferred / ddt_gdn_tree_states  the same with the node states
+ *                      written by a second call (e.g. on another stream)
  *   ddt_tree_accept    greedy walk of the tree against the target's argmax tokens
  *   ddt_tree_accept_sampled  the walk over sampled target tokens (Gumbel-max draws)
  *   ddt_commit         copy only the accepted path into the committed buffers
@@ -231,6 +233,29 @@ int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state
                       const float* S, float* S_scratch, void* o, const int32_t* parent,
                       int n, int B, int L, int H, int dk, int dv, int C, int W, int act_dt,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* The same step with the node states written by a call of their own, so that a caller can
+ * run that write (the step's 93% of bytes; only the commit reads it) on another stream
+ * while the next layers run: [notes] "Why hybrid attention makes it hard" (each node's
+ * state goes to scratch; the commit reads the accepted one).
+ * ddt_gdn_tree_step_deferred: everything of ddt_gdn_tree_step (chunk form) except S_scratch:
+ *   o and conv_scratch are written, and each node's k, w, decay products and ancestor
+ *   records are left in ws.  Same arguments and limits as ddt_gdn_tree_step without
+ *   S_scratch; conv_scratch is required; bf16 activations only (DDT_ERR_UNSUPPORTED
+ *   otherwise); any depth (the state write costs more for deeper nodes).
+ * ddt_gdn_tree_states: writes S_scratch [n][T][H][dv][dk] (f32) from the committed S and
+ *   the ws a ddt_gdn_tree_step_deferred call with the same n, B, H, dk left.  The caller
+ *   keeps that ws and S unchanged and orders this call after that one (same stream, or an
+ *   event); with several layers in flight each needs a ws of its own.
+ * Results are the same as ddt_gdn_tree_step's with L <= 16, bit for bit.
+ */
+int ddt_gdn_tree_step_deferred(const void* x, const float* conv_w, const void* conv_state,
+                               void* conv_scratch, const void* v, const float* beta, const float* g,
+                               const float* S, void* o, const int32_t* parent, int n, int B, int L,
+                               int H, int dk, int dv, int C, int W, int act_dt, void* ws,
+                               size_t ws_bytes, void* stream);
+int ddt_gdn_tree_states(const float* S, float* S_scratch, int n, int B, int H, int dk, int dv,
+                        const void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- tree walk
  * [arch]: after the verify pass, walk down from the root while the target's token

@@ -21,7 +21,7 @@ def declared():
 def test_header_symbols_exported():
     L = ddt.lib()
     names = declared()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for name in names:
         assert hasattr(L, name), name
     assert sorted(ddt.EXPORTS) == names
@@ -157,6 +157,27 @@ def test_gdn_validation():
     a = args()
     a[0] = None
     assert status("ddt_gdn_tree_step", *a) == ddt.DDT_ERR_ARG
+
+
+def test_gdn_deferred_validation():
+    def args(**k):
+        a = [P] * 10 + [1, 8, k.get("L", 4), k.get("H", 1), k.get("dk", 32), k.get("dv", 32), k.get("C", 64),
+                        k.get("W", 4), k.get("dt", ddt.DDT_BF16), P, k.get("wsb", 1 << 30), None]
+        return a
+    assert status("ddt_gdn_tree_step_deferred", *args(dt=ddt.DDT_F32)) == ddt.DDT_ERR_UNSUPPORTED  # bf16 only
+    assert status("ddt_gdn_tree_step_deferred", *args(C=63)) == ddt.DDT_ERR_ARG
+    assert status("ddt_gdn_tree_step_deferred", *args(dk=48, dv=48, C=96)) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_step_deferred", *args(L=64)) == ddt.DDT_ERR_ARG
+    assert status("ddt_gdn_tree_step_deferred", *args(wsb=64)) == ddt.DDT_ERR_WORKSPACE
+    a = args()
+    a[3] = None                                                       # conv scratch is required
+    assert status("ddt_gdn_tree_step_deferred", *a) == ddt.DDT_ERR_ARG
+    #     S  S_scratch n  B  H  dk  dv  ws ws_bytes stream
+    st = [P, P, 1, 8, 1, 32, 32, P, 1 << 30, None]
+    assert status("ddt_gdn_tree_states", *(st[:3] + [65] + st[4:])) == ddt.DDT_ERR_ARG       # B > 64
+    assert status("ddt_gdn_tree_states", *(st[:5] + [48, 48] + st[7:])) == ddt.DDT_ERR_UNSUPPORTED
+    assert status("ddt_gdn_tree_states", *(st[:8] + [64] + st[9:])) == ddt.DDT_ERR_WORKSPACE
+    assert status("ddt_gdn_tree_states", *([None] + st[1:])) == ddt.DDT_ERR_ARG
 
 
 def test_accept_and_commit_validation():

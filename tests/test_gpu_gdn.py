@@ -144,3 +144,28 @@ def test_chunk_form_matches_walk_states():
     assert_close(down(a["S_scratch"]), down(b["S_scratch"]), "f32", "states chunk form vs walk")
     assert_close(down(a["o"]), down(b["o"]), "bf16", "o chunk form vs walk")
     np.testing.assert_array_equal(down(a["conv_scratch"]), down(b["conv_scratch"]))
+
+
+def test_deferred_state_write_matches_the_call():
+    # ddt_gdn_tree_step_deferred + ddt_gdn_tree_states (the latter on a second stream after
+    # an event) leave exactly what one ddt_gdn_tree_step call (chunk form) leaves
+    say("gdn deferred state write on a second stream vs the single call")
+    rng = np.random.default_rng(55)
+    n, B, L, H, dk = 2, 64, 15, 4, 128
+    parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, 4)
+    dev = {k: up(x[k], "bf16" if k in ("x", "v", "conv_state") else "f32")[0] for k in x}
+    pt = up_int(parents)
+    args = (dev["x"], dev["conv_w"], dev["conv_state"], dev["v"], dev["beta"], dev["g"], dev["S"], pt)
+    ref = ddt.gdn_tree_step(*args, L)
+    ws = torch.empty(ddt.gdn_tree_step_workspace(n, B, H, dk), dtype=torch.uint8, device="cuda")
+    out = ddt.gdn_tree_step_deferred(*args, L, ws)
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record()
+    side.wait_event(ev)
+    ddt.gdn_tree_states(dev["S"], out["S_scratch"], ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for key in ("o", "conv_scratch", "S_scratch"):
+        assert torch.equal(out[key], ref[key]), key

@@ -317,3 +317,26 @@ def test_full_size_hybrid_round_sampled():
             r = int(acc_rows[s][int(acc_len[s])])
             assert torch.equal(g["S"][s], g["out"]["S_scratch"][s, r]), ("S", j, s)
             assert torch.equal(g["conv_state"][s], g["out"]["conv_scratch"][s, r]), ("conv", j, s)
+
+
+def test_overlapped_state_writes_match():
+    # the round with each layer's node-state write on a second stream (the default) leaves
+    # exactly what the round with every call on one stream leaves, over two rounds
+    say("step bf16: state writes overlapped on a second stream vs one stream")
+    kw = dict(n=2, V=151936, L=15, B=64, prefix=640, extra_cap=32, n_attn=1, n_gdn=3)
+    a = HybridVerifyStep(HybridConfig(overlap_states=True, **kw))
+    b = HybridVerifyStep(HybridConfig(overlap_states=False, **kw))
+    a.fill_random(seed=6)
+    b.fill_random(seed=6)
+    for r in range(2):
+        a()
+        b()
+        torch.cuda.synchronize()
+        for j, (ga, gb) in enumerate(zip(a.gdn, b.gdn)):
+            for key in ("o", "S_scratch", "conv_scratch"):
+                assert torch.equal(ga["out"][key], gb["out"][key]), "round %d layer %d %s" % (r, j, key)
+            assert torch.equal(ga["S"], gb["S"]), "round %d committed S layer %d" % (r, j)
+            assert torch.equal(ga["conv_state"], gb["conv_state"]), "round %d conv state layer %d" % (r, j)
+        assert torch.equal(a.prefix_len, b.prefix_len) and torch.equal(a.root_token, b.root_token)
+        for la, lb in zip(a.attn, b.attn):
+            assert torch.equal(la["k_cache"], lb["k_cache"]) and torch.equal(la["v_cache"], lb["v_cache"])

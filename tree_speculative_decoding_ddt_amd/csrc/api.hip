@@ -339,6 +339,42 @@ int ddt_gdn_tree_step(const void* x, const float* conv_w, const void* conv_state
                     "ddt_gdn_tree_step");
 }
 
+int ddt_gdn_tree_step_deferred(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                               const void* v, const float* beta, const float* g, const float* S, void* o,
+                               const int32_t* parent, int n, int B, int L, int H, int dk, int dv, int C, int W,
+                               int act_dt, void* ws, size_t ws_bytes, void* stream) {
+  DDT_NEED(x); DDT_NEED(conv_w); DDT_NEED(conv_state); DDT_NEED(conv_scratch); DDT_NEED(v);
+  DDT_NEED(beta); DDT_NEED(g); DDT_NEED(S); DDT_NEED(o); DDT_NEED(parent); DDT_NEED(ws);
+  const int st = gdn_args(n, B, L, H, dk, dv, C, W, act_dt);
+  if (st != DDT_OK) return st;
+  DDT_CHECK(act_dt == DDT_BF16, DDT_ERR_UNSUPPORTED,
+            "ddt_gdn_tree_step_deferred: built for bf16 activations (fp32 ones: ddt_gdn_tree_step)");
+  const size_t need = ddt::gdn_workspace(n, B + 1, H, dk);
+  DDT_CHECK(ws_bytes >= need, DDT_ERR_WORKSPACE, "ddt_gdn_tree_step_deferred: workspace %zu < %zu bytes", ws_bytes,
+            need);
+  DDT_CHECK(aligned16(ws) && aligned16(S) && aligned16(x) && aligned16(conv_state) && aligned16(conv_scratch),
+            DDT_ERR_ARG, "ddt_gdn_tree_step_deferred: workspace, state and activation buffers must be 16-byte aligned");
+  return hip_status(ddt::launch_gdn_tree_step_deferred(x, conv_w, conv_state, conv_scratch, v, beta, g, S, o, parent,
+                                                       n, B + 1, H, dk, W, act_dt, ws,
+                                                       static_cast<hipStream_t>(stream)),
+                    "ddt_gdn_tree_step_deferred");
+}
+
+int ddt_gdn_tree_states(const float* S, float* S_scratch, int n, int B, int H, int dk, int dv, const void* ws,
+                        size_t ws_bytes, void* stream) {
+  DDT_NEED(S); DDT_NEED(S_scratch); DDT_NEED(ws);
+  DDT_CHECK(n >= 1 && B >= 0 && B <= 64 && H >= 1, DDT_ERR_ARG,
+            "ddt_gdn_tree_states: need n>=1, 0<=B<=64, H>=1 (got n=%d B=%d H=%d)", n, B, H);
+  DDT_CHECK(dk == dv && (dk == 32 || dk == 64 || dk == 128), DDT_ERR_UNSUPPORTED,
+            "ddt_gdn_tree_states: dk=%d dv=%d not built (dk == dv in {32, 64, 128})", dk, dv);
+  const size_t need = ddt::gdn_workspace(n, B + 1, H, dk);
+  DDT_CHECK(ws_bytes >= need, DDT_ERR_WORKSPACE, "ddt_gdn_tree_states: workspace %zu < %zu bytes", ws_bytes, need);
+  DDT_CHECK(aligned16(ws) && aligned16(S) && aligned16(S_scratch), DDT_ERR_ARG,
+            "ddt_gdn_tree_states: workspace and state buffers must be 16-byte aligned");
+  return hip_status(ddt::launch_gdn_tree_states(S, S_scratch, n, B + 1, H, dk, ws, static_cast<hipStream_t>(stream)),
+                    "ddt_gdn_tree_states");
+}
+
 // ---------------------------------------------------------------- GDN replay on commit
 int ddt_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,
                    int n_layers, int H, int dk, int dv, int C, int W, int act_dt, int n, int B, int L,

@@ -762,10 +762,15 @@ size_t gdn_chunk_store_bytes(int n, int T, int H) {
   return ((size_t)n * tri * 4 + 255) / 256 * 256 + ((size_t)n * H * tri * 4 + 255) / 256 * 256;
 }
 
-hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
-                                   const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
-                                   void* o, const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt,
-                                   float* kbuf, float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st) {
+// The record tables follow one another in `tables`: rows [n][TRI] int32, then rho [n][H][TRI].
+static float* rho_table(void* tables, int n, int T) {
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(tables) + ((size_t)n * rec_base(T) * 4 + 255) / 256 * 256);
+}
+
+hipError_t launch_gdn_chunk_exports(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                                    const void* v, const float* beta, const float* g, const float* S, void* o,
+                                    const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt, float* kbuf,
+                                    float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st) {
   if (!chunk_shape_ok(act_dt, T, W, dk) || W < 2) return hipErrorInvalidValue;
   ChunkStoreOut so;
   so.conv_scratch = static_cast<uint16_t*>(conv_scratch);
@@ -774,19 +779,40 @@ hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const voi
   so.gam = gam;
   so.dep = dep;
   so.rows = static_cast<int32_t*>(tables);
-  so.rho = reinterpret_cast<float*>(static_cast<uint8_t*>(tables) + ((size_t)n * rec_base(T) * 4 + 255) / 256 * 256);
-#define DDT_STORED(DKV)                                                                                           \
-  do {                                                                                                            \
-    constexpr int RPT = kStatesRPT * 1024 <= DKV * DKV ? kStatesRPT : DKV * DKV / 1024;                           \
-    launch_chunk_w<DKV, true>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);               \
-    hipLaunchKernelGGL((gdn_states_kernel<DKV, RPT>), dim3((unsigned)((size_t)n * T * H * DKV * DKV / (1024 * RPT))), \
-                       dim3(256), 0, st, S, kbuf, wbuf, so.rows, so.rho, gam, dep, S_scratch, T, H);             \
-  } while (0)
-  if (dk == 32) DDT_STORED(32);
-  else if (dk == 64) DDT_STORED(64);
-  else DDT_STORED(128);
-#undef DDT_STORED
+  so.rho = rho_table(tables, n, T);
+  if (dk == 32) launch_chunk_w<32, true>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);
+  else if (dk == 64) launch_chunk_w<64, true>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);
+  else launch_chunk_w<128, true>(x, conv_w, conv_state, v, beta, g, S, o, parent, n, T, H, W, so, st);
   return hipGetLastError();
+}
+
+hipError_t launch_gdn_states(const float* S, float* S_scratch, int n, int T, int H, int dk, const float* kbuf,
+                             const float* wbuf, const float* gam, const int32_t* dep, const void* tables,
+                             hipStream_t st) {
+  if (T < 1 || T > kChunkMaxT || !(dk == 32 || dk == 64 || dk == 128)) return hipErrorInvalidValue;
+  const int32_t* rows = static_cast<const int32_t*>(tables);
+  const float* rho = rho_table(const_cast<void*>(tables), n, T);
+#define DDT_STATES(DKV)                                                                                          \
+  do {                                                                                                           \
+    constexpr int RPT = kStatesRPT * 1024 <= DKV * DKV ? kStatesRPT : DKV * DKV / 1024;                          \
+    hipLaunchKernelGGL((gdn_states_kernel<DKV, RPT>), dim3((unsigned)((size_t)n * T * H * DKV * DKV / (1024 * RPT))), \
+                       dim3(256), 0, st, S, kbuf, wbuf, rows, rho, gam, dep, S_scratch, T, H);                  \
+  } while (0)
+  if (dk == 32) DDT_STATES(32);
+  else if (dk == 64) DDT_STATES(64);
+  else DDT_STATES(128);
+#undef DDT_STATES
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                                   const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
+                                   void* o, const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt,
+                                   float* kbuf, float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st) {
+  const hipError_t e = launch_gdn_chunk_exports(x, conv_w, conv_state, conv_scratch, v, beta, g, S, o, parent, n, T, H,
+                                                dk, W, act_dt, kbuf, wbuf, gam, dep, tables, st);
+  if (e != hipSuccess) return e;
+  return launch_gdn_states(S, S_scratch, n, T, H, dk, kbuf, wbuf, gam, dep, tables, st);
 }
 
 }  // namespace ddt

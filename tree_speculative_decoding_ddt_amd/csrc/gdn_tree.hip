@@ -419,6 +419,43 @@ size_t gdn_workspace(int n, int T, int H, int dk) {
   return (qk + 255) / 256 * 256 + (kq + 255) / 256 * 256 + (ord + 255) / 256 * 256 + gdn_chunk_store_bytes(n, T, H);
 }
 
+// Where the chunk form with node states keeps its hand-over in the workspace (the areas of
+// gdn_workspace()): k and w in the q|k area, G_t in the k.q area, the depths in the order
+// area, then the record tables.
+struct ChunkWs {
+  float *k, *w, *gam;
+  int32_t* dep;
+  void* tables;
+};
+static ChunkWs chunk_ws(void* ws, int n, int T, int H, int dk) {
+  const size_t qk_b = ((size_t)n * T * H * 2 * dk * sizeof(float) + 255) / 256 * 256;
+  const size_t kq_b = ((size_t)n * T * H * sizeof(float) + 255) / 256 * 256;
+  const size_t ord_b = ((size_t)n * T * sizeof(int32_t) + 255) / 256 * 256;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  ChunkWs c;
+  c.k = reinterpret_cast<float*>(b);
+  c.w = c.k + (size_t)n * T * H * dk;
+  c.gam = reinterpret_cast<float*>(b + qk_b);
+  c.dep = reinterpret_cast<int32_t*>(b + qk_b + kq_b);
+  c.tables = b + qk_b + kq_b + ord_b;
+  return c;
+}
+
+hipError_t launch_gdn_tree_step_deferred(const void* x, const float* conv_w, const void* conv_state,
+                                         void* conv_scratch, const void* v, const float* beta, const float* g,
+                                         const float* S, void* o, const int32_t* parent, int n, int T, int H, int dk,
+                                         int W, int act_dt, void* ws, hipStream_t st) {
+  const ChunkWs c = chunk_ws(ws, n, T, H, dk);
+  return launch_gdn_chunk_exports(x, conv_w, conv_state, conv_scratch, v, beta, g, S, o, parent, n, T, H, dk, W,
+                                  act_dt, c.k, c.w, c.gam, c.dep, c.tables, st);
+}
+
+hipError_t launch_gdn_tree_states(const float* S, float* S_scratch, int n, int T, int H, int dk, const void* ws,
+                                  hipStream_t st) {
+  const ChunkWs c = chunk_ws(const_cast<void*>(ws), n, T, H, dk);
+  return launch_gdn_states(S, S_scratch, n, T, H, dk, c.k, c.w, c.gam, c.dep, c.tables, st);
+}
+
 // Depth bound up to which node states are formed from the chunk form.  The states
 // kernel's work grows with each node's path length: on bushy trees (mean path about 5
 // rows at L 15) it writes the states in 0.22 ms per call against the walk's 0.24, while
@@ -449,9 +486,9 @@ static hipError_t launch_gdn(const void* x, const float* conv_w, const void* con
     // stored states, bf16 activations: the chunk form gives every node's w, then each
     // state is written by short-lived blocks (k and w in the q|k area, G_t in the k.q
     // area, depths in the order area)
+    const ChunkWs c = chunk_ws(ws, n, T, H, DK);
     return launch_gdn_chunk_stored(x, conv_w, conv_state, conv_scratch, v, beta, g, S, S_scratch, o, parent, n, T, H,
-                                   DK, W, DDT_BF16, qk, qk + (size_t)n * T * H * DK, kq, ord,
-                                   static_cast<uint8_t*>(ws) + qk_b + kq_b + ((size_t)n * T * 4 + 255) / 256 * 256, st);
+                                   DK, W, DDT_BF16, c.k, c.w, c.gam, c.dep, c.tables, st);
   }
   const dim3 cgrid(n * T, (H + 256 / (DK / 4) - 1) / (256 / (DK / 4)));
   if (W == 4)

@@ -106,6 +106,20 @@ hipError_t launch_gdn_chunk_stored(const void* x, const float* conv_w, const voi
                                    const void* v, const float* beta, const float* g, const float* S, float* S_scratch,
                                    void* o, const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt,
                                    float* kbuf, float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st);
+hipError_t launch_gdn_chunk_exports(const void* x, const float* conv_w, const void* conv_state, void* conv_scratch,
+                                    const void* v, const float* beta, const float* g, const float* S, void* o,
+                                    const int32_t* parent, int n, int T, int H, int dk, int W, int act_dt, float* kbuf,
+                                    float* wbuf, float* gam, int32_t* dep, void* tables, hipStream_t st);
+hipError_t launch_gdn_states(const float* S, float* S_scratch, int n, int T, int H, int dk, const float* kbuf,
+                             const float* wbuf, const float* gam, const int32_t* dep, const void* tables,
+                             hipStream_t st);
+// the same split behind the C ABI (workspace of gdn_workspace(); see gdn_tree.hip)
+hipError_t launch_gdn_tree_step_deferred(const void* x, const float* conv_w, const void* conv_state,
+                                         void* conv_scratch, const void* v, const float* beta, const float* g,
+                                         const float* S, void* o, const int32_t* parent, int n, int T, int H, int dk,
+                                         int W, int act_dt, void* ws, hipStream_t st);
+hipError_t launch_gdn_tree_states(const float* S, float* S_scratch, int n, int T, int H, int dk, const void* ws,
+                                  hipStream_t st);
 
 // ---- GDN replay on commit
 hipError_t launch_gdn_replay(const int32_t* acc_rows, const int32_t* acc_len, const ddt_gdn_replay_layer* layers,

@@ -24,7 +24,7 @@ EXPORTS = ("ddt_status_string", "ddt_last_error", "ddt_abi_version",
            "ddt_tree_attn_rope_workspace", "ddt_tree_attn_rope", "ddt_tree_rope",
            "ddt_tree_attn_paged_workspace", "ddt_tree_attn_paged", "ddt_commit_paged",
            "ddt_tree_accept_sampled",
-           "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step",
+           "ddt_gdn_tree_step_workspace", "ddt_gdn_tree_step", "ddt_gdn_tree_step_deferred", "ddt_gdn_tree_states",
            "ddt_tree_accept_workspace", "ddt_tree_accept",
            "ddt_commit", "ddt_gdn_replay")
 
@@ -86,6 +86,8 @@ def lib():
         "ddt_tree_attn_rope": (I, [P, P, P, P, I, F, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P]),
         "ddt_gdn_tree_step_workspace": (Z, [I, I, I, I]),
         "ddt_gdn_tree_step": (I, [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P]),
+        "ddt_gdn_tree_step_deferred": (I, [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P]),
+        "ddt_gdn_tree_states": (I, [P, P, I, I, I, I, I, P, Z, P]),
         "ddt_tree_accept_workspace": (Z, [I, I, I]),
         "ddt_tree_accept": (I, [P, I, P, P, I, I, I, I, P, P, P, P, Z, P]),
         "ddt_commit": (I, [P, P, P, ctypes.POINTER(KVLayer), I, I, I, I, I,
@@ -309,6 +311,37 @@ def gdn_tree_step(x, conv_w, conv_state, v, beta, g, S, parent, L, ws=None, out=
         _ptr(S), _ptr(Ssc), _ptr(out["o"]), _ptr(parent), n, T - 1, L, H, dk, dv, C, W,
         _dt(x), _ptr(w), w.numel() * w.element_size(), _stream(dev)))
     return out
+
+
+def gdn_tree_step_deferred(x, conv_w, conv_state, v, beta, g, S, parent, L, ws, out=None):
+    """The tree step without the node-state write (bf16): o and conv_scratch, with each node's
+    k, w and path records left in ws (a uint8 tensor of gdn_tree_step_workspace bytes, which the
+    caller keeps for gdn_tree_states) -> dict o, S_scratch (allocated, not written), conv_scratch."""
+    _gpu(x, conv_w, conv_state, v, beta, g, S, parent, ws)
+    n, T, C = x.shape
+    W = conv_w.shape[1]
+    H, dv, dk = S.shape[1], S.shape[2], S.shape[3]
+    dev = x.device
+    if out is None:
+        out = {"o": torch.empty(n, T, H, dv, dtype=x.dtype, device=dev),
+               "S_scratch": torch.empty(n, T, H, dv, dk, dtype=torch.float32, device=dev),
+               "conv_scratch": torch.empty(n, T, W - 1, C, dtype=x.dtype, device=dev)}
+    _check("ddt_gdn_tree_step_deferred", lib().ddt_gdn_tree_step_deferred(
+        _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(out["conv_scratch"]), _ptr(v), _ptr(beta), _ptr(g),
+        _ptr(S), _ptr(out["o"]), _ptr(parent), n, T - 1, L, H, dk, dv, C, W,
+        _dt(x), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out
+
+
+def gdn_tree_states(S, S_scratch, ws, stream=None):
+    """Write every node's state into S_scratch [n][T][H][dv][dk] from S [n][H][dv][dk] and the ws a
+    gdn_tree_step_deferred call left (on `stream`, a torch stream; default the current one)."""
+    _gpu(S, S_scratch, ws)
+    n, T, H, dv, dk = S_scratch.shape
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(S.device)
+    _check("ddt_gdn_tree_states", lib().ddt_gdn_tree_states(
+        _ptr(S), _ptr(S_scratch), n, T - 1, H, dk, dv, _ptr(ws), ws.numel() * ws.element_size(), st))
+    return S_scratch
 
 
 def tree_accept(target_logits, tok, parent, L, ws=None, out=None):
