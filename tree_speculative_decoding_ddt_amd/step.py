@@ -45,9 +45,9 @@ class HybridConfig:
     page_size: int = 0         # > 0: the committed KV lives in pages of this many positions (block table)
     sampled: bool = False      # the walk over sampled target tokens (gumbel noise + per-sequence temperature)
     # stored states, bf16: each GDN layer's node-state write (ddt_gdn_tree_states) runs on a
-    # second stream while the next layers run, joined before the commit (one workspace per
-    # GDN layer). Off by default: the state blocks then take CUs from the attention and chunk
-    # kernels, and the round is about 0.7 ms slower than with the writes in line.
+    # second stream beside the next GDN layers, joined before each attention layer and the
+    # commit (one workspace per GDN layer). Off by default: the state writes fill every CU,
+    # so the next chunk kernel waits for them anyway and the round gains nothing.
     overlap_states: bool = False
 
     def layer_pattern(self):
@@ -190,6 +190,8 @@ class HybridVerifyStep:
         ia = ig = 0
         for kind in self.pattern:
             if kind == "attn":
+                if self.overlapping():
+                    main.wait_stream(self.side)  # the state writes run beside GDN layers only
                 a = self.attn[ia]
                 ia += 1
                 if self.cfg.rope:
