@@ -146,13 +146,19 @@ def test_chunk_form_matches_walk_states():
     np.testing.assert_array_equal(down(a["conv_scratch"]), down(b["conv_scratch"]))
 
 
-def test_deferred_state_write_matches_the_call():
+@pytest.mark.parametrize("kind", ["random", "chain"])
+def test_deferred_state_write_matches_the_call(kind):
     # ddt_gdn_tree_step_deferred + ddt_gdn_tree_states (the latter on a second stream after
-    # an event) leave exactly what one ddt_gdn_tree_step call (chunk form) leaves
-    say("gdn deferred state write on a second stream vs the single call")
+    # an event) leave exactly what one ddt_gdn_tree_step call (chunk form) leaves, also for
+    # a 64-deep chain (paths of up to 65 rows; the chunk form itself is checked against the
+    # oracle on that chain in test_chunk_form_states)
+    say("gdn deferred state write on a second stream vs the single call, %s tree" % kind)
     rng = np.random.default_rng(55)
     n, B, L, H, dk = 2, 64, 15, 4, 128
-    parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
+    if kind == "chain":
+        parents = np.stack([np.arange(-1, B)] * n)
+    else:
+        parents = np.stack([synth.random_parents(rng, B, L)[0] for _ in range(n)])
     x = synth.gdn_inputs(rng, n, B + 1, H, dk, dk, 4)
     dev = {k: up(x[k], "bf16" if k in ("x", "v", "conv_state") else "f32")[0] for k in x}
     pt = up_int(parents)
