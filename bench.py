@@ -192,8 +192,16 @@ def cpu_baseline(step, a):
                        "fp64, BLAS threads %s, %d host cores"
                        % (cfg.n, t["build"], cfg.n_attn, P, t["attn"], cfg.n_gdn, t["gdn"], t["walk"], t["commit"],
                           per_seq, cfg.n, cfg.n * per_seq, blas, cores)),
-            "blas_threads": blas[0] if blas else None,
+            "blas_threads": blas[0] if blas else None, "cpu_model": cpu_model(),
             "agrees_with_gpu_round": agrees, "accepted_seq0": int(acc)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        return None
 
 
 def kernel_configs(a):
@@ -244,8 +252,7 @@ def kernel_configs(a):
 
     # the host and the box's own copy rate (a STREAM-style 1 GiB device-to-device copy,
     # bytes read + written), beside the nominal HBM peak
-    model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")), "?")
-    emit({"config": "host", "cpu_model": model, "cpu_threads": len(os.sched_getaffinity(0))})
+    emit({"config": "host", "cpu_model": cpu_model() or "?", "cpu_threads": len(os.sched_getaffinity(0))})
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(3)
