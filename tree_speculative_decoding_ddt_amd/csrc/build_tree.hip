@@ -611,17 +611,14 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
-// One wavefront per sequence, T = B+1 <= 65.  The frontier has one slot per lane: the
-// seed takes slot 0, pop i puts the popped node's sibling in the popped slot and its best
-// child in slot i at most (a fresh slot per pop), and the child of the last pop is never
-// popped, so 64 slots suffice.  A pop's chain is short: the wave-wide max of the slots'
-// 32-bit score keys (DPP; the 64-bit key (token, parent) only among lanes tied on the
-// score), the winner's fields by readlane, and the two new entries written by lane
-// selects.  The new sibling's score is the parent's score (kept in the slot) plus its
-// log-prob (prefetched when the slot was made); the best child comes from the lanes of
-// the depth (ranks 0 and 1 of depth d + 1 in lane d); the one LDS read, the new
-// sibling's own next sibling, is merged one pop later.  Node i's row, score and
-// ancestor mask are kept by lane i (node 64 in scalars) and stored at the end.
+// One wavefront per sequence, T = B+1 <= 65.  The frontier is kept sorted across the
+// lanes by the 64-bit key (score desc, token asc, parent row asc), so a pop reads lane 0
+// and needs no reduction.  Of its two successors, the next sibling's score is the parent
+// row's score plus the sibling's log-prob (one LDS read), and the best child comes from
+// the lanes of the depth (rank 0 of depth d + 1 in lane d); each is placed by one ballot
+// of the larger keys, and the other entries shift by DPP.  The pop order is the
+// best-first heap's, so the tree is the same.  Node i's row, score and ancestor mask are
+// kept by lane i (node 64 in scalars) and stored at the end.
 __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restrict__ top_id,
                                                          const float* __restrict__ top_lp, int L, int K,
                                                          int T, const int32_t* __restrict__ root_token,
@@ -630,8 +627,7 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
                                                          uint64_t* __restrict__ anc) {
   const int s = blockIdx.x, lane = threadIdx.x;
   extern __shared__ uint8_t smem[];
-  float* lp = reinterpret_cast<float*>(smem);                  // [L][K]
-  int32_t* ids = reinterpret_cast<int32_t*>(lp + L * K);       // [L][K]
+  float2* cand = reinterpret_cast<float2*>(smem);  // [L][K]: (log-prob, token bits), one 8-byte read
   for (int i0 = 0; i0 < L * K; i0 += 16 * 64) {  // sixteen loads of each in flight per lane
     float a[16];
     int b[16];
@@ -644,17 +640,15 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = min(i0 + 64 * u + lane, L * K - 1);
-      lp[i] = a[u];
-      ids[i] = b[u];
+      cand[i] = make_float2(a[u], __builtin_bit_cast(float, b[u]));
     }
   }
   __syncthreads();
 
-  // ranks 0 and 1 of depth d + 1 in lane d
-  const float bl0 = lane < L ? lp[lane * K] : -INFINITY;
-  const int bt0 = lane < L ? ids[lane * K] : -1;
-  const float bl1 = lane < L && 1 < K ? lp[lane * K + 1] : -INFINITY;
-  const int bt1 = lane < L && 1 < K ? ids[lane * K + 1] : -1;
+  // rank 0 of depth d + 1 in lane d
+  const float2 c0 = cand[min(lane, L - 1) * K];
+  const float bl0 = lane < L ? c0.x : -INFINITY;
+  const int bt0 = lane < L ? __builtin_bit_cast(int, c0.y) : -1;
   // node i (i <= 63) in lane i: token, parent, depth, score, ancestor mask
   int o_tok = lane == 0 ? root_token[s] : -1, o_par = -1, o_dep = lane == 0 ? 0 : -1;
   float o_sc = lane == 0 ? 0.f : -INFINITY;
@@ -663,95 +657,93 @@ __global__ void __launch_bounds__(64) heap_expand_kernel(const int32_t* __restri
   float sc64 = -INFINITY;
   uint64_t anc64 = 0ull;
 
-  // the slot in this lane: an entry (score, token, parent row, depth, rank), its parent's
-  // score and its next-ranked sibling (token, log-prob); everything a pop needs of the
-  // winner is in the winner's lane or, for the best child, in lanes of the depth
-  bool s_ok = false;
-  float s_sc = 0.f, s_psc = 0.f, s_nlp = -INFINITY;
-  int s_tok = 0, s_par = 0, s_dep = 0, s_rk = 0, s_ntk = -1;
-  // the next sibling of a popped slot's new entry is read from LDS at the pop and
-  // merged at the next one, after the reduction that hides its latency
-  int pend_lane = -1, pend_tok = -1;
-  float pend_lp = -INFINITY;
-  int nslots = 0;
+  // The frontier, sorted: lane p holds the entry of rank p by frontier key (lane 0 the
+  // best; empty lanes have f_tk1 = 0 and sort last).  An entry is its score, token + 1 and
+  // the packed (parent row << 16 | depth << 8 | rank); its parent's score is the parent
+  // row's (lane `parent` of o_sc) and its next-ranked sibling is read from LDS at its pop.
+  // A pop takes lane 0; its two successors (the next sibling, the best child) are placed
+  // by counting the lanes whose key is larger (one ballot each), and every other entry
+  // moves by 0, 1 or 2 lanes (wave-wide DPP shifts).  An entry pushed past lane 63 ranks
+  // below every pop still to come.
+  float f_sc = 0.f;
+  int f_tk1 = 0, f_pdr = 0;
   const int tok0 = __builtin_amdgcn_readlane(bt0, 0);
-  if (T > 1 && L >= 1 && tok0 >= 0) {
-    const float sc0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl0), 0));
-    const int nt = __builtin_amdgcn_readlane(bt1, 0);
-    const float nl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl1), 0));
-    if (lane == 0) {
-      s_sc = sc0; s_tok = tok0; s_par = 0; s_dep = 1; s_rk = 0; s_psc = 0.f; s_ntk = nt; s_nlp = nl; s_ok = true;
-    }
-    nslots = 1;
+  if (T > 1 && L >= 1 && tok0 >= 0 && lane == 0) {
+    f_sc = bl0; f_tk1 = tok0 + 1; f_pdr = 1 << 8;  // parent row 0 (the root), depth 1, rank 0
   }
-
-  for (int i = 1; i < T; ++i) {
-    const uint32_t k32 = s_ok ? max(float_key(s_sc), 1u) : 0u;  // 0: an empty slot
-    const uint32_t m32 = wave_max_u32_uniform(k32);
-    if (m32 == 0) break;
-    if (pend_lane >= 0) {
-      const bool me = lane == pend_lane;
-      s_ntk = me ? pend_tok : s_ntk;
-      s_nlp = me ? pend_lp : s_nlp;
-    }
-    const uint64_t tie = __ballot(s_ok && k32 == m32);
-    int owner;
-    if (__popcll(tie) == 1) {
-      owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(tie));
-    } else {  // equal scores: token asc, then parent row asc
-      const bool inn = s_ok && k32 == m32;
-      const uint64_t k = inn ? frontier_key(s_sc, s_tok, s_par) : 0ull;
-      const uint64_t best = wave_max_u64_uniform(k);
-      owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(__ballot(inn && k == best)));
-    }
-#define DDT_RLF(x) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), owner))
-    const float sc = DDT_RLF(s_sc), psc = DDT_RLF(s_psc), nlp = DDT_RLF(s_nlp);
-#undef DDT_RLF
-    const int tk = __builtin_amdgcn_readlane(s_tok, owner), pr = __builtin_amdgcn_readlane(s_par, owner);
-    const int dp = __builtin_amdgcn_readlane(s_dep, owner), rk = __builtin_amdgcn_readlane(s_rk, owner);
-    const int ntk = __builtin_amdgcn_readlane(s_ntk, owner);
-    // the popped slot takes its next-ranked sibling (whose own next sibling is fetched
-    // now), or empties; the best child goes to a fresh slot (none after the last pop).
-    // Written without branches: every update is a lane select.
-    const bool own = lane == owner;
-    const bool sib = ntk >= 0;
-    s_sc = own && sib ? psc + nlp : s_sc;
-    s_tok = own && sib ? ntk : s_tok;
-    s_rk = own && sib ? rk + 1 : s_rk;
-    s_ok = own && !sib ? false : s_ok;
-    const int nx = min(max((dp - 1) * K + rk + 2, 0), L * K - 1);
-    pend_tok = sib && rk + 2 < K ? ids[nx] : -1;
-    pend_lp = sib && rk + 2 < K ? lp[nx] : -INFINITY;
-    pend_lane = sib ? owner : -1;
+  // wave_shl:1 (lane l reads lane l+1) and wave_shr:1 (lane l reads lane l-1); a lane
+  // with no source reads 0 (an empty entry, as f_tk1 = 0)
+#define DDT_SHL1(x) __builtin_amdgcn_mov_dpp((x), 0x130, 0xf, 0xf, true)
+#define DDT_SHR1(x) __builtin_amdgcn_mov_dpp((x), 0x138, 0xf, 0xf, true)
+#define DDT_RLF(x, l) __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, (x)), (l)))
+  // pops 1 .. min(T, 64) - 1 (node 64, if any, is popped after the loop); a pop from an
+  // empty frontier (a tree of fewer than B nodes) changes nothing
+  const int tpop = min(T, 64);
+  for (int i = 1; i < tpop; ++i) {
+    const int tk = __builtin_amdgcn_readfirstlane(f_tk1) - 1;
+    const bool live = tk >= 0;
+    const float sc = DDT_RLF(f_sc, 0);
+    const int pdr = __builtin_amdgcn_readfirstlane(f_pdr);
+    const int pr = pdr >> 16, dp = (pdr >> 8) & 255, rk = pdr & 255;
+    // the next sibling: rank rk + 1 of depth dp under the same parent
+    const int nx = min(max((dp - 1) * K + rk + 1, 0), L * K - 1);
+    const float2 nc = cand[nx];
+    const float nlp = nc.x;
+    const int ntk = live && rk + 1 < K ? __builtin_bit_cast(int, nc.y) : -1;
+    const float psc = DDT_RLF(o_sc, pr);
+    // the best child: rank 0 of depth dp + 1 (none after the last pop)
     const int dpc = min(dp, 63);
     const int ctk = __builtin_amdgcn_readlane(bt0, dpc);
-    const float clp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl0), dpc));
-    const int cnt = __builtin_amdgcn_readlane(bt1, dpc);
-    const float cnl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl1), dpc));
-    const bool chd = i + 1 < T && dp < L && ctk >= 0;
-    const bool fr = chd && lane == nslots;
-    s_sc = fr ? sc + clp : s_sc;
-    s_tok = fr ? ctk : s_tok;
-    s_par = fr ? i : s_par;
-    s_dep = fr ? dp + 1 : s_dep;
-    s_rk = fr ? 0 : s_rk;
-    s_psc = fr ? sc : s_psc;
-    s_ntk = fr ? cnt : s_ntk;
-    s_nlp = fr ? cnl : s_nlp;
-    s_ok = fr ? true : s_ok;
-    nslots += chd ? 1 : 0;
-    // node i's row (off the next pop's path)
+    const float clp = DDT_RLF(bl0, dpc);
+    const bool sib = ntk >= 0;
+    const bool chd = live && i + 1 < T && dp < L && ctk >= 0;
+    const float scA = psc + nlp, scB = sc + clp;
+    const uint64_t kA = frontier_key(scA, ntk, pr), kB = frontier_key(scB, ctk, i);
+    // ranks among the entries left after the pop (lanes 1..63)
+    const uint64_t kl = (lane >= 1 && f_tk1 > 0) ? frontier_key(f_sc, f_tk1 - 1, f_pdr >> 16) : 0ull;
+    const int cA = __popcll(__ballot(kl > kA)), cB = __popcll(__ballot(kl > kB));
+    const int posA = sib ? cA + (chd && kB > kA ? 1 : 0) : 99;
+    const int posB = chd ? cB + (sib && kA > kB ? 1 : 0) : 99;
+    // entry of lane l after the pop and the insertions: A or B, else the old entry of lane
+    // l + 1 - (new entries placed before l)
+    const int nb = (lane > posA ? 1 : 0) + (lane > posB ? 1 : 0);
+    {
+      const int s0 = __builtin_bit_cast(int, f_sc);
+      const int a0 = DDT_SHL1(s0), a2 = DDT_SHR1(s0);
+      const int b0 = DDT_SHL1(f_tk1), b2 = DDT_SHR1(f_tk1);
+      const int c0 = DDT_SHL1(f_pdr), c2 = DDT_SHR1(f_pdr);
+      const int ms = nb == 0 ? a0 : (nb == 1 ? s0 : a2);
+      f_tk1 = nb == 0 ? b0 : (nb == 1 ? f_tk1 : b2);
+      f_pdr = nb == 0 ? c0 : (nb == 1 ? f_pdr : c2);
+      f_sc = __builtin_bit_cast(float, ms);
+    }
+    const bool isA = lane == posA, isB = lane == posB;
+    f_sc = isA ? scA : (isB ? scB : f_sc);
+    f_tk1 = isA ? ntk + 1 : (isB ? ctk + 1 : f_tk1);
+    f_pdr = isA ? pdr + 1 : (isB ? ((i << 16) | ((dp + 1) << 8)) : f_pdr);
+    // node i's row
     const uint64_t a = readlane_u64(o_anc, pr) | (1ull << (i - 1));
-    const bool me = lane == i;
+    const bool me = live && lane == i;
     o_tok = me ? tk : o_tok;
     o_par = me ? pr : o_par;
     o_dep = me ? dp : o_dep;
     o_sc = me ? sc : o_sc;
     o_anc = me ? a : o_anc;
-    if (i == 64) {
-      tok64 = tk; par64 = pr; dep64 = dp; sc64 = sc; anc64 = a;
+  }
+  if (T > 64) {  // the last pop: node 64 (its successors are not needed)
+    const int tk = __builtin_amdgcn_readfirstlane(f_tk1) - 1;
+    if (tk >= 0) {
+      const int pdr = __builtin_amdgcn_readfirstlane(f_pdr);
+      tok64 = tk;
+      par64 = pdr >> 16;
+      dep64 = (pdr >> 8) & 255;
+      sc64 = DDT_RLF(f_sc, 0);
+      anc64 = readlane_u64(o_anc, par64) | (1ull << 63);
     }
   }
+#undef DDT_SHL1
+#undef DDT_SHR1
+#undef DDT_RLF
   // the rows: node i from lane i (rows not reached keep tok -1, depth -1, score -inf)
   const size_t ob = (size_t)s * T;
   if (lane < T) {
@@ -840,7 +832,7 @@ hipError_t launch_build_tree(const void* logits, int dt, int n, int L, int V, in
                        tid, tlp);
   }
 #undef DDT_TOPK
-  const size_t smem = (size_t)L * plan.K * (sizeof(float) + sizeof(int32_t));
+  const size_t smem = (size_t)L * plan.K * sizeof(float2);
   hipLaunchKernelGGL(heap_expand_kernel, dim3(n), dim3(64), smem, st, tid, tlp, L, plan.K, B + 1, root_token,
                      tok, parent, depth, score, anc);
   return hipGetLastError();
