@@ -106,7 +106,8 @@ def test_bf16_full_size_sampled(n, P):
 
 def test_bf16_bench_launch_configuration_sampled():
     # the launch the step benchmark times: 8 sequences at a prefix that has grown past
-    # 32768 in a cache of 33104 rows (four splits of 8288 keys, the last one ragged)
+    # 32768 in a cache of 33104 rows (four splits, planned at up to 8288 keys from the
+    # capacity; each sequence's prefix and tree keys spread as 8224 keys per split)
     say("tree_attn bf16 n=8 P=32790 Pmax=33104 (sampled rows)")
     run_case(91, 8, 64, 15, 24, 4, 256, 33104, [32790 + s for s in range(8)], "bf16",
              rows=lambda p: sample_rows(p)[:4])
@@ -118,6 +119,14 @@ def test_bf16_workload_batch_full_compare():
     # the multi-split path (splits of at least 512 keys) and the two row groups per kv head
     say("tree_attn bf16 n=8 P~4096, all rows and heads")
     run_case(95, 8, 64, 15, 24, 4, 256, 4160, [4096 - 37 * s for s in range(8)], "bf16")
+
+
+def test_bf16_prefix_far_below_capacity():
+    # the splits are planned from the capacity (here 16 of at most 512 keys); each
+    # sequence spreads its own prefix and tree keys over them: 224 keys per split for the
+    # first sequence, 64 for the second, whose later prefix splits are empty
+    say("tree_attn bf16 n=2 P=3000/700 in a cache of 8192, all rows and heads")
+    run_case(97, 2, 64, 15, 24, 4, 256, 8192, [3000, 700], "bf16")
 
 
 def test_bf16_long_context_lopsided():

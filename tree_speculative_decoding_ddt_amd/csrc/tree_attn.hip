@@ -203,10 +203,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
 
-  // key tiles: this split's slice of the prefix, then (last split) the tree rows
+  // key tiles: this split's slice of the prefix, then (last split) the tree rows.  The
+  // split length is this sequence's: its prefix plus the tree keys spread evenly over the
+  // nsplit splits in whole tiles (split_len, planned from the cache capacity, bounds it),
+  // so a prefix shorter than the capacity does not leave the last split short and the
+  // others long
   const int P = min(max(prefix_len[s], 0), Pmax);
-  const int k_beg = min(split * split_len, P);
-  const int k_end = min(P, k_beg + split_len);
+  const int ttl = (Tn + NK - 1) / NK * NK;
+  const int sl = min(split_len, ((P + ttl + nsplit - 1) / nsplit + NK - 1) / NK * NK);
+  const int k_beg = min(split * sl, P);
+  const int k_end = last ? P : min(P, k_beg + sl);
   const int n_pre = (k_end - k_beg + NK - 1) / NK;
   const int n_all = n_pre + (last ? (Tn + NK - 1) / NK : 0);
   const size_t hoff = (size_t)s * Hkv + kvh;
