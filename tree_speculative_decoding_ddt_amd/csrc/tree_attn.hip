@@ -607,11 +607,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
 }
 
 // Merge of the split partials: one lane per 4 output columns of one (sequence, tree
-// row, q head); parts are weighted by 2^(lse_p - max lse) and renormalised.
+// row, q head); parts are weighted by 2^(lse_p - max lse) and renormalised.  The loads
+// do not wait on one another: the parts' lse values first (eight in flight per lane),
+// then every part's O row unconditionally (a split that saw no key wrote lse -inf and
+// O = 0, so its weight is 0), eight at a time.
 template <int D>
 __global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __restrict__ part_lse,
                                                              const float* __restrict__ part_o, int Tn, int Hq,
                                                              int Hkv, int nparts, uint16_t* __restrict__ out) {
+  constexpr int U = 8;
   const int hq = blockIdx.x % Hq;
   const int t = (blockIdx.x / Hq) % Tn;
   const int s = blockIdx.x / (Hq * Tn);
@@ -619,16 +623,30 @@ __global__ void __launch_bounds__(D / 4) attn_combine_kernel(const float* __rest
   const int d4 = threadIdx.x;
   const size_t base = (size_t)(s * Hkv + hq / G) * nparts * R + t * G + hq % G;
   float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, part_lse[base + (size_t)p * R]);
+  for (int p0 = 0; p0 < nparts; p0 += U) {
+    float ls[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ls[u] = part_lse[base + (size_t)min(p0 + u, nparts - 1) * R];
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, ls[u]);  // a clamped index repeats a part: same max
+  }
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = 0; p < nparts; ++p) {
-    const float ls = part_lse[base + (size_t)p * R];
-    if (ls == -INFINITY) continue;
-    const float w = exp2f(ls - M);
-    const float4 o = *reinterpret_cast<const float4*>(&part_o[(base + (size_t)p * R) * D + 4 * d4]);
-    wsum += w;
-    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+  for (int p0 = 0; p0 < nparts; p0 += U) {
+    float ls[U];
+    float4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t pb = base + (size_t)min(p0 + u, nparts - 1) * R;
+      ls[u] = part_lse[pb];
+      o[u] = *reinterpret_cast<const float4*>(&part_o[pb * D + 4 * d4]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // weight 0 (adds exact zeros: the O rows are finite) past the parts
+      const float w = (p0 + u < nparts && ls[u] != -INFINITY) ? exp2f(ls[u] - M) : 0.f;
+      wsum += w;
+      acc.x += w * o[u].x; acc.y += w * o[u].y; acc.z += w * o[u].z; acc.w += w * o[u].w;
+    }
   }
   const float inv = 1.f / wsum;
   const uint32_t lo = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
