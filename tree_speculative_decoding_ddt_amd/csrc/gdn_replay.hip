@@ -16,9 +16,10 @@
 //
 // Two kernels per group of layers:
 //   replay_state  grid (n*H, dv/R, layers): a block owns R rows of one head's state in
-//                 registers (a thread 8 columns of one row, as in the tree walk); per
-//                 path node the block computes the head's dk k-channels in LDS, then
-//                 every row takes its rank-1 update.  Reads the committed conv rows.
+//                 registers (a thread 8 columns of one row, as in the tree walk); the
+//                 path's inputs are read into LDS first, all at once; per path node the
+//                 block computes the head's dk k-channels, then every row takes its
+//                 rank-1 update.  Reads the committed conv rows.
 //   replay_conv   grid (n, layers, C/256): one thread per channel rebuilds the W-1
 //                 committed conv rows (exact copies), after every state block has read
 //                 them (stream order).
@@ -71,11 +72,14 @@ __global__ void __launch_bounds__(256) replay_state_kernel(ReplayTable tab, cons
   constexpr int GS = DK / (CPT / 4);     // stride between a thread's column groups
   const int s = blockIdx.x / H, h = blockIdx.x % H, layer = blockIdx.z;
   const int tid = threadIdx.x;
-  const int r = blockIdx.y * R + tid / LPR;
+  const int rl = tid / LPR, r = blockIdx.y * R + rl;
   const int c0 = (tid % LPR) * 4;
   __shared__ int rows[64];
   __shared__ float ks[DK];
   __shared__ float red[DK / 64 + 1];
+  __shared__ float gbs[2][64];  // g and beta of every path node (this head)
+  __shared__ float vs[64][R];   // v of every path node (this block's rows)
+  extern __shared__ float xk[];  // [(W-1) + a+1][DK]: the k channels' committed conv rows, then path rows
   int a;
   if (!load_path(acc_rows, acc_len, s, Tn, Lp1, rows, a)) return;
 
@@ -92,18 +96,41 @@ __global__ void __launch_bounds__(256) replay_state_kernel(ReplayTable tab, cons
 #pragma unroll
   for (int e = 0; e < CPT; ++e) st[e] = srow[(e / 4) * GS + (e % 4)];
 
+  // Every input of the path is read up front, all loads in flight together (they depend
+  // on the path rows only, not on the state): the window values of the head's k channels
+  // (the W-1 committed conv rows, then the path rows in order, so that node j's window is
+  // entries j .. j+W-1), each node's g, beta and v, and this channel's weights.
+  const int nw = (W - 1) + (a + 1);
+  for (int i = tid; i < nw * DK; i += 256) {
+    const int q = i / DK, kc = H * DK + h * DK + (i % DK);
+    const A val = q < W - 1 ? cs[((size_t)s * (W - 1) + q) * C + kc]
+                            : x[((size_t)s * Tn + rows[q - (W - 1)]) * C + kc];
+    xk[i] = Elem<A>::load(&val, 0);
+  }
+  for (int j = tid; j <= a; j += 256) {
+    const size_t ti = ((size_t)s * Tn + rows[j]) * H + h;
+    gbs[0][j] = g[ti];
+    gbs[1][j] = beta[ti];
+  }
+  for (int i = tid; i < (a + 1) * R; i += 256) {
+    const int j = i / R, q = i % R;
+    vs[j][q] = Elem<A>::load(v, (((size_t)s * Tn + rows[j]) * H + h) * DV + blockIdx.y * R + q);
+  }
   const int kc = H * DK + h * DK + tid;  // k channel computed by thread tid < DK
+  float wk[kReplayMaxW];                 // wk[b]: the weight of back b (tap W-1-b)
+#pragma unroll
+  for (int b = 0; b < kReplayMaxW; ++b) wk[b] = tid < DK && b < W ? w[(size_t)kc * W + (W - 1 - b)] : 0.f;
+  __syncthreads();
+
   for (int j = 0; j <= a; ++j) {
-    const int u = rows[j];
     float y = 0.f;
     if (tid < DK) {
-      // back b: path row r_{j-b}, or past the root the committed conv row W-1-(b-j)
+      // back b: entry j + W-1 - b of the window (path row r_{j-b}, or past the root the
+      // committed conv row W-1-(b-j))
       float acc = 0.f;
-      for (int b = 0; b < W; ++b) {
-        const A val = b <= j ? x[((size_t)s * Tn + rows[j - b]) * C + kc]
-                             : cs[((size_t)s * (W - 1) + (W - 1 - (b - j))) * C + kc];
-        acc += w[(size_t)kc * W + (W - 1 - b)] * Elem<A>::load(&val, 0);
-      }
+#pragma unroll
+      for (int b = 0; b < kReplayMaxW; ++b)
+        if (b < W) acc += wk[b] * xk[(j + W - 1 - b) * DK + tid];
       y = acc / (1.f + __expf(-acc));
       ks[tid] = y;
     }
@@ -123,9 +150,8 @@ __global__ void __launch_bounds__(256) replay_state_kernel(ReplayTable tab, cons
 #pragma unroll
     for (int e = 0; e < CPT; ++e) dot += st[e] * kv[e];
     dot = group_sum<LPR>(dot);
-    const size_t ti = ((size_t)s * Tn + u) * H + h;
-    const float gi = g[ti], bi = beta[ti];
-    const float delta = bi * (Elem<A>::load(v, ti * DV + r) - gi * dot);
+    const float gi = gbs[0][j], bi = gbs[1][j];
+    const float delta = bi * (vs[j][rl] - gi * dot);
 #pragma unroll
     for (int e = 0; e < CPT; ++e) st[e] = gi * st[e] + delta * kv[e];
     __syncthreads();  // ks and red are rewritten by the next node
@@ -165,7 +191,8 @@ template <typename A, int DK>
 static void launch_replay_dk(const ReplayTable& tab, int cnt, const int32_t* acc_rows, const int32_t* acc_len, int n,
                              int T, int Lp1, int H, int C, int W, hipStream_t st) {
   constexpr int R = 256 / (DK / (DK >= 64 ? 8 : 4));
-  hipLaunchKernelGGL((replay_state_kernel<A, DK>), dim3(n * H, DK / R, cnt), dim3(256), 0, st, tab, acc_rows,
+  const size_t smem = (size_t)((W - 1) + Lp1) * DK * sizeof(float);  // the path's window values (<= 36 KB)
+  hipLaunchKernelGGL((replay_state_kernel<A, DK>), dim3(n * H, DK / R, cnt), dim3(256), smem, st, tab, acc_rows,
                      acc_len, T, Lp1, H, C, W);
 }
 
