@@ -208,7 +208,7 @@ def kernel_configs(a):
     """Per-config kernel figures (tree build, tree attention at 8K/32K/128K, the full step at
     its 16K prefix): median of 50 calls after 10 warm-up calls, each timed call preceded by a
     512 MB write so that no input is served from the 256 MB last-level cache.  Prints one JSON
-    line per measurement, fractions against the nominal HBM peak and against the box's own
+    line per measurement, fractions against the nominal HBM peak and against this GPU's own
     device-copy rate; for n = 1 the CPU oracle's time on the same shapes is given beside it
     (one sequence, float64 NumPy on every host core and, except at 131072, on one BLAS
     thread; skipped with --no-cpu)."""
@@ -250,7 +250,7 @@ def kernel_configs(a):
     def emit(rec):
         print(json.dumps(rec), flush=True)
 
-    # the host and the box's own copy rate (a STREAM-style 1 GiB device-to-device copy,
+    # the host and this GPU's own copy rate (a STREAM-style 1 GiB device-to-device copy,
     # bytes read + written), beside the nominal HBM peak
     emit({"config": "host", "cpu_model": cpu_model() or "?", "cpu_threads": len(os.sched_getaffinity(0))})
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

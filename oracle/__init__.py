@@ -1,8 +1,8 @@
 """CPU oracle for the DDTree verification step -- TEST INFRASTRUCTURE ONLY.
 
 A plain, slow, float64 NumPy definition of what the step computes, written from
-the source pages (cited per function by page title and section) and from the
-readings listed in the design doc where the pages are silent.  It is independent of
+the source pages (cited per function by page title and section) and, where the
+pages are silent, from the readings each module states in its own docstring.  It is independent of
 the HIP library: the two share no code, and neither imports the other.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of

@@ -7,7 +7,7 @@ vLLM: candid research notes", section "What broke along the way": accepted and
 emitted tokens are kept apart -- the bonus token is emitted but is not an
 accepted draft node.
 
-Readings (DESIGN.md): greedy acceptance; argmax ties go to the lowest token
+Readings: greedy acceptance; argmax ties go to the lowest token
 id; a = number of accepted non-root nodes; acc_rows lists the root then the
 accepted rows, padded with -1 to L+1 entries; bonus = target argmax at the last
 accepted row.  Sibling tokens are distinct, so at most one child can match.

@@ -6,7 +6,7 @@ plus its own ancestors and never to its siblings.  "From DDTree to drafter
 training", section "The Architecture of DDTree": the whole tree is verified in
 one target pass with an ancestor-only attention mask.
 
-Readings (DESIGN.md): query head h reads kv head h // (Hq/Hkv); scale defaults
+Readings: query head h reads kv head h // (Hq/Hkv); scale defaults
 to D**-0.5; row i sees prefix keys [0, P), tree row 0 (the root), and tree row
 j+1 for every set bit j of anc[i] (which includes row i itself).  Tree keys and
 values sit in their own buffers, separate from the committed cache.

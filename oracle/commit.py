@@ -7,7 +7,7 @@ an explicit accepted-branch commit keyed by node and parent ids.  "From DDTree
 to drafter training", section "The Architecture of DDTree": the KV cache keeps
 only the accepted path's entries.
 
-Readings (DESIGN.md): the root plus the a accepted rows land at cache
+Readings: the root plus the a accepted rows land at cache
 positions P..P+a; the recurrent and conv state of the deepest accepted row
 (the root when a = 0) replace the committed state; prefix_len grows by a+1.
 A sequence whose prefix would exceed the cache capacity Pmax is left

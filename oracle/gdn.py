@@ -7,7 +7,7 @@ from its parent and writes its own to scratch, never to the committed state.
 "The architecture of speculation", section "The DDTree Integration
 Challenge": the recurrent state cannot be shared across branches.
 
-The pages never write the recurrence down.  Readings (DESIGN.md):
+The pages never write the recurrence down.  Readings:
   * conv: depthwise causal, width W, no bias, SiLU after.  Tap W-1 multiplies
     the current input; the state is the last W-1 inputs, oldest first.
     Channels C = 2*H*dk hold [q | k]; v, beta and g bypass the conv.

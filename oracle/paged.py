@@ -7,7 +7,7 @@ to run over the serving engine's paged KV blocks, and the accepted path is then
 written into the committed KV.  "From DDTree to drafter training", section "The
 Architecture of DDTree": the cache keeps only the accepted path's entries.
 
-Readings (DESIGN.md): a page holds page_size consecutive positions of every kv
+Readings: a page holds page_size consecutive positions of every kv
 head, pool layout [num_pages][Hkv][page_size][D]; position p of sequence s lives in
 page block_table[s][p // page_size] at slot p % page_size.  Attention and commit
 are exactly those of the contiguous cache after this gather (and its inverse

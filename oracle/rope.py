@@ -6,7 +6,7 @@ at those positions, must follow the branch depth, not the row order of the
 flattened tree.  "From DDTree to drafter training", section "The Architecture of
 DDTree": the whole tree is verified in one pass over the committed prefix.
 
-Readings (DESIGN.md): a tree row at depth d of a sequence with committed prefix
+Readings: a tree row at depth d of a sequence with committed prefix
 length P sits at position P + d (nodes at one depth share a position; the root,
 depth 0, is the token right after the prefix).  RoPE is the rotary embedding of
 Su et al. (RoFormer) in the rotate-half layout: the first rot_dim channels of a

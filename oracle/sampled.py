@@ -6,7 +6,7 @@ hid anomalies.  "From DDTree to drafter training", section "The Architecture of
 DDTree": walk down from the root while the target's token at the current node
 matches a child; the last target token is the bonus.
 
-Readings (DESIGN.md): the pages give no acceptance rule beyond comparing sampled
+Readings: the pages give no acceptance rule beyond comparing sampled
 tokens, so the walk is the greedy walk with each row's argmax replaced by a draw
 from the target's distribution at that row, softmax(z / temperature).  Every
 emitted token is then a plain sample of the target at its own context, so the

@@ -9,7 +9,8 @@ Architecture of DDTree" (heap build, flatten, verify, walk, compaction).
 
 Order: build the tree -> every layer in the given pattern ("attn" or "gdn") ->
 walk against the target argmaxes -> commit the accepted path.  The layers' own
-inputs are given (there are no projections between layers).
+inputs are given (the pages name no hidden size, so there are no projections
+between layers).
 """
 
 import numpy as np

@@ -12,7 +12,7 @@ flattens the tree into ids, per-depth positions and an ancestor-only mask.
 along the way": the drafter's per-depth logits are not conditioned on the
 branch, so a node's score is the sum of its path's per-depth log-probs.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
   * score(node) = sum over its path of full-vocabulary log-softmax values.
   * K defaults to B, which makes the result exactly the B best prefixes.
   * Heap order: score descending, then token id ascending (the configured tie
