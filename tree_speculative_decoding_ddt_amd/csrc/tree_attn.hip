@@ -254,28 +254,44 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_mfma_kernel(const uint16_t* _
     // scratch reload waits for every outstanding copy (they share vmcnt)
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    // paged: the pool rows of this wave's RPW key rows (wave-uniform scalar lookups)
+    // paged: the pool rows of this wave's RPW key rows (wave-uniform scalar lookups).  With
+    // the staged table and pages of at least 4 keys, a wave copies 4 consecutive key rows
+    // (tiles start 32 keys apart, so they lie in one page): one lookup, then base + 1, 2, 3
     size_t prow[RPW];
+    bool grp4 = false;
     if constexpr (PAGED) {
       static_assert(RPW == 4, "the paged lookup batches four rows per wave");
       if (pre) {
-        int keys[4];
+        grp4 = use_tab && pg.lps >= 2;
+        if (grp4) {
+          const int key0 = r0 + min(4 * wave, rows - 1);
+          const int pgid = __builtin_amdgcn_readfirstlane(pgtab[(key0 >> pg.lps) - pfirst]);  // one value for the wave
+          const size_t p0 = (((size_t)pgid * Hkv + kvh) << pg.lps) + (key0 & ((1 << pg.lps) - 1));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) keys[k] = r0 + min(wave + NW * k, rows - 1);
-        if (use_tab) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            prow[k] = (((size_t)pgtab[(keys[k] >> pg.lps) - pfirst] * Hkv + kvh) << pg.lps) +
-                      (keys[k] & ((1 << pg.lps) - 1));
+          for (int k = 0; k < 4; ++k) {
+            const size_t pr = p0 + (size_t)(min(4 * wave + k, rows - 1) - (key0 - r0));
+            prow[k] = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(pr >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)pr);
+          }
         } else {
-          pg.rows_uniform4(s, kvh, Hkv, keys, prow);
+          int keys[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) keys[k] = r0 + min(wave + NW * k, rows - 1);
+          if (use_tab) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              prow[k] = (((size_t)pgtab[(keys[k] >> pg.lps) - pfirst] * Hkv + kvh) << pg.lps) +
+                        (keys[k] & ((1 << pg.lps) - 1));
+          } else {
+            pg.rows_uniform4(s, kvh, Hkv, keys, prow);
+          }
         }
       }
     }
     if (ln < LPR) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
-        const int row = wave + NW * k;
+        const int row = grp4 ? 4 * wave + k : wave + NW * k;
         const int key = r0 + min(row, rows - 1);
         size_t e = (size_t)key * D;  // wave-uniform row start
         if constexpr (PAGED)
