@@ -68,9 +68,11 @@ def test_fp32_scalar_path(ps):
     run_case(ps, 2, 8, 4, 2, 1, 64, ps, 160 // ps, [128, 77], "f32")
 
 
-@pytest.mark.parametrize("ps", [16, 32, 64])
+@pytest.mark.parametrize("ps", [2, 4, 8, 16, 32, 64, 128])
 def test_bf16_d256_page_sizes(ps):
-    # the workload's heads; prefixes with ragged last pages
+    # the workload's heads; prefixes with ragged last pages.  Pages of 4 keys and more are
+    # copied four consecutive keys of one page per wave (one table lookup), smaller ones
+    # key by key
     say("paged bf16 D256 page size", ps)
     run_case(10 + ps, 2, 64, 15, 24, 4, 256, ps, 2048 // ps, [1000, 1777], "bf16")
 
