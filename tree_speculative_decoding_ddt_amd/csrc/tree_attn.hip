@@ -36,7 +36,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnNK = 32;      // keys per K/V tile (bf16 path)
 constexpr int kAttnStages = 4;   // LDS ring of K/V tiles (bf16 path)
-constexpr int kAttnMinSplit = 512;  // fewest prefix keys per split: a split's (lse, O) partials
+constexpr int kAttnMinSplit = 256;  // fewest prefix keys per split: a split's (lse, O) partials
                                     // cost about the traffic of 400 keys of K/V, but with few
                                     // sequences more splits fill more of the 256 CUs
 constexpr float kMaxRowSum = 0x1p64f;  // a pass whose row sum reaches this is redone (see below)
