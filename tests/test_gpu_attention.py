@@ -116,7 +116,7 @@ def test_bf16_bench_launch_configuration_sampled():
 def test_bf16_workload_batch_full_compare():
     # the workload's batch and heads (8 sequences, 24 q heads over 4 kv heads, head_dim
     # 256, 65 tree rows) at a prefix near 4K, every row and head compared: this reaches
-    # the multi-split path (four splits of 1040 keys) and the two row groups per kv head
+    # the multi-split path (four splits of up to 1056 keys) and the two row groups per kv head
     say("tree_attn bf16 n=8 P~4096, all rows and heads")
     run_case(95, 8, 64, 15, 24, 4, 256, 4160, [4096 - 37 * s for s in range(8)], "bf16")
 
