@@ -60,3 +60,12 @@ def test_graph_replay_next_paths():
                      H=4, dk=64, W=4, replay=True, rope=(64, 10000.0), sampled=True), seed=2)
     run(HybridConfig(n=2, V=4096, L=6, B=16, prefix=256, extra_cap=64, n_attn=1, n_gdn=2, Hq=8, Hkv=2, D=128,
                      H=4, dk=64, W=4, replay=True, page_size=16), seed=3)
+
+
+def test_graph_replay_overlapped_state_writes():
+    # the node-state writes on a second stream (joined before the attention layer and the
+    # commit) captured with the round: the committed state the commit copies from them
+    # must match the eager rounds after every replay
+    say("graph replay: node states written on a second stream")
+    run(HybridConfig(n=2, V=4096, L=6, B=16, prefix=256, extra_cap=64, n_attn=1, n_gdn=2, Hq=8, Hkv=2, D=128,
+                     H=4, dk=64, W=4, overlap_states=True), seed=4)
